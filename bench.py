@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache decode step on one MI355X.
+
+A step is one pass of the hot path over one batch: the cache write of every
+sequence's new token into its page, then paged decode attention of the whole
+batch.  The default workload is the 8B-class decode (32 sequences, 32 query /
+8 KV heads, head_dim 128, bf16 KV, 16-token pages, context lengths uniform in
+[512, 4096], pages randomly permuted in a pool sized to the total).
+
+The inputs are resident in HBM before timing starts.  Consecutive steps use
+different copies of the KV pool (R replicas, together several times larger
+than the 256 MB last-level cache), the way successive layers of a model read
+different caches, so no step finds its pages in cache.
+
+Prints one JSON line (rank 0, N = 1).  Besides the step throughput it reports
+the decode kernel against the HBM roofline (timed with HIP events on the
+launch stream) and the fp64 CPU oracle timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+# The CPU oracle's workers each run one sequence at a time; keep numpy's BLAS
+# single-threaded in them (set before numpy is imported).
+os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
+os.environ.setdefault("MKL_NUM_THREADS", "1")
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import CONFIGS, ELEM_BYTES, make_case, raw_bits  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + seqs/s"
+
+
+def decode_bytes(case) -> dict:
+    """Algorithmic bytes of one decode call and of one step's cache write."""
+    eb = ELEM_BYTES[case.kv_dtype]
+    qb = 2
+    B, Hq, D, Hkv = case.num_seqs, case.num_q_heads, case.head_dim, case.num_kv_heads
+    kept = 0
+    pages = 0
+    for n in case.context_lens.tolist():
+        lo = max(0, n - case.window) if case.window > 0 else 0
+        kept += max(0, n - lo)
+        pages += (n + 15) // 16 - lo // 16 if n > 0 else 0
+    kv = kept * Hkv * D * eb * 2
+    other = 2 * B * Hq * D * qb + pages * 4 + B * 4
+    write = B * Hkv * D * (2 * qb + 2 * eb) + B * 8
+    return dict(kv=kv, decode=kv + other, write=write, kept_tokens=kept)
+
+
+def cpu_baseline(case, seconds: float) -> dict:
+    """The fp64 oracle, unchanged, on this host: whole decode steps (cache
+    write of the batch's new tokens + decode of every sequence) repeated for
+    about ``seconds``."""
+    from oracle import attention as A
+    from oracle import scatter as S
+    cores = min(16, len(os.sched_getaffinity(0)))
+    t0 = time.time()
+    pool0 = raw_bits(case.sentinel_pool())
+    slots = case.fill_slots.numpy()
+    kp = S.cache_write_fast(pool0, raw_bits(case.fill_k), slots, case.kv_src_dtype, case.kv_dtype,
+                            case.k_scale)
+    vp = S.cache_write_fast(pool0, raw_bits(case.fill_v), slots, case.kv_src_dtype, case.kv_dtype,
+                            case.v_scale)
+    del pool0
+    setup = time.time() - t0
+    rows = case.step_rows.numpy()
+    step_slots = slots[rows]
+    kb, vb = raw_bits(case.fill_k)[rows], raw_bits(case.fill_v)[rows]
+    qb = raw_bits(case.q)
+    bt, ctx = case.block_tables.numpy(), case.context_lens.numpy()
+    steps, t0 = 0, time.time()
+    while True:
+        kp = S.cache_write_fast(kp, kb, step_slots, case.kv_src_dtype, case.kv_dtype, case.k_scale)
+        vp = S.cache_write_fast(vp, vb, step_slots, case.kv_src_dtype, case.kv_dtype, case.v_scale)
+        A.decode(qb, case.q_dtype, kp, vp, case.kv_dtype, bt, ctx, case.scale, case.window,
+                 case.k_scale, case.v_scale, workers=cores)
+        steps += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = (time.time() - t0) / steps
+    by = decode_bytes(case)
+    return {"value": round((by["decode"] + by["write"]) / dt / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{steps} whole decode step(s) of the benchmark batch "
+                      f"({case.num_seqs} seqs, cache write + fp64 decode), {dt:.2f} s each; "
+                      f"seqs/s {case.num_seqs / dt:.2f}; pool build {setup:.1f} s untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index (default: 8B-class decode)")
+    ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
+    ap.add_argument("--replicas", type=int, default=0, help="KV pool copies rotated over steps (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: the hot path here is a single-GPU kernel "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+    cfg = CONFIGS[args.config]
+    if cfg["kind"] != "decode":
+        print("bench.py times decode workloads", file=sys.stderr)
+        sys.exit(2)
+
+    case = make_case(args.config)
+    by = decode_bytes(case)
+    # CPU baseline first: it forks worker processes, which must happen
+    # before this process initialises the GPU.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
+
+    import paged_kv_cache_183_amd as P
+    from paged_kv_cache_183_amd.binding import tensor_desc  # noqa: F401  (library loaded)
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    view = (lambda t: t) if case.kv_dtype == "e4m3" else \
+        (lambda t: t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16))
+
+    fill_k, fill_v = case.fill_k.to(dev), case.fill_v.to(dev)
+    fill_slots = case.fill_slots.to(dev)
+    kc0, vc0 = case.sentinel_pool().to(dev), case.sentinel_pool().to(dev)
+    P.vllm_paged_cache_write(fill_k, fill_v, fill_slots, view(kc0), view(vc0),
+                             k_scale=case.k_scale, v_scale=case.v_scale)
+    pool_bytes = 2 * kc0.numel() * kc0.element_size()
+    R = args.replicas or max(2, math.ceil(3 * 256e6 / pool_bytes) + 1)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    rows = case.step_rows.to(dev)
+    new_k, new_v = fill_k[rows].contiguous(), fill_v[rows].contiguous()
+    new_slots = fill_slots[rows].contiguous()
+    del fill_k, fill_v
+    q = case.q.to(dev)
+    out = torch.empty_like(q)
+    bt, ctx = case.block_tables.to(dev), case.context_lens.to(dev)
+    part = args.partition or case.partition
+    ws_bytes = P.vllm_paged_attn_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                                case.head_dim, case.block_tables.shape[1], part)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % R]
+        P.vllm_paged_cache_write(new_k, new_v, new_slots, view(kc), view(vc),
+                                 k_scale=case.k_scale, v_scale=case.v_scale, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        P.vllm_paged_attn_decode(out, q, view(kc), view(vc), bt, ctx, case.scale, case.window,
+                                 k_scale=case.k_scale, v_scale=case.v_scale,
+                                 partition_size=part, workspace=ws if ws_bytes else None,
+                                 stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    step_bytes = by["decode"] + by["write"]
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = by["decode"] / (dec_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": case.name, "num_seqs": case.num_seqs,
+                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": 16,
+                   "context_lens": cfg.get("ctx_range") or cfg.get("ctx_list"),
+                   "kept_tokens": by["kept_tokens"], "kv_bytes_per_step": by["kv"],
+                   "bytes_per_step": step_bytes, "partition_tokens": part or "auto",
+                   "pool_replicas": R, "seed": args.config},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "seqs_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
+        "decode_call_ms": {"mean": round(dec_avg, 5),
+                           "p10": round(float(np.percentile(dec_ms, 10)), 5),
+                           "p50": round(float(np.percentile(dec_ms, 50)), 5),
+                           "p90": round(float(np.percentile(dec_ms, 90)), 5)},
+        "roofline": {"bound": "hbm", "kernel": "decode call (decode_kernel + decode_reduce_kernel)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

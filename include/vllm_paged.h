@@ -1,0 +1,203 @@
+/*
+ * vllm_paged.h -- C ABI of the paged KV-cache hot path for AMD Instinct
+ * MI355X (gfx950): the cache-write scatter that fills a block-paged KV pool,
+ * attention decode over that pool (single pass or split-K with a
+ * log-sum-exp reduce), FP8-E4M3 pools, and an MFMA chunked-prefill variant.
+ *
+ * What is computed follows the pages' problem statement:
+ *   - a block-paged KV cache held in FP16 or FP8 pages ("Building and
+ *     Deploying vllm.cpp", architecture overview box and Step 3 CLI table:
+ *     --kv-cache-dtype fp16|fp8, where fp8 stores one byte per element);
+ *   - per-sequence block tables that may point at shared physical pages
+ *     (same page, Step 3: zero-copy cache hits bind a new sequence's block
+ *     table to existing physical pages);
+ *   - 16-token pages (same page, the --block-size 16 launch commands);
+ *   - paged attention over the block-paged cache in the model forward
+ *     (vllm.cpp repository listing, "What's implemented", model forward),
+ *     with the sliding window of its local-attention section.
+ * ABI conventions follow the engine's own C ABI (vllm.cpp README, "Use it as
+ * a library (C API)" and the note on the C ABI under the title): flat and
+ * exception-free, every call returns a status with VLLM_OK on success and a
+ * message from vllm_last_error(), the version is checkable at run time, and
+ * option structs only grow by appending fields whose zero value keeps the
+ * existing behaviour.
+ *
+ * Conventions for every call below
+ *   - All tensor data pointers are DEVICE pointers (hipMalloc / torch CUDA
+ *     tensors).  Host pointers are rejected with VLLM_ERR_DEVICE_PTR.
+ *   - The caller owns every buffer (inputs, pools, outputs, workspace).  The
+ *     library keeps no device memory between calls.
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronize the host.  A VLLM_OK return means the
+ *     work was enqueued; device-side faults surface on the stream.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     error nothing is launched and no output is touched.
+ *   - Values that only the device sees are not validated (that would need a
+ *     host sync): slots, block ids and context lengths.  The kernels never
+ *     read or write outside the pools and tables for any such value: a slot
+ *     >= num_blocks*16 is skipped like a negative one, a block id outside
+ *     [0, num_blocks) reads page 0, a context length above
+ *     16*max_blocks_per_seq is clipped to it, and a context length <= 0
+ *     yields an all-zero output row.  The results of such inputs are
+ *     otherwise meaningless.  Duplicate slots in one cache write leave one of
+ *     the written values in the slot.
+ */
+#ifndef VLLM_PAGED_H
+#define VLLM_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VLLM_PAGED_ABI_VERSION 1
+#define VLLM_PAGED_BLOCK_SIZE 16
+
+typedef enum vllm_status {
+  VLLM_OK = 0,
+  VLLM_ERR_INVALID_ARG = 1,   /* null pointer, rank/shape/stride mismatch, Hq % Hkv != 0, window < 0 */
+  VLLM_ERR_UNSUPPORTED = 2,   /* dtype combination, head_dim or block size outside the supported set */
+  VLLM_ERR_DEVICE_PTR = 3,    /* a pointer that is not device memory */
+  VLLM_ERR_WORKSPACE = 4,     /* caller workspace too small or misaligned */
+  VLLM_ERR_HIP = 5            /* a HIP runtime call failed; message from hipGetErrorString */
+} vllm_status;
+
+typedef enum vllm_dtype {
+  VLLM_DTYPE_F16 = 1,
+  VLLM_DTYPE_BF16 = 2,
+  VLLM_DTYPE_FP8_E4M3 = 3,    /* OCP FP8 E4M3 (bias 7, max 448, NaN 0x7F/0xFF, no infinities) */
+  VLLM_DTYPE_I32 = 4,
+  VLLM_DTYPE_I64 = 5,
+  VLLM_DTYPE_F32 = 6
+} vllm_dtype;
+
+/* A dense tensor view: `data` is a device pointer, `shape` and `stride`
+ * (in elements, row-major) give the first `ndim` dimensions.  Every tensor
+ * passed to this library must be contiguous (stride of the last dimension
+ * 1, each other stride the product of the later extents; dimensions of
+ * extent 1 may carry any stride). */
+typedef struct vllm_tensor {
+  void* data;
+  int32_t dtype;     /* vllm_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} vllm_tensor;
+
+/* Options shared by the calls; zero-initialised means defaults.  Fields are
+ * only ever appended. */
+typedef struct vllm_attn_opts {
+  float k_scale;            /* FP8 pools only: K value = code * k_scale; 0 means 1.0 */
+  float v_scale;            /* FP8 pools only: V value = code * v_scale; 0 means 1.0 */
+  int32_t partition_size;   /* decode split-K partition in tokens: 0 = automatic, else a
+                               multiple of 16 in [16, 1024]; a batch whose longest possible
+                               context (16 * max_blocks_per_seq) fits in one partition runs
+                               in a single pass with no workspace */
+  int32_t flags;            /* reserved, must be 0 */
+  void* workspace;          /* device scratch for split-K partials; NULL = the library
+                               allocates it stream-ordered (hipMallocAsync / hipFreeAsync
+                               on hip_stream) for the duration of the call */
+  size_t workspace_bytes;   /* size of `workspace`; see vllm_paged_attn_workspace_size */
+} vllm_attn_opts;
+
+/* The ABI version this library was built with (VLLM_PAGED_ABI_VERSION). */
+int32_t vllm_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none).  The
+ * pointer stays valid until the next call into this library on the same
+ * thread. */
+const char* vllm_last_error(void);
+
+/*
+ * Cache write (scatter).  For every token i with s = slot_mapping[i] >= 0:
+ *   k_cache[s / 16, h, s % 16, :] = enc(k[i, h, :])   for every kv-head h,
+ *   v_cache[s / 16, h, s % 16, :] = enc(v[i, h, :]).
+ * Negative slots mark padding tokens and are skipped.  enc is the identity
+ * (bit copy) when the pool has the input's dtype; for an FP8_E4M3 pool it is
+ * the OCP E4M3 code of (x / scale) with x converted exactly to fp32, one
+ * correctly-rounded fp32 division by k_scale (v_scale) from opts, saturation
+ * to +-448 (infinities included), round-to-nearest-even, NaN -> 0x7F with
+ * the input's sign.  Bit-exact.
+ *   k, v         [T, Hkv, D]  F16 or BF16 (both the same dtype)
+ *   slot_mapping [T]          I64
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D]  the input's dtype or FP8_E4M3
+ *   opts         nullable; k_scale / v_scale used for FP8 pools only
+ * Supported: D a multiple of 8, D <= 512.  T = 0 is a no-op.
+ */
+vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
+                                   const vllm_tensor* slot_mapping,
+                                   vllm_tensor* k_cache, vllm_tensor* v_cache,
+                                   const vllm_attn_opts* opts, void* hip_stream);
+
+/*
+ * Paged attention decode: one query token per sequence, at position n - 1
+ * where n = context_lens[s] counts every cached token including the query's
+ * own (its K/V are written by vllm_paged_cache_write first).
+ *   out[s, h, :] = sum_t softmax_t(scale * <q[s, h, :], K_s[t, h / g, :]>) V_s[t, h / g, :]
+ * over t in [max(0, n - window), n) (window = 0: all n tokens), where token t
+ * of sequence s is row t % 16 of physical page block_tables[s, t / 16] and
+ * g = Hq / Hkv (consecutive grouping of query heads).  fp32 accumulation,
+ * output rounded to nearest-even in q's dtype.  Entries of block_tables past
+ * ceil(n / 16) are never read; pool rows outside the kept range are never
+ * used (they may hold NaN).
+ *   out          [B, Hq, D]  dtype of q (written)
+ *   q            [B, Hq, D]  F16 or BF16
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D]  q's dtype, or FP8_E4M3
+ *   block_tables [B, max_blocks_per_seq]  I32
+ *   context_lens [B]  I32
+ *   scale        softmax scale applied to q.k (e.g. 1/sqrt(D))
+ *   window       sliding window in tokens, 0 = off, must be >= 0
+ *   opts         nullable; fp8 scales, split-K partition size, workspace
+ * Supported: D in {64, 128}; Hq % Hkv == 0 (any g >= 1).  B = 0 is a no-op.
+ */
+vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
+                                   const vllm_tensor* k_cache, const vllm_tensor* v_cache,
+                                   const vllm_tensor* block_tables,
+                                   const vllm_tensor* context_lens, float scale,
+                                   int32_t window, const vllm_attn_opts* opts,
+                                   void* hip_stream);
+
+/*
+ * Bytes of workspace vllm_paged_attn_decode needs for these sizes (0 when
+ * it will run in a single pass).  partition_size as in vllm_attn_opts.
+ * Returns 0 for invalid arguments.
+ */
+size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_blocks_per_seq,
+                                      int32_t partition_size);
+
+/*
+ * Chunked-prefill attention on matrix cores: sequence s has Q_s =
+ * query_start_loc[s+1] - query_start_loc[s] query tokens (rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1 of q) at positions
+ * n - Q_s .. n - 1, where n = context_lens[s] includes them (their K/V are
+ * already in the pool).  Query row at position p attends to keys t <= p with
+ * t > p - window (window = 0: no lower bound).  Scores use bf16/f16 matrix
+ * products with fp32 accumulation; the softmax probabilities are rounded to
+ * q's dtype before the product with V; output rounded to q's dtype.
+ *   out          [sumQ, Hq, D]  dtype of q (written)
+ *   q            [sumQ, Hq, D]  F16 or BF16
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D]  q's dtype
+ *   block_tables [B, max_blocks_per_seq]  I32
+ *   query_start_loc [B + 1]  I32, non-decreasing, query_start_loc[0] = 0,
+ *                    query_start_loc[B] = sumQ
+ *   context_lens [B]  I32, n >= Q_s
+ *   max_query_len    an upper bound of max_s Q_s
+ * Supported: D = 128.  sumQ = 0 is a no-op.
+ */
+vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
+                                    const vllm_tensor* k_cache, const vllm_tensor* v_cache,
+                                    const vllm_tensor* block_tables,
+                                    const vllm_tensor* query_start_loc,
+                                    const vllm_tensor* context_lens,
+                                    int32_t max_query_len, float scale, int32_t window,
+                                    const vllm_attn_opts* opts, void* hip_stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* VLLM_PAGED_H */

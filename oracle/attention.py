@@ -33,6 +33,7 @@ This file is test infrastructure (see the package docstring).
 """
 from __future__ import annotations
 
+import multiprocessing
 from concurrent.futures import ProcessPoolExecutor
 from typing import Optional
 
@@ -98,6 +99,14 @@ def _seq_args(s, q, k_pool, v_pool, kv_fmt, block_tables, context_lens, scale,
     return (q_bits_to_f64(q[s], q_fmt), K, V, float(scale), int(window), want_w)
 
 
+# Inputs of the current multi-process decode, inherited by forked workers.
+_FORK_ARGS = None
+
+
+def _decode_seq_job(s):
+    return _decode_one(_seq_args(s, *_FORK_ARGS))
+
+
 def decode(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
            kv_fmt: str, block_tables: np.ndarray, context_lens: np.ndarray,
            scale: float, window: int = 0, k_scale: float = 1.0,
@@ -107,19 +116,25 @@ def decode(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
     [num_blocks, Hkv, 16, D].  Returns float64 [len(seqs), Hq, D] (all
     sequences by default) and, if asked, the per-kv-head softmax weights.
 
-    ``workers`` > 1 splits whole sequences over processes; each sequence is
-    computed identically, so the result does not depend on the worker count.
+    ``workers`` > 1 splits whole sequences over forked processes (which read
+    the inputs they inherit); each sequence is computed identically, so the
+    result does not depend on the worker count.
     """
+    global _FORK_ARGS
     B = q.shape[0]
     seqs = list(range(B)) if seqs is None else list(seqs)
-    jobs = (_seq_args(s, q, k_pool, v_pool, kv_fmt, block_tables, context_lens,
-                      scale, window, k_scale, v_scale, q_fmt, return_weights)
-            for s in seqs)
-    if workers > 1:
-        with ProcessPoolExecutor(max_workers=workers) as ex:
-            res = list(ex.map(_decode_one, jobs))
+    args = (q, k_pool, v_pool, kv_fmt, block_tables, context_lens, scale, window,
+            k_scale, v_scale, q_fmt, return_weights)
+    if workers > 1 and len(seqs) > 1:
+        _FORK_ARGS = args
+        try:
+            ctx = multiprocessing.get_context("fork")
+            with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+                res = list(ex.map(_decode_seq_job, seqs))
+        finally:
+            _FORK_ARGS = None
     else:
-        res = [_decode_one(a) for a in jobs]
+        res = [_decode_one(_seq_args(s, *args)) for s in seqs]
     if return_weights:
         return np.stack([r[0] for r in res]), [r[1] for r in res]
     return np.stack(res) if res else np.zeros((0,) + q.shape[1:], np.float64)

@@ -22,13 +22,26 @@ from .formats import e4m3_quantize_bits
 
 BLOCK = 16
 
+_CODE_TABLES = {}
+
+
+def e4m3_code_table(src_fmt: str, scale: float) -> np.ndarray:
+    """The E4M3 code of every one of the 65,536 16-bit inputs, each computed by
+    ``formats.e4m3_quantize_bits``.  The input domain is finite, so encoding
+    by lookup in this table is the same function, only memoized."""
+    key = (src_fmt, float(np.float32(scale)))
+    if key not in _CODE_TABLES:
+        every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        _CODE_TABLES[key] = e4m3_quantize_bits(every, src_fmt, scale)
+    return _CODE_TABLES[key]
+
 
 def encode_rows(bits: np.ndarray, src_fmt: str, cache_fmt: str, scale: float) -> np.ndarray:
     """What the pool stores for input rows ``bits`` (raw 16-bit patterns)."""
     if cache_fmt == src_fmt:
         return np.asarray(bits, dtype=np.uint16).copy()
     if cache_fmt == "e4m3":
-        return e4m3_quantize_bits(bits, src_fmt, scale)
+        return e4m3_code_table(src_fmt, scale)[np.asarray(bits, dtype=np.uint16)]
     raise ValueError(f"unsupported {src_fmt} -> {cache_fmt}")
 
 

@@ -1,0 +1,17 @@
+"""Paged KV-cache hot path for AMD MI355X (gfx950).
+
+The work happens in ``libvllm_paged.so`` (hand-written HIP kernels behind a C
+ABI declared in ``include/vllm_paged.h``); this package only builds it
+(``build``) and binds it (``binding``).  Importing the package loads the
+library and raises ImportError if it has not been built.
+"""
+from .binding import (  # noqa: F401
+    BLOCK_SIZE,
+    VllmError,
+    vllm_abi_version,
+    vllm_last_error,
+    vllm_paged_attn_decode,
+    vllm_paged_attn_prefill,
+    vllm_paged_attn_workspace_size,
+    vllm_paged_cache_write,
+)

@@ -1,0 +1,402 @@
+// C ABI of the paged KV-cache library: host-side validation of every argument,
+// then one or two asynchronous kernel launches on the caller's stream.  The
+// conventions (flat, exception-free, status codes with a thread-local last
+// error, runtime-checkable version, zero-valued option fields keeping the
+// default behaviour) follow the engine's C ABI as its README describes it
+// ("Use it as a library (C API)" and the note on the C ABI under the title).
+#include "vllm_paged.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vllm_status fail(vllm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+vllm_status ok() {
+  g_last_error.clear();
+  return VLLM_OK;
+}
+
+#define VP_TRY(expr)                        \
+  do {                                      \
+    vllm_status st_ = (expr);               \
+    if (st_ != VLLM_OK) return st_;         \
+  } while (0)
+
+const char* dtype_name(int32_t d) {
+  switch (d) {
+    case VLLM_DTYPE_F16: return "F16";
+    case VLLM_DTYPE_BF16: return "BF16";
+    case VLLM_DTYPE_FP8_E4M3: return "FP8_E4M3";
+    case VLLM_DTYPE_I32: return "I32";
+    case VLLM_DTYPE_I64: return "I64";
+    case VLLM_DTYPE_F32: return "F32";
+    default: return "unknown";
+  }
+}
+
+int64_t numel(const vllm_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+int elem_bytes(int32_t d) {
+  switch (d) {
+    case VLLM_DTYPE_F16: case VLLM_DTYPE_BF16: return 2;
+    case VLLM_DTYPE_FP8_E4M3: return 1;
+    case VLLM_DTYPE_I32: case VLLM_DTYPE_F32: return 4;
+    case VLLM_DTYPE_I64: return 8;
+    default: return 0;
+  }
+}
+
+// Rank, non-negative extents, contiguous strides, non-null data when non-empty.
+vllm_status check_tensor(const vllm_tensor* t, const char* name, int ndim) {
+  if (!t) return fail(VLLM_ERR_INVALID_ARG, "%s: null tensor descriptor", name);
+  if (t->ndim != ndim)
+    return fail(VLLM_ERR_INVALID_ARG, "%s: expected rank %d, got %d", name, ndim, (int)t->ndim);
+  int64_t expect = 1;
+  for (int i = ndim - 1; i >= 0; --i) {
+    if (t->shape[i] < 0) return fail(VLLM_ERR_INVALID_ARG, "%s: negative extent in dim %d", name, i);
+    if (t->shape[i] != 1 && t->stride[i] != expect)
+      return fail(VLLM_ERR_INVALID_ARG, "%s: not contiguous (dim %d stride %lld, expected %lld)", name,
+                  i, (long long)t->stride[i], (long long)expect);
+    expect *= t->shape[i];
+  }
+  if (elem_bytes(t->dtype) == 0)
+    return fail(VLLM_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)t->dtype);
+  if (numel(t) > 0 && t->data == nullptr)
+    return fail(VLLM_ERR_INVALID_ARG, "%s: null data pointer", name);
+  return VLLM_OK;
+}
+
+vllm_status check_dtype(const vllm_tensor* t, const char* name, int32_t want) {
+  if (t->dtype != want)
+    return fail(VLLM_ERR_UNSUPPORTED, "%s: dtype %s, expected %s", name, dtype_name(t->dtype),
+                dtype_name(want));
+  return VLLM_OK;
+}
+
+vllm_status check_align(const void* p, const char* name, uintptr_t a) {
+  if ((reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0)
+    return fail(VLLM_ERR_INVALID_ARG, "%s: data pointer not %u-byte aligned", name, (unsigned)a);
+  return VLLM_OK;
+}
+
+// Device memory only: the cache and everything the kernels touch must live
+// on the GPU (the listing's device-resident cache work asserts that every
+// cache pointer is device memory).
+vllm_status check_device_ptr(const void* p, const char* name) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(VLLM_ERR_DEVICE_PTR, "%s: not device memory (%s)", name, hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(VLLM_ERR_DEVICE_PTR, "%s: not device memory (memory type %d)", name, (int)attr.type);
+  return VLLM_OK;
+}
+
+vllm_status check_data(const vllm_tensor* t, const char* name, uintptr_t align) {
+  if (numel(t) == 0) return VLLM_OK;
+  VP_TRY(check_align(t->data, name, align));
+  return check_device_ptr(t->data, name);
+}
+
+vllm_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return VLLM_OK;
+  return fail(VLLM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int fmt_of(int32_t d) {
+  switch (d) {
+    case VLLM_DTYPE_F16: return vp::kF16;
+    case VLLM_DTYPE_BF16: return vp::kBF16;
+    case VLLM_DTYPE_FP8_E4M3: return vp::kE4M3;
+    default: return -1;
+  }
+}
+
+vllm_status scale_of(float s, const char* name, float* out) {
+  const float v = (s == 0.0f) ? 1.0f : s;
+  if (!std::isfinite(v) || v <= 0.0f)
+    return fail(VLLM_ERR_INVALID_ARG, "%s must be finite and > 0 (got %g)", name, (double)s);
+  *out = v;
+  return VLLM_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+// Decode partitioning: tokens per partition (multiple of 16, <= 1024).
+vllm_status pick_partition(int32_t requested, int32_t* tokens) {
+  int32_t p = requested;
+  if (p == 0) p = env_int("VLLM_PAGED_PARTITION", 0);
+  if (p == 0) p = 512;
+  if (p < 16 || p > 16 * vp::kMaxPartPages || p % 16 != 0)
+    return fail(VLLM_ERR_INVALID_ARG, "partition_size %d: must be a multiple of 16 in [16, %d]", (int)p,
+                16 * vp::kMaxPartPages);
+  *tokens = p;
+  return VLLM_OK;
+}
+
+struct SplitPlan {
+  int32_t part_pages;
+  int32_t num_parts;
+  size_t o_off, m_off, l_off, bytes;
+};
+
+SplitPlan plan_split(int64_t B, int64_t Hq, int64_t D, int64_t max_blocks, int32_t part_tokens) {
+  SplitPlan sp{};
+  sp.part_pages = part_tokens / 16;
+  sp.num_parts = (int32_t)((max_blocks + sp.part_pages - 1) / sp.part_pages);
+  if (sp.num_parts <= 1) {
+    sp.num_parts = 1;
+    sp.part_pages = (int32_t)(max_blocks > 0 ? max_blocks : 1);
+    return sp;
+  }
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t rows = (size_t)B * (size_t)Hq * (size_t)sp.num_parts;
+  sp.o_off = 0;
+  sp.m_off = up(rows * (size_t)D * 4);
+  sp.l_off = sp.m_off + up(rows * 4);
+  sp.bytes = sp.l_off + up(rows * 4);
+  return sp;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vllm_abi_version(void) { return VLLM_PAGED_ABI_VERSION; }
+
+const char* vllm_last_error(void) { return g_last_error.c_str(); }
+
+vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
+                                   const vllm_tensor* slot_mapping, vllm_tensor* k_cache,
+                                   vllm_tensor* v_cache, const vllm_attn_opts* opts,
+                                   void* hip_stream) {
+  VP_TRY(check_tensor(k, "k", 3));
+  VP_TRY(check_tensor(v, "v", 3));
+  VP_TRY(check_tensor(slot_mapping, "slot_mapping", 1));
+  VP_TRY(check_tensor(k_cache, "k_cache", 4));
+  VP_TRY(check_tensor(v_cache, "v_cache", 4));
+  if (opts && opts->flags != 0) return fail(VLLM_ERR_INVALID_ARG, "opts.flags must be 0");
+  const int64_t T = k->shape[0], Hkv = k->shape[1], D = k->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (v->shape[i] != k->shape[i]) return fail(VLLM_ERR_INVALID_ARG, "v shape differs from k");
+  if (slot_mapping->shape[0] != T)
+    return fail(VLLM_ERR_INVALID_ARG, "slot_mapping has %lld entries for %lld tokens",
+                (long long)slot_mapping->shape[0], (long long)T);
+  const int64_t NB = k_cache->shape[0];
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i])
+      return fail(VLLM_ERR_INVALID_ARG, "v_cache shape differs from k_cache");
+  if (k_cache->shape[2] != VLLM_PAGED_BLOCK_SIZE)
+    return fail(VLLM_ERR_UNSUPPORTED, "block size %lld: only 16 is supported", (long long)k_cache->shape[2]);
+  if (k_cache->shape[1] != Hkv || k_cache->shape[3] != D)
+    return fail(VLLM_ERR_INVALID_ARG, "k_cache [%lld, %lld, 16, %lld] does not match k [T, %lld, %lld]",
+                (long long)NB, (long long)k_cache->shape[1], (long long)k_cache->shape[3],
+                (long long)Hkv, (long long)D);
+  if (k->dtype != VLLM_DTYPE_F16 && k->dtype != VLLM_DTYPE_BF16)
+    return fail(VLLM_ERR_UNSUPPORTED, "k: dtype %s, expected F16 or BF16", dtype_name(k->dtype));
+  VP_TRY(check_dtype(v, "v", k->dtype));
+  VP_TRY(check_dtype(slot_mapping, "slot_mapping", VLLM_DTYPE_I64));
+  if (k_cache->dtype != k->dtype && k_cache->dtype != VLLM_DTYPE_FP8_E4M3)
+    return fail(VLLM_ERR_UNSUPPORTED, "k_cache: dtype %s with %s input", dtype_name(k_cache->dtype),
+                dtype_name(k->dtype));
+  VP_TRY(check_dtype(v_cache, "v_cache", k_cache->dtype));
+  if (D % 8 != 0 || D > 512 || D == 0)
+    return fail(VLLM_ERR_UNSUPPORTED, "head_dim %lld: must be a positive multiple of 8, <= 512", (long long)D);
+  if ((double)T * (double)Hkv * (double)(D / 8) >= 4294967295.0)
+    return fail(VLLM_ERR_UNSUPPORTED, "too many tokens for one call");
+  const bool to_fp8 = k_cache->dtype == VLLM_DTYPE_FP8_E4M3;
+  float ks = 1.0f, vs = 1.0f;
+  if (to_fp8) {
+    VP_TRY(scale_of(opts ? opts->k_scale : 0.0f, "k_scale", &ks));
+    VP_TRY(scale_of(opts ? opts->v_scale : 0.0f, "v_scale", &vs));
+  }
+  if (T == 0 || Hkv == 0) return ok();
+  VP_TRY(check_data(k, "k", 16));
+  VP_TRY(check_data(v, "v", 16));
+  VP_TRY(check_data(slot_mapping, "slot_mapping", 8));
+  VP_TRY(check_data(k_cache, "k_cache", to_fp8 ? 8 : 16));
+  VP_TRY(check_data(v_cache, "v_cache", to_fp8 ? 8 : 16));
+
+  vp::CacheWriteParams p{};
+  p.k = k->data;
+  p.v = v->data;
+  p.slot_mapping = static_cast<const int64_t*>(slot_mapping->data);
+  p.k_cache = k_cache->data;
+  p.v_cache = v_cache->data;
+  p.num_slots = NB * VLLM_PAGED_BLOCK_SIZE;
+  p.src_tok_stride = Hkv * D;
+  p.num_items = (uint32_t)(T * Hkv * (D / 8));
+  p.items_per_token = (uint32_t)(Hkv * (D / 8));
+  p.items_per_head = (uint32_t)(D / 8);
+  p.num_kv_heads = (int32_t)Hkv;
+  p.head_dim = (int32_t)D;
+  p.k_scale = ks;
+  p.v_scale = vs;
+  VP_TRY(hip_status(vp::launch_cache_write(p, fmt_of(k->dtype), to_fp8, (hipStream_t)hip_stream),
+                    "cache_write launch"));
+  return ok();
+}
+
+size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_blocks_per_seq,
+                                      int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      (head_dim != 64 && head_dim != 128) || max_blocks_per_seq < 0)
+    return 0;
+  int32_t part_tokens = 0;
+  if (pick_partition(partition_size, &part_tokens) != VLLM_OK) return 0;
+  SplitPlan sp = plan_split(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, part_tokens);
+  return sp.num_parts > 1 ? sp.bytes : 0;
+}
+
+vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
+                                   const vllm_tensor* k_cache, const vllm_tensor* v_cache,
+                                   const vllm_tensor* block_tables,
+                                   const vllm_tensor* context_lens, float scale, int32_t window,
+                                   const vllm_attn_opts* opts, void* hip_stream) {
+  VP_TRY(check_tensor(out, "out", 3));
+  VP_TRY(check_tensor(q, "q", 3));
+  VP_TRY(check_tensor(k_cache, "k_cache", 4));
+  VP_TRY(check_tensor(v_cache, "v_cache", 4));
+  VP_TRY(check_tensor(block_tables, "block_tables", 2));
+  VP_TRY(check_tensor(context_lens, "context_lens", 1));
+  if (opts && opts->flags != 0) return fail(VLLM_ERR_INVALID_ARG, "opts.flags must be 0");
+  const int64_t B = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(VLLM_ERR_INVALID_ARG, "out shape differs from q");
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i])
+      return fail(VLLM_ERR_INVALID_ARG, "v_cache shape differs from k_cache");
+  const int64_t NB = k_cache->shape[0], Hkv = k_cache->shape[1];
+  if (k_cache->shape[2] != VLLM_PAGED_BLOCK_SIZE)
+    return fail(VLLM_ERR_UNSUPPORTED, "block size %lld: only 16 is supported", (long long)k_cache->shape[2]);
+  if (k_cache->shape[3] != D)
+    return fail(VLLM_ERR_INVALID_ARG, "k_cache head_dim %lld != q head_dim %lld",
+                (long long)k_cache->shape[3], (long long)D);
+  if (block_tables->shape[0] != B || context_lens->shape[0] != B)
+    return fail(VLLM_ERR_INVALID_ARG, "block_tables / context_lens must have %lld rows", (long long)B);
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0)
+    return fail(VLLM_ERR_INVALID_ARG, "num_q_heads %lld is not a positive multiple of num_kv_heads %lld",
+                (long long)Hq, (long long)Hkv);
+  if (window < 0) return fail(VLLM_ERR_INVALID_ARG, "window must be >= 0 (got %d)", (int)window);
+  if (!std::isfinite(scale)) return fail(VLLM_ERR_INVALID_ARG, "scale must be finite");
+  if (q->dtype != VLLM_DTYPE_F16 && q->dtype != VLLM_DTYPE_BF16)
+    return fail(VLLM_ERR_UNSUPPORTED, "q: dtype %s, expected F16 or BF16", dtype_name(q->dtype));
+  VP_TRY(check_dtype(out, "out", q->dtype));
+  if (k_cache->dtype != q->dtype && k_cache->dtype != VLLM_DTYPE_FP8_E4M3)
+    return fail(VLLM_ERR_UNSUPPORTED, "k_cache: dtype %s with %s queries", dtype_name(k_cache->dtype),
+                dtype_name(q->dtype));
+  VP_TRY(check_dtype(v_cache, "v_cache", k_cache->dtype));
+  VP_TRY(check_dtype(block_tables, "block_tables", VLLM_DTYPE_I32));
+  VP_TRY(check_dtype(context_lens, "context_lens", VLLM_DTYPE_I32));
+  if (D != 64 && D != 128)
+    return fail(VLLM_ERR_UNSUPPORTED, "head_dim %lld: supported 64, 128", (long long)D);
+  if (NB > INT32_MAX || block_tables->shape[1] > INT32_MAX / 16 || B > 65535 || Hq > 65535)
+    return fail(VLLM_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  const bool fp8 = k_cache->dtype == VLLM_DTYPE_FP8_E4M3;
+  float ks = 1.0f, vs = 1.0f;
+  if (fp8) {
+    VP_TRY(scale_of(opts ? opts->k_scale : 0.0f, "k_scale", &ks));
+    VP_TRY(scale_of(opts ? opts->v_scale : 0.0f, "v_scale", &vs));
+  }
+  int32_t part_tokens = 0;
+  VP_TRY(pick_partition(opts ? opts->partition_size : 0, &part_tokens));
+  const int64_t max_blocks = block_tables->shape[1];
+  const SplitPlan sp = plan_split(B, Hq, D, max_blocks, part_tokens);
+  if (B == 0) return ok();
+  if (sp.num_parts > 1 && opts && opts->workspace && opts->workspace_bytes < sp.bytes)
+    return fail(VLLM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, sp.bytes);
+  VP_TRY(check_data(q, "q", 16));
+  VP_TRY(check_data(out, "out", 2));
+  VP_TRY(check_data(k_cache, "k_cache", fp8 ? 8 : 16));
+  VP_TRY(check_data(v_cache, "v_cache", fp8 ? 8 : 16));
+  VP_TRY(check_data(block_tables, "block_tables", 4));
+  VP_TRY(check_data(context_lens, "context_lens", 4));
+
+  hipStream_t stream = (hipStream_t)hip_stream;
+  vp::DecodeParams p{};
+  p.q = q->data;
+  p.out = out->data;
+  p.k_cache = k_cache->data;
+  p.v_cache = v_cache->data;
+  p.block_tables = static_cast<const int32_t*>(block_tables->data);
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.num_seqs = (int32_t)B;
+  p.num_q_heads = (int32_t)Hq;
+  p.num_kv_heads = (int32_t)Hkv;
+  p.group = (int32_t)(Hq / Hkv);
+  p.bt_stride = (int32_t)max_blocks;
+  p.num_blocks = (int32_t)NB;
+  p.num_parts = sp.num_parts;
+  p.part_pages = sp.part_pages;
+  p.window = window;
+  p.score_scale = scale * 1.4426950408889634f * ks;
+  p.out_scale = vs;
+
+  void* ws = nullptr;
+  bool owned = false;
+  if (sp.num_parts > 1) {
+    if (opts && opts->workspace) {
+      ws = opts->workspace;
+      VP_TRY(check_align(ws, "workspace", 256));
+      VP_TRY(check_device_ptr(ws, "workspace"));
+    } else {
+      VP_TRY(hip_status(hipMallocAsync(&ws, sp.bytes, stream), "workspace hipMallocAsync"));
+      owned = true;
+    }
+    char* base = static_cast<char*>(ws);
+    p.ws_o = reinterpret_cast<float*>(base + sp.o_off);
+    p.ws_m = reinterpret_cast<float*>(base + sp.m_off);
+    p.ws_l = reinterpret_cast<float*>(base + sp.l_off);
+  }
+  hipError_t e = vp::launch_decode(p, (int)D, fmt_of(k_cache->dtype), fmt_of(q->dtype), stream);
+  if (owned) {
+    hipError_t e2 = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = e2;
+  }
+  VP_TRY(hip_status(e, "decode launch"));
+  return ok();
+}
+
+vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
+                                    const vllm_tensor* k_cache, const vllm_tensor* v_cache,
+                                    const vllm_tensor* block_tables,
+                                    const vllm_tensor* query_start_loc,
+                                    const vllm_tensor* context_lens, int32_t max_query_len,
+                                    float scale, int32_t window, const vllm_attn_opts* opts,
+                                    void* hip_stream) {
+  (void)out; (void)q; (void)k_cache; (void)v_cache; (void)block_tables; (void)query_start_loc;
+  (void)context_lens; (void)max_query_len; (void)scale; (void)window; (void)opts; (void)hip_stream;
+  return fail(VLLM_ERR_UNSUPPORTED, "prefill: not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels of the paged KV-cache library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace vp {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+template <typename T, typename U>
+__device__ __forceinline__ T bitcast(U u) {
+  static_assert(sizeof(T) == sizeof(U), "size");
+  return __builtin_bit_cast(T, u);
+}
+
+// ---- 16-bit <-> fp32 ---------------------------------------------------------
+
+// Two packed bf16 -> two fp32 (exact: bf16 is the upper half of an fp32).
+__device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) {
+  lo = bitcast<float>(w << 16);
+  hi = bitcast<float>(w & 0xFFFF0000u);
+}
+
+// Two packed fp16 -> two fp32 (exact).
+__device__ __forceinline__ void f16x2_to_f32(uint32_t w, float& lo, float& hi) {
+  half2_t h = bitcast<half2_t>(w);
+  lo = (float)h.x;
+  hi = (float)h.y;
+}
+
+template <int F>
+__device__ __forceinline__ void x2_to_f32(uint32_t w, float& lo, float& hi) {
+  if constexpr (F == kBF16) bf16x2_to_f32(w, lo, hi);
+  else f16x2_to_f32(w, lo, hi);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = bitcast<uint32_t>(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> fp16 bits, round to nearest even (hardware conversion, default mode).
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  return bitcast<uint16_t>((_Float16)f);
+}
+
+template <int F>
+__device__ __forceinline__ uint16_t f32_to_16(float f) {
+  if constexpr (F == kBF16) return f32_to_bf16_rne(f);
+  else return f32_to_f16_rne(f);
+}
+
+// ---- OCP FP8 E4M3 -------------------------------------------------------------
+//
+// Encoder written from the OCP 8-bit floating point specification (E4M3:
+// bias 7, 3 mantissa bits, max 448, NaN S.1111.111, no infinities) with
+// integer operations on the fp32 bit pattern: saturate to +-448, round to
+// nearest with ties to the even code, NaN -> 0x7F | sign, zero keeps its sign.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
+  const uint32_t u = bitcast<uint32_t>(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // >= 448 (and inf): saturate
+  if (a < 0x3C800000u) {                             // below 2^-6: spacing 2^-9
+    // |y| * 2^9 is exact; round it to the nearest even integer (0..8).
+    float r = __builtin_rintf(bitcast<float>(a) * 512.0f);
+    return sign | (uint32_t)r;                       // 8 is the code of 2^-6
+  }
+  const uint32_t e = (a >> 23) - 127u + 7u;          // 1 .. 15
+  const uint32_t mant = a & 0x7FFFFFu;
+  const uint32_t keep = mant >> 20;                  // top 3 mantissa bits
+  const uint32_t rest = mant & 0xFFFFFu;             // 20 dropped bits
+  uint32_t code = (e << 3) | keep;
+  code += (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+  return sign | code;                                // never reaches 0x7F below 448
+}
+
+// ---- cross-lane sums within 16-lane rows (DPP) ---------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kRowMirror = 0x140;      // lane i <- lane 15 - i within a row of 16
+constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7 - i within each 8
+constexpr int kQuad3210 = 0x1B;        // quad_perm [3,2,1,0]
+constexpr int kQuad1032 = 0xB1;        // quad_perm [1,0,3,2]
+
+// Sum over aligned groups of W lanes (W = 4, 8 or 16); every lane of the group
+// receives the total.  Each step pairs the two halves of a group, so after
+// log2(W) steps every lane holds the full group sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(W == 4 || W == 8 || W == 16, "group width");
+  if constexpr (W == 16) x += dpp_f<kRowMirror>(x);
+  if constexpr (W >= 8) x += dpp_f<kRowHalfMirror>(x);
+  x += dpp_f<kQuad3210>(x);
+  x += dpp_f<kQuad1032>(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace vp

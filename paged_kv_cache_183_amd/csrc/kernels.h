@@ -1,0 +1,84 @@
+// Parameter blocks and host-side launchers of the gfx950 kernels.  The C ABI
+// layer (abi.cpp) validates everything before filling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vp {
+
+// Storage formats handled by the kernels.
+enum Fmt : int { kF16 = 0, kBF16 = 1, kE4M3 = 2 };
+
+struct CacheWriteParams {
+  const void* k;               // [T, Hkv, D] 16-bit
+  const void* v;
+  const int64_t* slot_mapping; // [T]
+  void* k_cache;               // [num_blocks, Hkv, 16, D]
+  void* v_cache;
+  int64_t num_slots;           // num_blocks * 16
+  int64_t src_tok_stride;      // elements between tokens of k / v (Hkv * D)
+  uint32_t num_items;          // T * Hkv * D / 8
+  uint32_t items_per_token;    // Hkv * D / 8
+  uint32_t items_per_head;     // D / 8
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float k_scale;               // FP8 pools: stored code = e4m3(x / k_scale)
+  float v_scale;
+};
+
+hipError_t launch_cache_write(const CacheWriteParams& p, int src_fmt, bool to_fp8,
+                              hipStream_t stream);
+
+struct DecodeParams {
+  const void* q;               // [B, Hq, D]
+  void* out;                   // [B, Hq, D]
+  const void* k_cache;         // [num_blocks, Hkv, 16, D]
+  const void* v_cache;
+  const int32_t* block_tables; // [B, bt_stride]
+  const int32_t* context_lens; // [B]
+  float* ws_o;                 // [B, Hq, num_parts, D]   (split-K only)
+  float* ws_m;                 // [B, Hq, num_parts]      running max, log2 units
+  float* ws_l;                 // [B, Hq, num_parts]      sum of exp2(s - m)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;               // g = Hq / Hkv
+  int32_t bt_stride;           // max_blocks_per_seq
+  int32_t num_blocks;
+  int32_t num_parts;           // partitions per sequence (grid.x); 1 = single pass
+  int32_t part_pages;          // pages per partition
+  int32_t window;              // 0 = off
+  float score_scale;           // scale * log2(e) * k_scale
+  float out_scale;             // v_scale (1 for 16-bit pools)
+};
+
+// kv_fmt: kF16 / kBF16 / kE4M3; q_fmt: kF16 / kBF16.
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt,
+                         hipStream_t stream);
+
+struct PrefillParams {
+  const void* q;               // [sumQ, Hq, D]
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* query_start_loc;  // [B + 1]
+  const int32_t* context_lens;     // [B]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t bt_stride;
+  int32_t num_blocks;
+  int32_t max_query_len;
+  int32_t window;
+  float score_scale;           // scale * log2(e)
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipStream_t stream);
+
+// Largest number of pages one decode partition may cover.
+constexpr int kMaxPartPages = 64;
+
+}  // namespace vp

@@ -87,3 +87,13 @@ def test_fp8_write_matches_codec_and_scale():
     xf = kv_bits_to_f64(x, "f16")
     err = np.abs(Kc - xf)
     assert np.all(err <= np.abs(xf) * 2.0 ** -4 + 0.05 * 2.0 ** -10)
+
+
+def test_fp8_code_table_equals_direct_encoder():
+    rng = np.random.default_rng(7)
+    for fmt in ("f16", "bf16"):
+        for scale in (1.0, 0.05):
+            bits = rng.integers(0, 65536, size=5000).astype(np.uint16)
+            from oracle.formats import e4m3_quantize_bits
+            assert np.array_equal(scatter.encode_rows(bits, fmt, "e4m3", scale),
+                                  e4m3_quantize_bits(bits, fmt, scale))
