@@ -108,7 +108,19 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies rotated over steps (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (a "
+                         "kernel of known traffic for scaling profiler byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the hot path here is a single-GPU kernel "
               f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
