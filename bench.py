@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies rotated over steps (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay captured HIP graphs instead of launching every call eagerly")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (a "
                          "kernel of known traffic for scaling profiler byte counters) and exit")
@@ -141,7 +143,6 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
     view = (lambda t: t) if case.kv_dtype == "e4m3" else \
         (lambda t: t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16))
 
@@ -164,31 +165,63 @@ def main():
     ws_bytes = P.vllm_paged_attn_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                                 case.head_dim, case.block_tables.shape[1], part)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
-        kc, vc = pools[i % R]
+    def write(r):
+        kc, vc = pools[r]
         P.vllm_paged_cache_write(new_k, new_v, new_slots, view(kc), view(vc),
-                                 k_scale=case.k_scale, v_scale=case.v_scale, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+                                 k_scale=case.k_scale, v_scale=case.v_scale)
+
+    def decode(r):
+        kc, vc = pools[r]
         P.vllm_paged_attn_decode(out, q, view(kc), view(vc), bt, ctx, case.scale, case.window,
                                  k_scale=case.k_scale, v_scale=case.v_scale,
-                                 partition_size=part, workspace=ws if ws_bytes else None,
-                                 stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+                                 partition_size=part, workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
+    for i in range(max(args.warmup, R)):          # eager warm-up (also checks every replica)
+        write(i % R)
+        decode(i % R)
     torch.cuda.synchronize()
+
+    if not args.graph:
+        run_write = write
+        run_decode = decode
+    else:
+        # One graph per replica for the cache write and one for the decode (a
+        # decode step of a serving engine is replayed from a captured graph;
+        # this removes the Python launch cost from the timed region).
+        gw, gd = [], []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(R):
+                g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g1, stream=side, capture_error_mode="relaxed"):
+                    write(r)
+                with torch.cuda.graph(g2, stream=side, capture_error_mode="relaxed"):
+                    decode(r)
+                gw.append(g1)
+                gd.append(g2)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        run_write = lambda r: gw[r].replay()
+        run_decode = lambda r: gd[r].replay()
+        for i in range(args.warmup):
+            run_write(i % R)
+            run_decode(i % R)
+        torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        r = (args.warmup + i) % R
+        run_write(r)
+        evs[i][0].record(stream)
+        run_decode(r)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -217,14 +250,15 @@ def main():
                    "context_lens": cfg.get("ctx_range") or cfg.get("ctx_list"),
                    "kept_tokens": by["kept_tokens"], "kv_bytes_per_step": by["kv"],
                    "bytes_per_step": step_bytes, "partition_tokens": part or "auto",
-                   "pool_replicas": R, "seed": args.config},
+                   "pool_replicas": R, "seed": args.config,
+                   "launch": "hip_graph_replay" if args.graph else "eager"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seqs_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
         "decode_call_ms": {"mean": round(dec_avg, 5),
                            "p10": round(float(np.percentile(dec_ms, 10)), 5),
                            "p50": round(float(np.percentile(dec_ms, 50)), 5),
                            "p90": round(float(np.percentile(dec_ms, 90)), 5)},
-        "roofline": {"bound": "hbm", "kernel": "decode call (decode_kernel + decode_reduce_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "decode call (decode_kernel + decode_merge_kernel)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
         "cpu_baseline": cpu,

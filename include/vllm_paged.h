@@ -1,8 +1,9 @@
 /*
  * vllm_paged.h -- C ABI of the paged KV-cache hot path for AMD Instinct
  * MI355X (gfx950): the cache-write scatter that fills a block-paged KV pool,
- * attention decode over that pool (single pass or split-K with a
- * log-sum-exp reduce), FP8-E4M3 pools, and an MFMA chunked-prefill variant.
+ * attention decode over that pool (work split evenly over the GPU's waves,
+ * pieces of cut sequences merged with the log-sum-exp rule), FP8-E4M3 pools,
+ * and an MFMA chunked-prefill variant.
  *
  * What is computed follows the pages' problem statement:
  *   - a block-paged KV cache held in FP16 or FP8 pages ("Building and
@@ -91,14 +92,17 @@ typedef struct vllm_tensor {
 typedef struct vllm_attn_opts {
   float k_scale;            /* FP8 pools only: K value = code * k_scale; 0 means 1.0 */
   float v_scale;            /* FP8 pools only: V value = code * v_scale; 0 means 1.0 */
-  int32_t partition_size;   /* decode split-K partition in tokens: 0 = automatic, else a
-                               multiple of 16 in [16, 1024]; a batch whose longest possible
-                               context (16 * max_blocks_per_seq) fits in one partition runs
-                               in a single pass with no workspace */
+  int32_t partition_size;   /* decode work split: 0 = automatic (the kept pages of the whole
+                               batch are cut into one equal chunk per wave the GPU holds at
+                               once); else a fixed chunk of this many tokens, a positive
+                               multiple of 16.  Pieces of a sequence cut by chunk boundaries
+                               are merged with the log-sum-exp rule by a second kernel */
   int32_t flags;            /* reserved, must be 0 */
-  void* workspace;          /* device scratch for split-K partials; NULL = the library
-                               allocates it stream-ordered (hipMallocAsync / hipFreeAsync
-                               on hip_stream) for the duration of the call */
+  void* workspace;          /* device scratch of the decode (piece records, page prefix,
+                               partial results of cut sequences), 256-byte aligned; needs no
+                               initialisation; calls that share a workspace must not overlap.
+                               NULL = the library allocates one stream-ordered
+                               (hipMallocAsync / hipFreeAsync on hip_stream) for the call */
   size_t workspace_bytes;   /* size of `workspace`; see vllm_paged_attn_workspace_size */
 } vllm_attn_opts;
 
@@ -142,7 +146,7 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
  * output rounded to nearest-even in q's dtype.  Entries of block_tables past
  * ceil(n / 16) are never read; pool rows outside the kept range are never
  * used (they may hold NaN).
- *   out          [B, Hq, D]  dtype of q (written)
+ *   out          [B, Hq, D]  dtype of q (written; 16-byte aligned)
  *   q            [B, Hq, D]  F16 or BF16
  *   k_cache, v_cache [num_blocks, Hkv, 16, D]  q's dtype, or FP8_E4M3
  *   block_tables [B, max_blocks_per_seq]  I32
@@ -150,7 +154,10 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
  *   scale        softmax scale applied to q.k (e.g. 1/sqrt(D))
  *   window       sliding window in tokens, 0 = off, must be >= 0
  *   opts         nullable; fp8 scales, split-K partition size, workspace
- * Supported: D in {64, 128}; Hq % Hkv == 0 (any g >= 1).  B = 0 is a no-op.
+ * Supported: D in {64, 128}; Hq % Hkv == 0 (any g >= 1); at most 131072
+ * work units B * Hkv * (g / head chunk), where the head chunk is g for
+ * g <= 8, else the largest divisor of g not above 8; the work bound
+ * units * max_blocks_per_seq below 2^31 pages.  B = 0 is a no-op.
  */
 vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
                                    const vllm_tensor* k_cache, const vllm_tensor* v_cache,
@@ -160,9 +167,10 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
                                    void* hip_stream);
 
 /*
- * Bytes of workspace vllm_paged_attn_decode needs for these sizes (0 when
- * it will run in a single pass).  partition_size as in vllm_attn_opts.
- * Returns 0 for invalid arguments.
+ * Bytes of workspace vllm_paged_attn_decode needs for these sizes (it
+ * depends on the sizes and partition_size only, not on the device or the
+ * dtypes).  partition_size as in vllm_attn_opts.  Returns 0 for invalid
+ * arguments.
  */
 size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,

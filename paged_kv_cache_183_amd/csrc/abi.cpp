@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -151,40 +152,55 @@ int env_int(const char* name, int dflt) {
   return std::atoi(s);
 }
 
-// Decode partitioning: tokens per partition (multiple of 16, <= 1024).
-vllm_status pick_partition(int32_t requested, int32_t* tokens) {
+// Decode work split: tokens per chunk (a multiple of 16), or 0 for the
+// automatic equal split over the waves the GPU holds at once.
+vllm_status pick_chunk_tokens(int32_t requested, int32_t* tokens) {
   int32_t p = requested;
   if (p == 0) p = env_int("VLLM_PAGED_PARTITION", 0);
-  if (p == 0) p = 512;
-  if (p < 16 || p > 16 * vp::kMaxPartPages || p % 16 != 0)
-    return fail(VLLM_ERR_INVALID_ARG, "partition_size %d: must be a multiple of 16 in [16, %d]", (int)p,
-                16 * vp::kMaxPartPages);
+  if (p != 0 && (p < 16 || p % 16 != 0))
+    return fail(VLLM_ERR_INVALID_ARG, "partition_size %d: must be 0 or a positive multiple of 16", (int)p);
   *tokens = p;
   return VLLM_OK;
 }
 
-struct SplitPlan {
-  int32_t part_pages;
-  int32_t num_parts;
-  size_t o_off, m_off, l_off, bytes;
+struct DecodePlan {
+  int32_t head_chunk, units_per_seq, chunk_pages;
+  int64_t pages_bound, max_chunks;
+  size_t cnt_off, pre_off, o_off, m_off, l_off, bytes;
 };
 
-SplitPlan plan_split(int64_t B, int64_t Hq, int64_t D, int64_t max_blocks, int32_t part_tokens) {
-  SplitPlan sp{};
-  sp.part_pages = part_tokens / 16;
-  sp.num_parts = (int32_t)((max_blocks + sp.part_pages - 1) / sp.part_pages);
-  if (sp.num_parts <= 1) {
-    sp.num_parts = 1;
-    sp.part_pages = (int32_t)(max_blocks > 0 ? max_blocks : 1);
-    return sp;
-  }
-  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t rows = (size_t)B * (size_t)Hq * (size_t)sp.num_parts;
-  sp.o_off = 0;
-  sp.m_off = up(rows * (size_t)D * 4);
-  sp.l_off = sp.m_off + up(rows * 4);
-  sp.bytes = sp.l_off + up(rows * 4);
-  return sp;
+// Workspace layout of a decode: per-unit piece records (2 ints per unit),
+// page prefix (B + 3 ints), then the partial outputs, maxima and sums of up
+// to 2 pieces per chunk.  The kernels rewrite every part they read, so the
+// workspace needs no initialisation.
+vllm_status plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t max_blocks,
+                        int32_t chunk_tokens, DecodePlan* dp) {
+  DecodePlan x{};
+  x.head_chunk = vp::decode_head_chunk((int)(Hq / Hkv));
+  x.units_per_seq = (int32_t)(Hkv * (Hq / Hkv / x.head_chunk));
+  x.pages_bound = B * x.units_per_seq * max_blocks;
+  if (x.pages_bound >= ((int64_t)1 << 31))
+    return fail(VLLM_ERR_UNSUPPORTED, "batch too large: %lld pages of work", (long long)x.pages_bound);
+  x.chunk_pages = chunk_tokens / 16;
+  if (x.chunk_pages > 0)
+    x.max_chunks = (x.pages_bound + x.chunk_pages - 1) / x.chunk_pages;
+  else
+    x.max_chunks = std::min<int64_t>(vp::kMaxWorkers,
+                                     (x.pages_bound + vp::kMinChunkPages - 1) / vp::kMinChunkPages);
+  if (x.max_chunks < 1) x.max_chunks = 1;
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  const size_t pieces = (size_t)x.max_chunks * 2 * (size_t)x.head_chunk;
+  if (B * x.units_per_seq > (int64_t)(vp::kUnitBytes / 8))
+    return fail(VLLM_ERR_UNSUPPORTED, "batch too large: %lld work units (at most %zu)",
+                (long long)(B * x.units_per_seq), vp::kUnitBytes / 8);
+  x.cnt_off = 0;
+  x.pre_off = up((size_t)B * (size_t)x.units_per_seq * 8);
+  x.o_off = x.pre_off + up((size_t)(B + 3) * 4);
+  x.m_off = x.o_off + up(pieces * (size_t)D * 4);
+  x.l_off = x.m_off + up(pieces * 4);
+  x.bytes = x.l_off + up(pieces * 4);
+  *dp = x;
+  return VLLM_OK;
 }
 
 }  // namespace
@@ -272,10 +288,13 @@ size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
       (head_dim != 64 && head_dim != 128) || max_blocks_per_seq < 0)
     return 0;
-  int32_t part_tokens = 0;
-  if (pick_partition(partition_size, &part_tokens) != VLLM_OK) return 0;
-  SplitPlan sp = plan_split(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, part_tokens);
-  return sp.num_parts > 1 ? sp.bytes : 0;
+  int32_t chunk_tokens = 0;
+  DecodePlan dp;
+  if (pick_chunk_tokens(partition_size, &chunk_tokens) != VLLM_OK ||
+      plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, chunk_tokens,
+                  &dp) != VLLM_OK)
+    return 0;
+  return dp.bytes;
 }
 
 vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
@@ -328,21 +347,23 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
     VP_TRY(scale_of(opts ? opts->k_scale : 0.0f, "k_scale", &ks));
     VP_TRY(scale_of(opts ? opts->v_scale : 0.0f, "v_scale", &vs));
   }
-  int32_t part_tokens = 0;
-  VP_TRY(pick_partition(opts ? opts->partition_size : 0, &part_tokens));
+  int32_t chunk_tokens = 0;
+  VP_TRY(pick_chunk_tokens(opts ? opts->partition_size : 0, &chunk_tokens));
   const int64_t max_blocks = block_tables->shape[1];
-  const SplitPlan sp = plan_split(B, Hq, D, max_blocks, part_tokens);
+  DecodePlan dp;
+  VP_TRY(plan_decode(B, Hq, Hkv, D, max_blocks, chunk_tokens, &dp));
   if (B == 0) return ok();
-  if (sp.num_parts > 1 && opts && opts->workspace && opts->workspace_bytes < sp.bytes)
-    return fail(VLLM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, sp.bytes);
+  if (opts && opts->workspace && opts->workspace_bytes < dp.bytes)
+    return fail(VLLM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, dp.bytes);
   VP_TRY(check_data(q, "q", 16));
-  VP_TRY(check_data(out, "out", 2));
+  VP_TRY(check_data(out, "out", 16));
   VP_TRY(check_data(k_cache, "k_cache", fp8 ? 8 : 16));
   VP_TRY(check_data(v_cache, "v_cache", fp8 ? 8 : 16));
   VP_TRY(check_data(block_tables, "block_tables", 4));
   VP_TRY(check_data(context_lens, "context_lens", 4));
 
   hipStream_t stream = (hipStream_t)hip_stream;
+  const int kv_fmt = fmt_of(k_cache->dtype), q_fmt = fmt_of(q->dtype);
   vp::DecodeParams p{};
   p.q = q->data;
   p.out = out->data;
@@ -354,31 +375,40 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
   p.num_q_heads = (int32_t)Hq;
   p.num_kv_heads = (int32_t)Hkv;
   p.group = (int32_t)(Hq / Hkv);
+  p.head_chunk = dp.head_chunk;
   p.bt_stride = (int32_t)max_blocks;
   p.num_blocks = (int32_t)NB;
-  p.num_parts = sp.num_parts;
-  p.part_pages = sp.part_pages;
   p.window = window;
+  p.chunk_pages = dp.chunk_pages;
+  p.max_chunks = (int32_t)dp.max_chunks;
+  p.num_workers = dp.chunk_pages > 0
+                      ? (int32_t)std::min<int64_t>(dp.max_chunks,
+                                                   vp::decode_workers(dp.pages_bound, (int)D, kv_fmt,
+                                                                      q_fmt, dp.head_chunk))
+                      : vp::decode_workers(dp.pages_bound, (int)D, kv_fmt, q_fmt, dp.head_chunk);
+  p.num_workers = std::max<int32_t>(vp::kDecodeWaves,
+                                    (p.num_workers + vp::kDecodeWaves - 1) / vp::kDecodeWaves *
+                                        vp::kDecodeWaves);
   p.score_scale = scale * 1.4426950408889634f * ks;
   p.out_scale = vs;
 
   void* ws = nullptr;
   bool owned = false;
-  if (sp.num_parts > 1) {
-    if (opts && opts->workspace) {
-      ws = opts->workspace;
-      VP_TRY(check_align(ws, "workspace", 256));
-      VP_TRY(check_device_ptr(ws, "workspace"));
-    } else {
-      VP_TRY(hip_status(hipMallocAsync(&ws, sp.bytes, stream), "workspace hipMallocAsync"));
-      owned = true;
-    }
-    char* base = static_cast<char*>(ws);
-    p.ws_o = reinterpret_cast<float*>(base + sp.o_off);
-    p.ws_m = reinterpret_cast<float*>(base + sp.m_off);
-    p.ws_l = reinterpret_cast<float*>(base + sp.l_off);
+  if (opts && opts->workspace) {
+    ws = opts->workspace;
+    VP_TRY(check_align(ws, "workspace", 256));
+    VP_TRY(check_device_ptr(ws, "workspace"));
+  } else {
+    VP_TRY(hip_status(hipMallocAsync(&ws, dp.bytes, stream), "workspace hipMallocAsync"));
+    owned = true;
   }
-  hipError_t e = vp::launch_decode(p, (int)D, fmt_of(k_cache->dtype), fmt_of(q->dtype), stream);
+  char* base = static_cast<char*>(ws);
+  p.ws_unit = reinterpret_cast<int32_t*>(base + dp.cnt_off);
+  p.ws_prefix = reinterpret_cast<int32_t*>(base + dp.pre_off);
+  p.ws_o = reinterpret_cast<float*>(base + dp.o_off);
+  p.ws_m = reinterpret_cast<float*>(base + dp.m_off);
+  p.ws_l = reinterpret_cast<float*>(base + dp.l_off);
+  hipError_t e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
   if (owned) {
     hipError_t e2 = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = e2;

@@ -3,42 +3,73 @@
 // attention over the block-paged KV cache of the vllm.cpp model forward,
 // repository listing "What's implemented"; 16-token FP16/FP8 pages and block
 // tables bound to shared physical pages, "Building and Deploying vllm.cpp",
-// Step 3).  The pages give no kernel design; this one is built for CDNA4:
+// Step 3).  The pages give no kernel design; this one is built for CDNA4.
 //
-//  * Work unit = (sequence, kv-head, up to 8 query heads of its group,
-//    partition of at most 64 pages).  NW = 4 waves split the partition's
-//    pages round-robin; each page is one 16-token slice of one kv-head, 16*D
-//    contiguous elements.
-//  * Every lane issues 8-element (16 B for 16-bit, 8 B for FP8) loads; a wave
-//    load instruction covers 64*8 contiguous elements (TPI token rows), fully
-//    coalesced.  Lane (r, c) holds elements [8c, 8c+8) of token rows
-//    r, r+TPI, ... of the page.  The next page's K and V are in flight while
-//    the current one is computed (register double buffering).
-//  * Q.K: the lane's 8-element slices go through packed dot2 (fp16 or bf16
-//    pairs; FP8 codes are first converted exactly to q's 16-bit format), then
-//    a DPP butterfly over the D/8 lanes of a token row gives every lane the
-//    full dot products of its row for all query heads of the group.
-//  * Online softmax in fp32, log2 domain.  The running max is only moved when
-//    a new score exceeds it by more than 2^8 headroom (or on the first page),
-//    so the accumulator is rarely rescaled; exact up to rounding.  Keys
-//    outside [max(0, n - window), n) are skipped, never multiplied by zero:
-//    their score is -inf and their V slice is replaced by zeros, so NaN
-//    garbage in unused page rows cannot leak.
-//  * P.V: fp32 FMAs of each probability with the lane's 8 V elements.
-//  * End: token-row states are merged across lanes (xor shuffles), then
-//    across waves through LDS, and the result is either the final output
-//    (one partition) or a (max, sum, normalized output) triple per
-//    partition, merged by decode_reduce_kernel with the log-sum-exp rule.
+// Work split (equal work per wave).  A work unit is (sequence, kv-head,
+// up to 8 query heads of its group); unit u holds the np(s) pages of its
+// sequence's kept range.  All pages of all units are laid end to end in
+// (sequence, unit, page) order, T pages in total, and cut into chunks of C
+// pages; each wave takes one chunk (C = ceil(T / waves)), so every wave
+// streams the same number of pages whatever the context lengths are.  A
+// chunk covers the tail of one unit, whole units, and the head of another;
+// a unit finished inside one chunk writes its output directly; each piece
+// of a unit cut by chunk boundaries writes a (max, sum, normalized output)
+// triple to the workspace, and decode_merge_kernel (launched right after)
+// merges them with the log-sum-exp rule.  The per-sequence page prefix is
+// computed by every workgroup with a block-wide scan.
+//
+// Inside a wave, per 16-token page of one kv-head (CH = D/8 chunks of 8
+// elements per token row):
+//  * K role: LPR lanes share a token row; load instruction k gives lane
+//    (rho, c) chunk (k % CPL) * LPR + c of row (k / CPL) * RPI + rho, so the
+//    LPR lanes of a row read LPR adjacent chunks.  Packed dot2 (fp16 or bf16
+//    pairs; FP8 codes are first converted exactly to q's format) gives
+//    partial dot products, summed over the LPR lanes with DPP.
+//  * Online softmax in fp32, log2 domain, with a running max that is uniform
+//    over the wave and only moves when a score exceeds it by more than 2^8
+//    (one wave vote per page).  Keys outside [max(0, n - window), n) get
+//    score -inf and their V rows are replaced by zeros: NaN garbage in the
+//    unused rows of a page never reaches the output.
+//  * The probabilities, rounded to q's 16-bit format, go through a small
+//    per-wave LDS buffer to the V role: CH lanes share a V row, one chunk
+//    each, so every wave load reads 64 contiguous chunks.  Rows of two
+//    consecutive load instructions are paired so that P.V runs on packed
+//    dot2 (v[t1][e], v[t2][e]) . (p[t1][h], p[t2][h]) with fp32
+//    accumulation; the row sums use the same rounded probabilities.
+//  * The next page's K is loaded as soon as Q.K has consumed the registers,
+//    and the next V as soon as P.V has; these loads are unconditional (past
+//    the end they re-read the last page) so that the compiler can keep the
+//    buffers in flight across iterations.
+#include <cstdlib>
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace vp {
 
-constexpr int kNW = 4;         // waves per workgroup
-constexpr float kTau = 8.0f;   // rescale headroom, log2 units
+constexpr int kNW = kDecodeWaves;
+constexpr float kTau = 8.0f;       // rescale headroom, log2 units
+constexpr int kScanMax = 2048;     // sequences whose page prefix fits in LDS
 
 template <int KF> struct KvChunk { using T = uint4; };      // 8 x 16-bit
 template <> struct KvChunk<kE4M3> { using T = uint2; };     // 8 x fp8
+
+// Streaming (non-temporal) loads: every KV byte is read once per call.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ T ld_stream(const uint8_t* ptr);
+template <>
+__device__ __forceinline__ uint4 ld_stream<uint4>(const uint8_t* ptr) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <>
+__device__ __forceinline__ uint2 ld_stream<uint2>(const uint8_t* ptr) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ptr));
+  return make_uint2(v.x, v.y);
+}
 
 // 8 K elements -> 4 packed pairs in q's format.
 template <int KF, int QF>
@@ -58,340 +89,696 @@ __device__ __forceinline__ void k_pairs(const typename KvChunk<KF>::T& x, uint32
   }
 }
 
+// Two 16-bit values (low, high) of q's format from two floats, round to
+// nearest even (hardware conversions of gfx950).
 template <int QF>
-__device__ __forceinline__ float dot8(const uint4& q, const uint32_t (&k)[4]) {
-  float a = 0.0f;
-  if constexpr (QF == kF16) {
-    a = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.x), bitcast<half2_t>(k[0]), a, false);
-    a = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.y), bitcast<half2_t>(k[1]), a, false);
-    a = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.z), bitcast<half2_t>(k[2]), a, false);
-    a = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.w), bitcast<half2_t>(k[3]), a, false);
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (QF == kBF16) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return bitcast<uint32_t>(v);
   } else {
-    a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(q.x), bitcast<bf16x2_t>(k[0]), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(q.y), bitcast<bf16x2_t>(k[1]), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(q.z), bitcast<bf16x2_t>(k[2]), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(q.w), bitcast<bf16x2_t>(k[3]), a, false);
-  }
-  return a;
-}
-
-// 8 V elements -> fp32 (exact; FP8 codes stay in code units, v_scale is
-// applied once at the end).
-template <int KF>
-__device__ __forceinline__ void v_f32(const typename KvChunk<KF>::T& x, float (&f)[8]) {
-  if constexpr (KF == kE4M3) {
-    float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x.x, 1.0f, false);
-    float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x.x, 1.0f, true);
-    float2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x.y, 1.0f, false);
-    float2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x.y, 1.0f, true);
-    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
-    f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
-  } else {
-    x2_to_f32<KF>(x.x, f[0], f[1]);
-    x2_to_f32<KF>(x.y, f[2], f[3]);
-    x2_to_f32<KF>(x.z, f[4], f[5]);
-    x2_to_f32<KF>(x.w, f[6], f[7]);
+    half2_t v = {(_Float16)lo, (_Float16)hi};
+    return bitcast<uint32_t>(v);
   }
 }
 
-template <int D, int G, int KF, int QF>
+template <int QF>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (QF == kF16)
+    return __builtin_amdgcn_fdot2(bitcast<half2_t>(a), bitcast<half2_t>(b), c, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a), bitcast<bf16x2_t>(b), c, false);
+}
+
+// V elements of two tokens, paired per element for dot2: o[e] holds
+// (element e of token A, element e of token B) in q's 16-bit format.
+template <int KF, int QF>
+__device__ __forceinline__ void v_pairs(const typename KvChunk<KF>::T& a,
+                                        const typename KvChunk<KF>::T& b, uint32_t (&o)[8]) {
+  if constexpr (KF != kE4M3) {
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __builtin_amdgcn_perm(bw[i], aw[i], 0x05040100u);       // (a.lo, b.lo)
+      o[2 * i + 1] = __builtin_amdgcn_perm(bw[i], aw[i], 0x07060302u);   // (a.hi, b.hi)
+    }
+  } else {
+    const uint32_t aw[2] = {a.x, a.y};
+    const uint32_t bw[2] = {b.x, b.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      // byte interleave (a0, b0, a1, b1) and (a2, b2, a3, b3), then convert
+      // each byte pair exactly to two 16-bit values.
+      const uint32_t w01 = __builtin_amdgcn_perm(bw[i], aw[i], 0x05010400u);
+      const uint32_t w23 = __builtin_amdgcn_perm(bw[i], aw[i], 0x07030602u);
+      if constexpr (QF == kF16) {
+        o[4 * i + 0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, false));
+        o[4 * i + 1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, true));
+        o[4 * i + 2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, false));
+        o[4 * i + 3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, true));
+      } else {
+        o[4 * i + 0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w01, 1.0f, false));
+        o[4 * i + 1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w01, 1.0f, true));
+        o[4 * i + 2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w23, 1.0f, false));
+        o[4 * i + 3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w23, 1.0f, true));
+      }
+    }
+  }
+}
+
+template <int QF>
+__device__ __forceinline__ float lo16_to_f32(uint32_t w) {
+  if constexpr (QF == kBF16) return bitcast<float>(w << 16);
+  else return (float)bitcast<half2_t>(w).x;
+}
+template <int QF>
+__device__ __forceinline__ float hi16_to_f32(uint32_t w) {
+  if constexpr (QF == kBF16) return bitcast<float>(w & 0xFFFF0000u);
+  else return (float)bitcast<half2_t>(w).y;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Kept key range of a decode query and its page range.
+struct SeqRange {
+  int n, lo, lo_page, np;   // np = pages of the kept range (0 if n <= 0)
+};
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int s) {
+  SeqRange r;
+  r.n = min(p.context_lens[s], p.bt_stride * 16);
+  if (r.n <= 0) {
+    r.n = 0; r.lo = 0; r.lo_page = 0; r.np = 0;
+    return r;
+  }
+  r.lo = p.window > 0 ? max(0, r.n - p.window) : 0;
+  r.lo_page = r.lo >> 4;
+  r.np = ((r.n + 15) >> 4) - r.lo_page;
+  return r;
+}
+
+// Exclusive prefix of np(s) over the batch, computed by one workgroup of
+// kNW * 64 threads into pre[0 .. B] (pre[B] = total).
+__device__ void page_prefix(const DecodeParams& p, int* pre) {
+  __shared__ int s_tot[kNW * 64];
+  const int B = p.num_seqs;
+  const int nt = kNW * 64;
+  const int per = (B + nt - 1) / nt;
+  const int t = threadIdx.x;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = t * per + i;
+    if (s < B) sum += seq_range(p, s).np;
+  }
+  s_tot[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {       // inclusive Hillis-Steele scan
+    const int v = t >= off ? s_tot[t - off] : 0;
+    __syncthreads();
+    s_tot[t] += v;
+    __syncthreads();
+  }
+  int run = t > 0 ? s_tot[t - 1] : 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = t * per + i;
+    if (s < B) {
+      pre[s] = run;
+      run += seq_range(p, s).np;
+    }
+  }
+  if (t == nt - 1) pre[B] = s_tot[t];
+  __syncthreads();
+}
+
+// Waves per SIMD the decode kernel is compiled for (caps its registers).
+template <int G>
+constexpr int kWavesPerSimd = G <= 4 ? 4 : (G <= 6 ? 3 : 2);
+
+template <int D, int G, int KF, int QF, int LPR, int PD>
 __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
-  constexpr int CH = D / 8;            // lanes per token row
-  constexpr int TPI = 64 / CH;         // token rows per wave load instruction
-  constexpr int NK = 16 / TPI;         // load instructions per page (K or V)
+  constexpr int CH = D / 8;
+  static_assert(LPR >= 4 && LPR <= CH, "lanes per K row");
+  constexpr int CPL = CH / LPR;          // chunks per lane per K row
+  constexpr int RPI = 64 / LPR;          // K rows per load instruction
+  constexpr int NKI = CH / 4;            // load instructions per page (K or V)
+  constexpr int TPL = 16 / RPI;          // K rows per lane per page
+  constexpr int RPIV = 64 / CH;          // V rows per load instruction
+  static_assert(NKI % 2 == 0, "V rows are paired");
+  constexpr int GW = (G + 1) / 2;        // dwords of packed probabilities per token
   using LT = typename KvChunk<KF>::T;
-  constexpr int EB = (KF == kE4M3) ? 1 : 2;
-  constexpr int kInstrBytes = 64 * 8 * EB;
-  constexpr int64_t kPageBytes = 16 * D * EB;
+  constexpr int CB = (int)sizeof(LT);    // bytes per 8-element chunk
+  constexpr int ROWB = CH * CB;
+  constexpr int64_t kPageBytes = 16 * ROWB;
 
-  __shared__ float s_acc[kNW][G][D];
-  __shared__ float s_m[kNW][G];
-  __shared__ float s_l[kNW][G];
+  __shared__ int s_pre[kScanMax + 1];
+  __shared__ uint32_t s_p[kNW][16][GW];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int r = lane / CH;
-  const int c = lane % CH;
-  const int part = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rho = lane / LPR, c = lane % LPR;          // K role
+  const int rv = lane / CH, cv = lane % CH;            // V role
+  const int B = p.num_seqs;
   const int ngc = p.group / G;
-  const int hk = blockIdx.y / ngc;
-  const int h0 = hk * p.group + (blockIdx.y - hk * ngc) * G;
-  const int s = blockIdx.z;
+  const int NY = p.num_kv_heads * ngc;                 // units per sequence
 
-  const int n = min(p.context_lens[s], p.bt_stride * 16);
-  if (n <= 0) {
-    if (p.num_parts == 1) {   // single pass: nobody else writes this row
-      uint16_t* o = static_cast<uint16_t*>(p.out) + ((int64_t)s * p.num_q_heads + h0) * D;
-      for (int i = threadIdx.x; i < G * D; i += kNW * 64) o[i] = 0;
+  // Page prefix over the batch: in LDS for small batches (workgroup 0 also
+  // stores it for the merge), else precomputed in the workspace.
+  const int* pre;
+  if (B <= kScanMax) {
+    page_prefix(p, s_pre);
+    pre = s_pre;
+  } else {
+    pre = p.ws_prefix;
+  }
+  const int64_t T = (int64_t)NY * __builtin_amdgcn_readfirstlane(pre[B]);
+  const int64_t C = p.chunk_pages > 0 ? p.chunk_pages
+                                      : max((int64_t)1, (T + p.num_workers - 1) / p.num_workers);
+  const int64_t num_chunks = (T + C - 1) / C;
+
+  // Sequences with no key to attend to get all-zero output rows.
+  for (int sq = blockIdx.x; sq < B; sq += gridDim.x) {
+    if (pre[sq + 1] == pre[sq]) {
+      uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)sq * p.num_q_heads * D;
+      for (int i = threadIdx.x; i < p.num_q_heads * D; i += kNW * 64) o[i] = 0;
+      for (int i = threadIdx.x; i < NY; i += kNW * 64) p.ws_unit[((int64_t)sq * NY + i) * 2 + 1] = 0;
     }
-    return;
-  }
-  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
-  const int lo_page = lo >> 4;
-  const int hi_page = (n + 15) >> 4;
-  const int first = max(lo_page, part * p.part_pages);
-  const int last = min(hi_page, (part + 1) * p.part_pages);
-  if (first >= last) return;
-  const int p_lo = lo_page / p.part_pages;
-  const int p_hi = (hi_page + p.part_pages - 1) / p.part_pages;
-  const bool direct = (p_hi - p_lo) == 1;
-  const int npages = last - first;
-
-  // Query slices of the G heads: elements [8c, 8c+8) of each.
-  uint4 qv[G];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)s * p.num_q_heads + h0) * D + c * 8;
-#pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const uint4*>(qp + h * D);
-  }
-  // Physical page ids of this partition, one per lane.
-  int bt_lane = 0;
-  if (lane < npages) {
-    bt_lane = p.block_tables[(int64_t)s * p.bt_stride + first + lane];
-    if ((unsigned)bt_lane >= (unsigned)p.num_blocks) bt_lane = 0;
   }
 
-  const uint8_t* kbase = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes + lane * (int)sizeof(LT);
-  const uint8_t* vbase = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes + lane * (int)sizeof(LT);
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
+  int koff[NKI];
+#pragma unroll
+  for (int k = 0; k < NKI; ++k)
+    koff[k] = ((k / CPL) * RPI + rho) * ROWB + ((k % CPL) * LPR + c) * CB;
 
-  auto load_page = [&](int j, LT (&kd)[NK], LT (&vd)[NK]) {
-    const int blk = __builtin_amdgcn_readlane(bt_lane, j);
-    const uint8_t* kp = kbase + blk * blk_stride;
-    const uint8_t* vq = vbase + blk * blk_stride;
-#pragma unroll
-    for (int k = 0; k < NK; ++k) kd[k] = *reinterpret_cast<const LT*>(kp + k * kInstrBytes);
-#pragma unroll
-    for (int k = 0; k < NK; ++k) vd[k] = *reinterpret_cast<const LT*>(vq + k * kInstrBytes);
-  };
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-  }
-
-  auto process = [&](const LT (&kd)[NK], const LT (&vd)[NK], int pg) {
-    float sc[NK][G];
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      uint32_t kw[4];
-      k_pairs<KF, QF>(kd[k], kw);
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[k][h] = dot8<QF>(qv[h], kw);
+  for (int64_t chunk = (int64_t)blockIdx.x * kNW + wave; chunk < num_chunks;
+       chunk += p.num_workers) {
+    int64_t g = chunk * C;
+    const int64_t g_end = min(g + C, T);
+    // sequence holding global page g: last s with NY * pre[s] <= g
+    int s = 0;
+    {
+      int lo_s = 0, hi_s = B - 1;
+      while (lo_s < hi_s) {
+        const int mid = (lo_s + hi_s + 1) >> 1;
+        if ((int64_t)NY * __builtin_amdgcn_readfirstlane(pre[mid]) <= g) lo_s = mid; else hi_s = mid - 1;
+      }
+      s = lo_s;
     }
-#pragma unroll
-    for (int k = 0; k < NK; ++k)
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[k][h] = group_sum<CH>(sc[k][h]);
+    bool first_seg = true;
+    while (g < g_end) {
+      // (values read from LDS are wave-uniform: keep them in scalar registers)
+      while ((int64_t)NY * __builtin_amdgcn_readfirstlane(pre[s + 1]) <= g) ++s;   // skip empty seqs
+      const SeqRange sr = seq_range(p, s);
+      const int64_t off = g - (int64_t)NY * __builtin_amdgcn_readfirstlane(pre[s]);
+      const int y = (int)(off / sr.np);
+      const int i0 = (int)(off - (int64_t)y * sr.np);
+      const int i1 = (int)min((int64_t)sr.np, i0 + (g_end - g));
+      const int slot = first_seg ? 0 : 1;
+      const bool complete = (i0 == 0) && (i1 == sr.np);
+      const int hk = y / ngc;
+      const int h0 = hk * p.group + (y - hk * ngc) * G;
 
-    const int t0 = pg * 16;
-    const bool full = (t0 >= lo) && (t0 + 16 <= n);
-    float pm[G];
+      // ---- one segment: pages [i0, i1) of unit (s, y) ----
+      uint4 qv[G][CPL];
+      {
+        const uint16_t* qp =
+            static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.num_q_heads + h0) * D;
 #pragma unroll
-    for (int h = 0; h < G; ++h) pm[h] = -INFINITY;
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      const int t = t0 + k * TPI + r;
-      const bool ok = full || (t >= lo && t < n);
+          for (int sub = 0; sub < CPL; ++sub)
+            qv[h][sub] = *reinterpret_cast<const uint4*>(qp + h * D + (sub * LPR + c) * 8);
+      }
+      const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride + sr.lo_page;
+      const uint8_t* kbase = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
+      const uint8_t* vbase = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes +
+                             rv * ROWB + cv * CB;
+      const int count = i1 - i0;
+      // Block ids, 64 pages per lane vector; the next 64 are fetched one
+      // batch ahead so that reading them never waits on the page loads.
+      int bt_base = 0;
+      auto bt_fetch = [&](int base) __attribute__((always_inline)) {
+        const int q = i0 + base + lane;
+        int b = q < i1 ? bt[q] : 0;
+        return (unsigned)b < (unsigned)p.num_blocks ? b : 0;
+      };
+      int bt_cur = bt_fetch(0), bt_nxt = count > 64 ? bt_fetch(64) : 0;
+      auto blk_of = [&](int jj) __attribute__((always_inline)) {
+        if (jj >= bt_base + 64) {          // pages are requested in increasing order
+          bt_base += 64;
+          bt_cur = bt_nxt;
+          if (bt_base + 64 < count) bt_nxt = bt_fetch(bt_base + 64);
+        }
+        return __builtin_amdgcn_readlane(bt_cur, jj - bt_base);
+      };
+      auto load_k = [&](int blk, LT (&kd)[NKI]) __attribute__((always_inline)) {
+        const uint8_t* kp = kbase + blk * blk_stride;
+#pragma unroll
+        for (int k = 0; k < NKI; ++k) kd[k] = ld_stream<LT>(kp + koff[k]);
+      };
+      auto load_v = [&](int blk, LT (&vd)[NKI]) __attribute__((always_inline)) {
+        const uint8_t* vp = vbase + blk * blk_stride;
+#pragma unroll
+        for (int k = 0; k < NKI; ++k) vd[k] = ld_stream<LT>(vp + k * RPIV * ROWB);
+      };
+
+      float m[G], l[G], acc[G][8];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float x = ok ? sc[k][h] * p.score_scale : -INFINITY;
-        sc[k][h] = x;
-        pm[h] = fmaxf(pm[h], x);
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
       }
-    }
-    bool need = false;
+      // PD pages of K and V in flight: buffer u holds page jb + u.  Loads are
+      // unconditional (past the end they re-read the last page) so that no
+      // buffer goes through a control-flow merge.
+      LT kd[PD][NKI], vd[PD][NKI];
 #pragma unroll
-    for (int h = 0; h < G; ++h) need |= pm[h] > m[h] + kTau;
-    if (need) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], pm[h]);
-        const float alpha = (m[h] == -INFINITY) ? 0.0f : fast_exp2(m[h] - mn);
-        l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-        m[h] = mn;
+      for (int u = 0; u < PD; ++u) {
+        const int b0 = blk_of(min(u, count - 1));
+        load_k(b0, kd[u]);
+        load_v(b0, vd[u]);
       }
-    }
-    float ms[G];
+      for (int jb = 0; jb < count; jb += PD) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) ms[h] = (m[h] == -INFINITY) ? 0.0f : m[h];
+        for (int u = 0; u < PD; ++u) {
+          const int jj = jb + u;
+          const bool valid = jj < count;
+          const int t0 = (sr.lo_page + i0 + min(jj, count - 1)) * 16;
+          const bool full = (t0 >= sr.lo) && (t0 + 16 <= sr.n);
+          const int bn = blk_of(min(jj + PD, count - 1));
+          float sc[TPL][G];
+          if (valid) {
+            // ---- Q.K (K role) ----
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      float pk[G];
+            for (int rg = 0; rg < TPL; ++rg)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        pk[h] = fast_exp2(sc[k][h] - ms[h]);
-        l[h] += pk[h];
-      }
-      float vf[8];
-      v_f32<KF>(vd[k], vf);
-      if (!full) {
-        const int t = t0 + k * TPI + r;
-        if (!(t >= lo && t < n)) {
+              for (int h = 0; h < G; ++h) sc[rg][h] = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = 0.0f;
+            for (int k = 0; k < NKI; ++k) {
+              uint32_t kw[4];
+              k_pairs<KF, QF>(kd[u][k], kw);
+#pragma unroll
+              for (int h = 0; h < G; ++h) {
+                const uint4 qq = qv[h][k % CPL];
+                float a = sc[k / CPL][h];
+                a = dot2<QF>(qq.x, kw[0], a);
+                a = dot2<QF>(qq.y, kw[1], a);
+                a = dot2<QF>(qq.z, kw[2], a);
+                a = dot2<QF>(qq.w, kw[3], a);
+                sc[k / CPL][h] = a;
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          load_k(bn, kd[u]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (valid) {
+#pragma unroll
+            for (int rg = 0; rg < TPL; ++rg)
+#pragma unroll
+              for (int h = 0; h < G; ++h) sc[rg][h] = group_sum<LPR>(sc[rg][h]) * p.score_scale;
+            if (!full) {
+#pragma unroll
+              for (int rg = 0; rg < TPL; ++rg) {
+                const int t = t0 + rg * RPI + rho;
+                if (t < sr.lo || t >= sr.n) {
+#pragma unroll
+                  for (int h = 0; h < G; ++h) sc[rg][h] = -INFINITY;
+                }
+              }
+            }
+
+            // ---- online softmax ----
+            bool need = false;
+#pragma unroll
+            for (int rg = 0; rg < TPL; ++rg)
+#pragma unroll
+              for (int h = 0; h < G; ++h) need |= sc[rg][h] > m[h] + kTau;
+            if (__any(need)) {
+#pragma unroll
+              for (int h = 0; h < G; ++h) {
+                float pm = sc[0][h];
+#pragma unroll
+                for (int rg = 1; rg < TPL; ++rg) pm = fmaxf(pm, sc[rg][h]);
+                pm = wave_max(pm);
+                const float mn = fmaxf(m[h], pm);
+                const float alpha = (m[h] == -INFINITY) ? 0.0f : fast_exp2(m[h] - mn);
+                m[h] = mn;
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+              }
+            }
+#pragma unroll
+            for (int rg = 0; rg < TPL; ++rg) {
+              uint32_t pw[GW];
+#pragma unroll
+              for (int i = 0; i < GW; ++i) {
+                const int ha = 2 * i, hb = 2 * i + 1;
+                const float ma = (m[ha] == -INFINITY) ? 0.0f : m[ha];
+                const float pa = fast_exp2(sc[rg][ha] - ma);
+                float pb = 0.0f;
+                if (hb < G) {
+                  const float mb = (m[hb] == -INFINITY) ? 0.0f : m[hb];
+                  pb = fast_exp2(sc[rg][hb] - mb);
+                }
+                pw[i] = pack16<QF>(pa, pb);
+                l[ha] += lo16_to_f32<QF>(pw[i]);
+                if (hb < G) l[hb] += hi16_to_f32<QF>(pw[i]);
+              }
+              if (c == 0) {
+#pragma unroll
+                for (int i = 0; i < GW; ++i) s_p[wave][rg * RPI + rho][i] = pw[i];
+              }
+            }
+
+            // ---- P.V (V role) ----
+            auto pv = [&](const LT (&vx)[NKI]) __attribute__((always_inline)) {
+#pragma unroll
+              for (int pr = 0; pr < NKI / 2; ++pr) {
+                const int ta = (2 * pr) * RPIV + rv, tb = (2 * pr + 1) * RPIV + rv;
+                uint32_t vp2[8];
+                v_pairs<KF, QF>(vx[2 * pr], vx[2 * pr + 1], vp2);
+                uint32_t pp[G];
+#pragma unroll
+                for (int i = 0; i < GW; ++i) {
+                  const uint32_t A = s_p[wave][ta][i], B2 = s_p[wave][tb][i];
+                  pp[2 * i] = __builtin_amdgcn_perm(B2, A, 0x05040100u);
+                  if (2 * i + 1 < G) pp[2 * i + 1] = __builtin_amdgcn_perm(B2, A, 0x07060302u);
+                }
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) acc[h][e] = dot2<QF>(pp[h], vp2[e], acc[h][e]);
+              }
+            };
+            if (full) {
+              pv(vd[u]);
+            } else {
+              // rows outside the kept range may hold NaN: replace them by zeros
+              LT vv[NKI];
+#pragma unroll
+              for (int k = 0; k < NKI; ++k) {
+                const int t = t0 + k * RPIV + rv;
+                vv[k] = (t < sr.lo || t >= sr.n) ? LT{} : vd[u][k];
+              }
+              pv(vv);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          load_v(bn, vd[u]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pk[h], vf[e], acc[h][e]);
-    }
-  };
 
-  {
-    LT ka[NK], va[NK], kb[NK], vb[NK];
-    int j = wave;
-    if (j < npages) load_page(j, ka, va);
-    while (j < npages) {
-      int jn = j + kNW;
-      if (jn < npages) load_page(jn, kb, vb);
-      process(ka, va, first + j);
-      j = jn;
-      if (j >= npages) break;
-      jn = j + kNW;
-      if (jn < npages) load_page(jn, ka, va);
-      process(kb, vb, first + j);
-      j = jn;
-    }
-  }
+      // Sum the V rows (lanes cv, cv + CH, ...) and the K-role row sums (one
+      // lane per row: c == 0).  m is uniform over the wave.
+#pragma unroll
+      for (int off = CH; off < 64; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+#pragma unroll
+      for (int h = 0; h < G; ++h) l[h] = wave_sum(c == 0 ? l[h] : 0.0f);
 
-  // Merge the TPI token-row states of the wave (lanes c, c+CH, c+2CH, ...).
+      if (complete) {
+        if (rv == 0) {
 #pragma unroll
-  for (int off = CH; off < 64; off <<= 1) {
+          for (int h = 0; h < G; ++h) {
+            const float inv = p.out_scale / l[h];
+            uint32_t w[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float m2 = __shfl_xor(m[h], off);
-      const float l2 = __shfl_xor(l[h], off);
-      const float mn = fmaxf(m[h], m2);
-      const float f1 = (m[h] == -INFINITY) ? 0.0f : fast_exp2(m[h] - mn);
-      const float f2 = (m2 == -INFINITY) ? 0.0f : fast_exp2(m2 - mn);
-      l[h] = l[h] * f1 + l2 * f2;
+            for (int i = 0; i < 4; ++i)
+              w[i] = (uint32_t)f32_to_16<QF>(acc[h][2 * i] * inv) |
+                     ((uint32_t)f32_to_16<QF>(acc[h][2 * i + 1] * inv) << 16);
+            uint16_t* o = static_cast<uint16_t*>(p.out) +
+                          ((int64_t)s * p.num_q_heads + h0 + h) * D + cv * 8;
+            *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      } else {
+        const int64_t sl = chunk * 2 + slot;
+        if (rv == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * f1 + __shfl_xor(acc[h][e], off) * f2;
-      m[h] = mn;
-    }
-  }
-  if (r == 0) {
+          for (int h = 0; h < G; ++h) {
+            const float inv = 1.0f / l[h];
+            float* o = p.ws_o + (sl * G + h) * D + cv * 8;
+            *reinterpret_cast<float4*>(o) =
+                make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+            *reinterpret_cast<float4*>(o + 4) =
+                make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+          }
+        }
+        if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][h][c * 8 + e] = acc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_m[wave][h] = m[h];
-      s_l[wave][h] = l[h];
-    }
-  }
-  __syncthreads();
-
-  // Merge the waves; one thread per output element.
-  for (int i = threadIdx.x; i < G * D; i += kNW * 64) {
-    const int h = i / D;
-    const int d = i - h * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_m[w][h]);
-    float den = 0.0f, num = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      const float f = (s_m[w][h] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][h] - M);
-      den = fmaf(s_l[w][h], f, den);
-      num = fmaf(s_acc[w][h][d], f, num);
-    }
-    const int64_t row = (int64_t)s * p.num_q_heads + h0 + h;
-    if (direct) {
-      static_cast<uint16_t*>(p.out)[row * D + d] = f32_to_16<QF>(num / den * p.out_scale);
-    } else {
-      p.ws_o[(row * p.num_parts + part) * D + d] = num / den;
-      if (d == 0) {
-        p.ws_m[row * p.num_parts + part] = M;
-        p.ws_l[row * p.num_parts + part] = den;
+          for (int h = 0; h < G; ++h) {
+            p.ws_m[sl * G + h] = m[h];
+            p.ws_l[sl * G + h] = l[h];
+          }
+        }
       }
+      // The wave holding page 0 of the unit records where its pieces are:
+      // (slot of the first piece, number of pieces), or 0 pieces if done.
+      if (i0 == 0 && lane == 0) {
+        int npieces = 0;
+        if (!complete) {
+          const int64_t base = g;                 // = NY * pre[s] + y * np
+          npieces = (int)((base + sr.np - 1) / C - base / C + 1);
+        }
+        p.ws_unit[((int64_t)s * NY + y) * 2] = (int32_t)(chunk * 2 + slot);
+        p.ws_unit[((int64_t)s * NY + y) * 2 + 1] = npieces;
+      }
+      g += i1 - i0;
+      first_seg = false;
     }
   }
 }
 
-// Log-sum-exp merge of the partition triples of one (sequence, query head).
-template <int D, int QF>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int d = threadIdx.x;
-  const int64_t row = (int64_t)s * p.num_q_heads + h;
-  uint16_t* o = static_cast<uint16_t*>(p.out) + row * D + d;
-  const int n = min(p.context_lens[s], p.bt_stride * 16);
-  if (n <= 0) {
-    *o = 0;
-    return;
+// Log-sum-exp merge of the pieces of units cut by chunk boundaries.  One
+// workgroup per unit; the unit's record (first slot, piece count) comes from
+// the decode kernel.  All loads of a round are independent: each thread
+// fetches the (max, sum) of one piece and, for its output elements, the
+// normalized outputs of up to kMergeBatch pieces.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 32;        // pieces merged per round
+
+template <int D, int G, int QF>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
+  constexpr int R = (G * D + kMergeThreads - 1) / kMergeThreads;   // outputs per thread
+  __shared__ float s_m[kMergeBatch][G], s_l[kMergeBatch][G];
+  const int ngc = p.group / G;
+  const int NY = p.num_kv_heads * ngc;
+  const int u = blockIdx.x;
+  const int npieces = p.ws_unit[(int64_t)u * 2 + 1];
+  if (npieces == 0) return;                   // finished inside one chunk, or empty
+  const int64_t sl0 = p.ws_unit[(int64_t)u * 2];
+  const int64_t fk = sl0 >> 1;
+  const int s = u / NY;
+  const int y = u - s * NY;
+  const int hk = y / ngc;
+  const int h0 = hk * p.group + (y - hk * ngc) * G;
+  uint16_t* out = static_cast<uint16_t*>(p.out) + ((int64_t)s * p.num_q_heads + h0) * D;
+  const int t = threadIdx.x;
+  auto slot = [&](int k) __attribute__((always_inline)) { return k == 0 ? sl0 : (fk + k) * 2; };
+
+  float M[G], den[G], acc[R];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { M[h] = -INFINITY; den[h] = 0.0f; }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int k0 = 0; k0 < npieces; k0 += kMergeBatch) {
+    const int cnt = min(kMergeBatch, npieces - k0);
+    if (t < cnt * G) {
+      const int k = t / G, h = t - k * G;
+      const int64_t i = slot(k0 + k) * G + h;
+      s_m[k][h] = p.ws_m[i];
+      s_l[k][h] = p.ws_l[i];
+    }
+    float o[R][kMergeBatch];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = min(t + r * kMergeThreads, G * D - 1);
+      const int h = e / D, d = e - h * D;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k)
+        o[r][k] = k < cnt ? p.ws_o[(slot(k0 + k) * G + h) * D + d] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float Mn = M[h];
+      for (int k = 0; k < cnt; ++k) Mn = fmaxf(Mn, s_m[k][h]);
+      const float a = (M[h] == -INFINITY) ? 0.0f : fast_exp2(M[h] - Mn);
+      den[h] *= a;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (min(t + r * kMergeThreads, G * D - 1) / D == h) acc[r] *= a;
+      M[h] = Mn;
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (k < cnt) {
+        float w[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          w[h] = s_l[k][h] * fast_exp2(s_m[k][h] - M[h]);
+          den[h] += w[h];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int h = min(t + r * kMergeThreads, G * D - 1) / D;
+          acc[r] = fmaf(w[h], o[r][k], acc[r]);
+        }
+      }
+    }
+    __syncthreads();
   }
-  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
-  const int p_lo = (lo >> 4) / p.part_pages;
-  const int p_hi = (((n + 15) >> 4) + p.part_pages - 1) / p.part_pages;
-  if (p_hi - p_lo == 1) return;   // written directly by decode_kernel
-  const float* mr = p.ws_m + row * p.num_parts;
-  const float* lr = p.ws_l + row * p.num_parts;
-  const float* orow = p.ws_o + row * p.num_parts * D + d;
-  float M = -INFINITY;
-  for (int q = p_lo; q < p_hi; ++q) M = fmaxf(M, mr[q]);
-  float den = 0.0f, num = 0.0f;
-  for (int q = p_lo; q < p_hi; ++q) {
-    const float w = lr[q] * fast_exp2(mr[q] - M);
-    den += w;
-    num = fmaf(w, orow[(int64_t)q * D], num);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = t + r * kMergeThreads;
+    if (e < G * D) out[e] = f32_to_16<QF>(acc[r] / den[e / D] * p.out_scale);
   }
-  *o = f32_to_16<QF>(num / den * p.out_scale);
+}
+
+// Page prefix for batches too large for the LDS scan of decode_kernel.
+__global__ __launch_bounds__(kNW * 64) void decode_prefix_kernel(DecodeParams p) {
+  page_prefix(p, p.ws_prefix);
+}
+
+// Lanes per K row: fewer lanes -> fewer cross-lane sums but more query
+// registers per lane (CH / LPR chunks per head).
+template <int D, int G>
+constexpr int kLpr = (D == 64) ? (G <= 4 ? 4 : 8) : (G <= 2 ? 4 : (G <= 5 ? 8 : 16));
+
+// Pages of K and V in flight per wave.
+template <int D, int G>
+constexpr int kPd = 2;
+
+template <int D, int G, int KF, int QF>
+static const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&decode_kernel<D, G, KF, QF, kLpr<D, G>, kPd<D, G>>);
 }
 
 template <int D, int KF, int QF>
-static hipError_t launch_dg(const DecodeParams& p, int gc, hipStream_t stream) {
-  dim3 grid(p.num_parts, p.num_kv_heads * (p.group / gc), p.num_seqs);
-  dim3 block(kNW * 64);
+static const void* pick(int gc) {
   switch (gc) {
-#define VP_G(GG) case GG: hipLaunchKernelGGL((decode_kernel<D, GG, KF, QF>), grid, block, 0, stream, p); break;
-    VP_G(1) VP_G(2) VP_G(3) VP_G(4) VP_G(5) VP_G(6) VP_G(7) VP_G(8)
-#undef VP_G
-    default: return hipErrorInvalidValue;
+    case 1: return kernel_ptr<D, 1, KF, QF>();
+    case 2: return kernel_ptr<D, 2, KF, QF>();
+    case 3: return kernel_ptr<D, 3, KF, QF>();
+    case 4: return kernel_ptr<D, 4, KF, QF>();
+    case 5: return kernel_ptr<D, 5, KF, QF>();
+    case 6: return kernel_ptr<D, 6, KF, QF>();
+    case 7: return kernel_ptr<D, 7, KF, QF>();
+    case 8: return kernel_ptr<D, 8, KF, QF>();
+    default: return nullptr;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.num_parts == 1) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<D, QF>), dim3(p.num_q_heads, p.num_seqs), dim3(D), 0, stream, p);
-  return hipGetLastError();
 }
 
-// Query heads handled per workgroup: the whole group when g <= 8, else the
-// largest divisor of g that is at most 8.
-static int head_chunk(int g) {
-  if (g <= 8) return g;
-  for (int c = 8; c > 1; --c)
-    if (g % c == 0) return c;
-  return 1;
+static const void* decode_kernel_for(int D, int kv_fmt, int q_fmt, int gc) {
+  if (D == 128) {
+    if (kv_fmt == kF16 && q_fmt == kF16) return pick<128, kF16, kF16>(gc);
+    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<128, kBF16, kBF16>(gc);
+    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<128, kE4M3, kF16>(gc);
+    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<128, kE4M3, kBF16>(gc);
+  } else if (D == 64) {
+    if (kv_fmt == kF16 && q_fmt == kF16) return pick<64, kF16, kF16>(gc);
+    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<64, kBF16, kBF16>(gc);
+    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<64, kE4M3, kF16>(gc);
+    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<64, kE4M3, kBF16>(gc);
+  }
+  return nullptr;
 }
 
-template <int D>
-static hipError_t launch_d(const DecodeParams& p, int kv_fmt, int q_fmt, hipStream_t stream) {
-  const int gc = head_chunk(p.group);
-  if (kv_fmt == kF16 && q_fmt == kF16) return launch_dg<D, kF16, kF16>(p, gc, stream);
-  if (kv_fmt == kBF16 && q_fmt == kBF16) return launch_dg<D, kBF16, kBF16>(p, gc, stream);
-  if (kv_fmt == kE4M3 && q_fmt == kF16) return launch_dg<D, kE4M3, kF16>(p, gc, stream);
-  if (kv_fmt == kE4M3 && q_fmt == kBF16) return launch_dg<D, kE4M3, kBF16>(p, gc, stream);
-  return hipErrorInvalidValue;
+template <int D, int QF>
+static const void* merge_for(int gc) {
+  switch (gc) {
+    case 1: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 1, QF>);
+    case 2: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 2, QF>);
+    case 3: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 3, QF>);
+    case 4: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 4, QF>);
+    case 5: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 5, QF>);
+    case 6: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 6, QF>);
+    case 7: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 7, QF>);
+    case 8: return reinterpret_cast<const void*>(&decode_merge_kernel<D, 8, QF>);
+    default: return nullptr;
+  }
+}
+
+static const void* merge_kernel_for(int D, int q_fmt, int gc) {
+  if (D == 128) return q_fmt == kBF16 ? merge_for<128, kBF16>(gc) : merge_for<128, kF16>(gc);
+  if (D == 64) return q_fmt == kBF16 ? merge_for<64, kBF16>(gc) : merge_for<64, kF16>(gc);
+  return nullptr;
+}
+
+int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk) {
+  static int cus = -1;
+  if (cus < 0) {
+    int dev = 0;
+    int v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      v = 256;
+    }
+    cus = v;
+  }
+  // workgroups resident per CU, queried once per kernel variant
+  static constexpr int kVariants = 2 * 3 * 2 * 8;
+  static int occ_cache[kVariants] = {0};
+  int per_cu = 4;
+  const int vi = ((head_dim == 128) * 3 + kv_fmt) * 16 + q_fmt * 8 + (head_chunk - 1);
+  if (vi >= 0 && vi < kVariants && occ_cache[vi] > 0) {
+    per_cu = occ_cache[vi];
+  } else if (const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, head_chunk)) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, kNW * 64, 0) == hipSuccess && occ > 0) {
+      per_cu = occ;
+      if (vi >= 0 && vi < kVariants) occ_cache[vi] = occ;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  if (const char* e = getenv("VLLM_PAGED_WG_PER_CU")) {
+    const int v = atoi(e);
+    if (v > 0) per_cu = v;
+  }
+  int64_t w = (int64_t)cus * per_cu * kNW;
+  const int64_t by_pages = (pages_bound + kMinChunkPages - 1) / kMinChunkPages;
+  w = min(w, max((int64_t)kNW, by_pages));
+  w = min(w, (int64_t)kMaxWorkers);
+  return (int)((w + kNW - 1) / kNW * kNW);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
-  if (head_dim == 128) return launch_d<128>(p, kv_fmt, q_fmt, stream);
-  if (head_dim == 64) return launch_d<64>(p, kv_fmt, q_fmt, stream);
-  return hipErrorInvalidValue;
+  const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, p.head_chunk);
+  const void* mk = merge_kernel_for(head_dim, q_fmt, p.head_chunk);
+  if (!k || !mk) return hipErrorInvalidValue;
+  DecodeParams a = p;
+  void* args[] = {&a};
+  if (p.num_seqs > kScanMax) {
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_prefix_kernel), dim3(1),
+                                   dim3(kNW * 64), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipLaunchKernel(k, dim3(p.num_workers / kNW), dim3(kNW * 64), args, 0, stream);
+  if (e != hipSuccess) return e;
+  const int units = p.num_seqs * p.num_kv_heads * (p.group / p.head_chunk);
+  return hipLaunchKernel(mk, dim3(units), dim3(kMergeThreads), args, 0, stream);
 }
 
 }  // namespace vp

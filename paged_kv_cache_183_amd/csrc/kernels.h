@@ -37,18 +37,22 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables; // [B, bt_stride]
   const int32_t* context_lens; // [B]
-  float* ws_o;                 // [B, Hq, num_parts, D]   (split-K only)
-  float* ws_m;                 // [B, Hq, num_parts]      running max, log2 units
-  float* ws_l;                 // [B, Hq, num_parts]      sum of exp2(s - m)
+  int32_t* ws_prefix;          // [B + 3]: pages before each sequence, then T, C
+  float* ws_o;                 // [2 * max_chunks, G, D] normalized partial outputs
+  float* ws_m;                 // [2 * max_chunks, G]    running max, log2 units
+  float* ws_l;                 // [2 * max_chunks, G]    sum of exp2(s - m)
+  int32_t* ws_unit;            // [B * units][2]: slot of the first piece, number of pieces
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;               // g = Hq / Hkv
+  int32_t head_chunk;          // query heads per work unit (G of the kernel)
   int32_t bt_stride;           // max_blocks_per_seq
   int32_t num_blocks;
-  int32_t num_parts;           // partitions per sequence (grid.x); 1 = single pass
-  int32_t part_pages;          // pages per partition
   int32_t window;              // 0 = off
+  int32_t num_workers;         // waves in the grid
+  int32_t chunk_pages;         // pages per chunk; 0 = ceil(T / num_workers)
+  int32_t max_chunks;          // capacity of the partial arrays (chunks)
   float score_scale;           // scale * log2(e) * k_scale
   float out_scale;             // v_scale (1 for 16-bit pools)
 };
@@ -78,7 +82,26 @@ struct PrefillParams {
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipStream_t stream);
 
-// Largest number of pages one decode partition may cover.
-constexpr int kMaxPartPages = 64;
+// Decode work split: at most this many waves, each taking at least
+// kMinChunkPages pages when the chunk size is automatic.
+constexpr int kMaxWorkers = 4096;
+constexpr int kMinChunkPages = 4;
+// Bytes at the start of a decode workspace for the per-unit piece records
+// (two int32 per unit).
+constexpr size_t kUnitBytes = size_t(1) << 20;
+// Waves per workgroup of the decode kernel.
+constexpr int kDecodeWaves = 4;
+
+// Query heads handled per decode work unit: the whole group when g <= 8,
+// else the largest divisor of g that is at most 8.
+inline int decode_head_chunk(int g) {
+  if (g <= 8) return g;
+  for (int c = 8; c > 1; --c)
+    if (g % c == 0) return c;
+  return 1;
+}
+
+// Workers (waves) the decode grid uses for an upper bound of the page count.
+int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk);
 
 }  // namespace vp

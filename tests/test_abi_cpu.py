@@ -89,7 +89,7 @@ def test_decode_validation():
     c["block_tables"] = c["block_tables"].long()
     _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_decode, **c)
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_decode, **{**a, "partition_size": 24})
-    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_decode, **{**a, "partition_size": 2048})
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_decode, **{**a, "partition_size": -16})
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_decode, **{**a, "scale": float("nan")})
     _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_attn_decode, **a)
     # split-K with a caller workspace that is too small
@@ -99,11 +99,21 @@ def test_decode_validation():
 
 
 def test_workspace_size():
-    # one partition covers the longest possible context -> single pass
-    assert P.vllm_paged_attn_workspace_size(4, 4, 2, 64, 3, 512) == 0
-    assert P.vllm_paged_attn_workspace_size(4, 4, 2, 64, 32, 512) == 0
-    ws = P.vllm_paged_attn_workspace_size(32, 32, 8, 128, 256, 512)    # 8 partitions
-    rows = 32 * 32 * 8
-    assert ws >= rows * (128 + 2) * 4
-    assert P.vllm_paged_attn_workspace_size(4, 3, 2, 64, 3, 0) == 0     # invalid -> 0
+    # piece records (2 ints per unit) + page prefix (B + 3 ints) + 2 pieces
+    # per chunk of G x (D + 2) floats, each region rounded up to 256 bytes
+    def expect(B, Hq, Hkv, D, mb, part):
+        g = Hq // Hkv
+        gc = g if g <= 8 else max(c for c in range(1, 9) if g % c == 0)
+        bound = B * Hkv * (g // gc) * mb
+        chunks = -(-bound // (part // 16)) if part else min(4096, -(-bound // 4))
+        chunks = max(chunks, 1)
+        up = lambda v: (v + 255) // 256 * 256
+        pieces = chunks * 2 * gc
+        units = B * Hkv * (g // gc)
+        return up(units * 8) + up((B + 3) * 4) + up(pieces * D * 4) + 2 * up(pieces * 4)
+    for args in [(4, 4, 2, 64, 3, 0), (32, 32, 8, 128, 256, 0), (16, 40, 8, 128, 2048, 0),
+                 (4, 4, 2, 64, 3, 16), (32, 32, 8, 128, 256, 512), (3, 16, 1, 128, 10, 0)]:
+        assert P.vllm_paged_attn_workspace_size(*args) == expect(*args), args
+    assert P.vllm_paged_attn_workspace_size(4, 3, 2, 64, 3, 0) == 0     # Hq % Hkv -> 0
     assert P.vllm_paged_attn_workspace_size(4, 4, 2, 64, 3, 24) == 0    # invalid partition -> 0
+    assert P.vllm_paged_attn_workspace_size(4, 4, 2, 96, 3, 0) == 0     # unsupported D -> 0
