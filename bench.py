@@ -42,6 +42,25 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + seqs/s"
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode call (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy)
+    from the committed counter summary of this workload, or None when there is
+    none or the decode kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line.startswith(("source_sha256: ", "traffic_bytes_per_call: ")))
+    h = hashlib.sha256()
+    for f in ("decode.hip", "kernels.h", "common.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_183_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_call"])
+
+
 def decode_bytes(case) -> dict:
     """Algorithmic bytes of one decode call and of one step's cache write."""
     eb = ELEM_BYTES[case.kv_dtype]
@@ -260,7 +279,8 @@ def main():
                            "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "roofline": {"bound": "hbm", "kernel": "decode call (decode_kernel + decode_merge_kernel)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(case.name)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
