@@ -424,9 +424,81 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
                                     const vllm_tensor* context_lens, int32_t max_query_len,
                                     float scale, int32_t window, const vllm_attn_opts* opts,
                                     void* hip_stream) {
-  (void)out; (void)q; (void)k_cache; (void)v_cache; (void)block_tables; (void)query_start_loc;
-  (void)context_lens; (void)max_query_len; (void)scale; (void)window; (void)opts; (void)hip_stream;
-  return fail(VLLM_ERR_UNSUPPORTED, "prefill: not built yet");
+  VP_TRY(check_tensor(out, "out", 3));
+  VP_TRY(check_tensor(q, "q", 3));
+  VP_TRY(check_tensor(k_cache, "k_cache", 4));
+  VP_TRY(check_tensor(v_cache, "v_cache", 4));
+  VP_TRY(check_tensor(block_tables, "block_tables", 2));
+  VP_TRY(check_tensor(query_start_loc, "query_start_loc", 1));
+  VP_TRY(check_tensor(context_lens, "context_lens", 1));
+  if (opts && opts->flags != 0) return fail(VLLM_ERR_INVALID_ARG, "opts.flags must be 0");
+  const int64_t sumQ = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(VLLM_ERR_INVALID_ARG, "out shape differs from q");
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i])
+      return fail(VLLM_ERR_INVALID_ARG, "v_cache shape differs from k_cache");
+  const int64_t NB = k_cache->shape[0], Hkv = k_cache->shape[1];
+  const int64_t B = context_lens->shape[0];
+  if (k_cache->shape[2] != VLLM_PAGED_BLOCK_SIZE)
+    return fail(VLLM_ERR_UNSUPPORTED, "block size %lld: only 16 is supported", (long long)k_cache->shape[2]);
+  if (k_cache->shape[3] != D)
+    return fail(VLLM_ERR_INVALID_ARG, "k_cache head_dim %lld != q head_dim %lld",
+                (long long)k_cache->shape[3], (long long)D);
+  if (block_tables->shape[0] != B || query_start_loc->shape[0] != B + 1)
+    return fail(VLLM_ERR_INVALID_ARG, "block_tables must have %lld rows and query_start_loc %lld entries",
+                (long long)B, (long long)(B + 1));
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0)
+    return fail(VLLM_ERR_INVALID_ARG, "num_q_heads %lld is not a positive multiple of num_kv_heads %lld",
+                (long long)Hq, (long long)Hkv);
+  if (window < 0) return fail(VLLM_ERR_INVALID_ARG, "window must be >= 0 (got %d)", (int)window);
+  if (max_query_len < 0) return fail(VLLM_ERR_INVALID_ARG, "max_query_len must be >= 0");
+  if (!std::isfinite(scale)) return fail(VLLM_ERR_INVALID_ARG, "scale must be finite");
+  if (q->dtype != VLLM_DTYPE_F16 && q->dtype != VLLM_DTYPE_BF16)
+    return fail(VLLM_ERR_UNSUPPORTED, "q: dtype %s, expected F16 or BF16", dtype_name(q->dtype));
+  VP_TRY(check_dtype(out, "out", q->dtype));
+  if (k_cache->dtype != q->dtype)
+    return fail(VLLM_ERR_UNSUPPORTED, "prefill: k_cache dtype %s must match q (%s)",
+                dtype_name(k_cache->dtype), dtype_name(q->dtype));
+  VP_TRY(check_dtype(v_cache, "v_cache", k_cache->dtype));
+  VP_TRY(check_dtype(block_tables, "block_tables", VLLM_DTYPE_I32));
+  VP_TRY(check_dtype(query_start_loc, "query_start_loc", VLLM_DTYPE_I32));
+  VP_TRY(check_dtype(context_lens, "context_lens", VLLM_DTYPE_I32));
+  if (D != 128) return fail(VLLM_ERR_UNSUPPORTED, "prefill head_dim %lld: supported 128", (long long)D);
+  if (Hq / Hkv > 128) return fail(VLLM_ERR_UNSUPPORTED, "prefill: group size above 128");
+  if (NB > INT32_MAX || block_tables->shape[1] > INT32_MAX / 16 || B > 65535 || Hq > 65535 ||
+      sumQ > INT32_MAX)
+    return fail(VLLM_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  if (sumQ == 0 || B == 0 || max_query_len == 0) return ok();
+  VP_TRY(check_data(q, "q", 16));
+  VP_TRY(check_data(out, "out", 16));
+  VP_TRY(check_data(k_cache, "k_cache", 16));
+  VP_TRY(check_data(v_cache, "v_cache", 16));
+  VP_TRY(check_data(block_tables, "block_tables", 4));
+  VP_TRY(check_data(query_start_loc, "query_start_loc", 4));
+  VP_TRY(check_data(context_lens, "context_lens", 4));
+
+  vp::PrefillParams p{};
+  p.q = q->data;
+  p.out = out->data;
+  p.k_cache = k_cache->data;
+  p.v_cache = v_cache->data;
+  p.block_tables = static_cast<const int32_t*>(block_tables->data);
+  p.query_start_loc = static_cast<const int32_t*>(query_start_loc->data);
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.num_tokens = (int32_t)sumQ;
+  p.num_seqs = (int32_t)B;
+  p.num_q_heads = (int32_t)Hq;
+  p.num_kv_heads = (int32_t)Hkv;
+  p.group = (int32_t)(Hq / Hkv);
+  p.bt_stride = (int32_t)block_tables->shape[1];
+  p.num_blocks = (int32_t)NB;
+  p.max_query_len = max_query_len;
+  p.window = window;
+  p.score_scale = scale * 1.4426950408889634f;
+  VP_TRY(hip_status(vp::launch_prefill(p, (int)D, fmt_of(q->dtype), (hipStream_t)hip_stream),
+                    "prefill launch"));
+  return ok();
 }
 
 }  // extern "C"

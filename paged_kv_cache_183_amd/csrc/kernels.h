@@ -69,6 +69,7 @@ struct PrefillParams {
   const int32_t* block_tables;
   const int32_t* query_start_loc;  // [B + 1]
   const int32_t* context_lens;     // [B]
+  int32_t num_tokens;          // sumQ (rows of q)
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -77,6 +78,7 @@ struct PrefillParams {
   int32_t num_blocks;
   int32_t max_query_len;
   int32_t window;
+  int32_t num_tiles;           // token tiles per sequence (set by launch_prefill)
   float score_scale;           // scale * log2(e)
 };
 

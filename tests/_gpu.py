@@ -64,3 +64,39 @@ TOL = {"f16": 2e-3, "bf16": 8e-3, "e4m3": 3e-2}
 
 def tol_for(case) -> float:
     return TOL["e4m3"] if case.kv_dtype == "e4m3" else TOL[case.q_dtype]
+
+
+# Explicit mantissa bits of the 16-bit output formats.
+_MANT = {"f16": 10, "bf16": 7}
+
+
+def out_ulp(ref: np.ndarray, q_dtype: str) -> np.ndarray:
+    """One unit in the last place of q's 16-bit format at |ref| (normal range)."""
+    a = np.maximum(np.abs(ref), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(a)) - _MANT[q_dtype])
+
+
+def elem_bound(case, ref: np.ndarray) -> np.ndarray:
+    """Per-element bar: the stated max-abs tolerance, or one ulp of the output
+    format where that ulp is larger (|out| >= 2 in bf16, >= 4 in fp16): the
+    output is rounded to q's format, so an exact result one rounding step
+    away from a nearest-even midpoint can land one ulp off."""
+    return np.maximum(tol_for(case), out_ulp(ref, case.q_dtype))
+
+
+def assert_close(case, got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
+    """Element-by-element check against the oracle; returns the max abs error."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if not ref.size:
+        return 0.0
+    assert np.all(np.isfinite(got)), f"{case.name}{what}: non-finite output"
+    e = np.abs(got - ref)
+    bad = e > elem_bound(case, ref)
+    if np.any(bad):
+        i = np.unravel_index(np.argmax(np.where(bad, e, -1.0)), e.shape)
+        raise AssertionError(f"{case.name}{what}: {int(bad.sum())} elements beyond the bar; "
+                             f"at {tuple(int(x) for x in i)} ref {ref[i]:.6f} got {got[i]:.6f} "
+                             f"(err {e[i]:.3e}, tol {tol_for(case)})")
+    return float(e.max())

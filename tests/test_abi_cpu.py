@@ -117,3 +117,35 @@ def test_workspace_size():
     assert P.vllm_paged_attn_workspace_size(4, 3, 2, 64, 3, 0) == 0     # Hq % Hkv -> 0
     assert P.vllm_paged_attn_workspace_size(4, 4, 2, 64, 3, 24) == 0    # invalid partition -> 0
     assert P.vllm_paged_attn_workspace_size(4, 4, 2, 96, 3, 0) == 0     # unsupported D -> 0
+
+
+def _prefill_args(sumq=5, B=2, Hq=4, Hkv=2, D=128, dt=torch.bfloat16, kvdt=None, mb=3):
+    q = torch.zeros(sumq, Hq, D, dtype=dt)
+    kv = _pool(h=Hkv, d=D, dt=kvdt or dt)
+    return dict(out=torch.empty_like(q), q=q, k_cache=kv, v_cache=kv.clone(),
+                block_tables=torch.zeros(B, mb, dtype=torch.int32),
+                query_start_loc=torch.tensor([0, 2, sumq][:B + 1], dtype=torch.int32),
+                context_lens=torch.full((B,), 40, dtype=torch.int32),
+                max_query_len=3, scale=0.1)
+
+
+def test_prefill_validation():
+    a = _prefill_args()
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "window": -2})
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "max_query_len": -1})
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "scale": float("inf")})
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **_prefill_args(Hq=3, Hkv=2))
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(D=64))
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(kvdt=torch.uint8))
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(dt=torch.float32))
+    b = _prefill_args()
+    b["query_start_loc"] = torch.tensor([0, 5], dtype=torch.int32)       # needs B + 1 entries
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **b)
+    c = _prefill_args()
+    c["block_tables"] = torch.zeros(3, 3, dtype=torch.int32)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **c)
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(Hq=129 * 2, Hkv=2))
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_attn_prefill, **a)
+    # nothing to do: no launch, no pointer touched
+    P.vllm_paged_attn_prefill(**{**_prefill_args(sumq=0), "query_start_loc":
+                                 torch.zeros(3, dtype=torch.int32)}, stream=0)

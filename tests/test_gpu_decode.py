@@ -2,7 +2,8 @@
 
 Everything goes through the C ABI (the ctypes binding).  Bars: the scatter is
 bit-exact over whole pools; attention outputs are within max-abs 2e-3 (fp16),
-8e-3 (bf16) and 3e-2 (FP8 KV) of the oracle, compared element by element;
+8e-3 (bf16) and 3e-2 (FP8 KV) of the oracle, or one ulp of the output format
+where that is larger, compared element by element;
 invariance properties that the kernel's arithmetic order makes exact are
 checked bit for bit."""
 import numpy as np
@@ -15,7 +16,7 @@ from oracle import scatter as S
 from workloads import make_case, raw_bits
 
 from _util import oracle_pools
-from _gpu import gpu_fill, gpu_decode, to_f64, bits, tol_for, pool_view, DEV
+from _gpu import gpu_fill, gpu_decode, to_f64, bits, pool_view, assert_close, DEV
 
 pytestmark = pytest.mark.gpu
 
@@ -34,10 +35,7 @@ def check_decode(case, out, kp, vp, seqs=None, window=None):
     got = to_f64(out)
     if seqs is not None:
         got = got[seqs]
-    assert np.all(np.isfinite(got))
-    err = np.max(np.abs(got - ref)) if ref.size else 0.0
-    assert err <= tol_for(case), f"{case.name}: max abs err {err:.3e} > {tol_for(case)}"
-    return err
+    return assert_close(case, got, ref)
 
 
 # Reduced versions of the five workloads: same dtypes / heads / structure,
@@ -208,7 +206,7 @@ def test_zero_and_clipped_context():
         assert torch.all(out[1] == 0) and torch.all(out[2] == 0)
         kp, vp = oracle_pools(case)
         ref = oracle_decode(case, kp, vp, seqs=[0, 3])
-        assert np.max(np.abs(to_f64(out)[[0, 3]] - ref)) <= 8e-3
+        assert_close(case, to_f64(out)[[0, 3]], ref)
 
 
 def test_empty_batch_is_noop():
