@@ -193,8 +193,11 @@ size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   query_start_loc [B + 1]  I32, non-decreasing, query_start_loc[0] = 0,
  *                    query_start_loc[B] = sumQ
  *   context_lens [B]  I32, n >= Q_s
- *   max_query_len    an upper bound of max_s Q_s
- * Supported: D = 128.  sumQ = 0 is a no-op.
+ *   max_query_len    an upper bound of max_s Q_s (rows of longer chunks past
+ *                    it are not computed)
+ *   scale        softmax scale applied to q.k, finite and > 0
+ * Supported: D = 128; g = Hq / Hkv <= 128.  sumQ = 0 is a no-op.  Values of
+ * query_start_loc are clamped to [0, sumQ], so no value leads outside q/out.
  */
 vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
                                     const vllm_tensor* k_cache, const vllm_tensor* v_cache,

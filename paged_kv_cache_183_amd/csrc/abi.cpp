@@ -453,7 +453,8 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
                 (long long)Hq, (long long)Hkv);
   if (window < 0) return fail(VLLM_ERR_INVALID_ARG, "window must be >= 0 (got %d)", (int)window);
   if (max_query_len < 0) return fail(VLLM_ERR_INVALID_ARG, "max_query_len must be >= 0");
-  if (!std::isfinite(scale)) return fail(VLLM_ERR_INVALID_ARG, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(VLLM_ERR_INVALID_ARG, "prefill scale must be finite and positive");
   if (q->dtype != VLLM_DTYPE_F16 && q->dtype != VLLM_DTYPE_BF16)
     return fail(VLLM_ERR_UNSUPPORTED, "q: dtype %s, expected F16 or BF16", dtype_name(q->dtype));
   VP_TRY(check_dtype(out, "out", q->dtype));

@@ -12,15 +12,18 @@
 // walks the kept keys in blocks of 32 (two 16-token pages), staged through
 // LDS once for its four waves:
 //  * K block row-major ([key][D], rows padded by 16 bytes);
-//  * V block transposed ([D][key], key pairs XOR-swizzled per 16 rows of D),
-//    so that the P.V operand of a lane is two 8-byte reads.
+//  * V block transposed ([D][key pair], rows padded to 18 dwords), so that
+//    the P.V operand of a lane is two 8-byte reads; the staging writes and
+//    these reads hit distinct banks.
+// Global loads run two blocks ahead of the matrix cores.
 // Per block and wave, on v_mfma_f32_32x32x16 (bf16 or f16, fp32 accumulate):
 //  * S^T = K Q^T: the output column of a lane is its query row, so each lane
 //    holds 16 scores of one row (keys 8j + 4h + i, h = lane / 32);
 //  * online softmax per row in fp32 (log2 domain), the two half-waves of a
 //    row combined with one lane exchange; the running max only moves when a
 //    score exceeds it by more than 2^8;
-//  * P is rounded to q's 16-bit format (the row sums use the rounded values)
+//  * P is rounded to q's 16-bit format (the row sums, on v_dot2 against
+//    ones, use the rounded values)
 //    and used in place as the B operand of O^T += V^T P^T: the contraction
 //    over keys follows the same key order in both operands, so no transpose
 //    of P is needed and O^T keeps each query row in one lane as well.
@@ -61,15 +64,19 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// a.lo * b.lo + a.hi * b.hi + c with fp32 accumulation.
 template <int QF>
-__device__ __forceinline__ float lo_f(uint32_t w) {
-  if constexpr (QF == kBF16) return bitcast<float>(w << 16);
-  else return (float)bitcast<half2_t>(w).x;
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (QF == kF16)
+    return __builtin_amdgcn_fdot2(bitcast<half2_t>(a), bitcast<half2_t>(b), c, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a), bitcast<bf16x2_t>(b), c, false);
 }
-template <int QF>
-__device__ __forceinline__ float hi_f(uint32_t w) {
-  if constexpr (QF == kBF16) return bitcast<float>(w & 0xFFFF0000u);
-  else return (float)bitcast<half2_t>(w).y;
+
+// Max of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the halves).
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+  return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
 }
 
 }  // namespace
@@ -89,17 +96,19 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
 
   const int g = p.group;
   const int tq = kRows / g;                    // query tokens per workgroup
-  // Workgroup -> (sequence, kv-head, token tile), tiles of one (sequence,
-  // kv-head) placed on the same XCD (workgroups go to XCDs round-robin).
-  const int total = gridDim.x;
-  const int b = blockIdx.x;
-  const int xq = total / 8, xr = total % 8, xcd = b % 8;
-  const int L = xcd * xq + min(xcd, xr) + b / 8;
+  // Workgroup -> (sequence, kv-head, token tile).  Workgroups go to the 8
+  // XCDs round-robin; (sequence, kv-head) pair u runs on XCD u % 8 with all
+  // its tiles (they share K/V in that XCD's L2), so every XCD sees every
+  // sequence and the XCDs get even work.  Later tiles attend to more keys and
+  // are dispatched first.
   const int ntiles = p.num_tiles;
-  const int tile = L % ntiles;
-  const int sh = L / ntiles;
-  const int s = sh / p.num_kv_heads;
-  const int hk = sh - s * p.num_kv_heads;
+  const int b = blockIdx.x;
+  const int xcd = b % 8, k = b / 8;
+  const int u = (k / ntiles) * 8 + xcd;
+  if (u >= p.num_seqs * p.num_kv_heads) return;
+  const int tile = ntiles - 1 - (k % ntiles);
+  const int s = u / p.num_kv_heads;
+  const int hk = u - s * p.num_kv_heads;
 
   // (clamped to the rows of q, so that no value of query_start_loc leads
   // outside q / out)
@@ -136,16 +145,21 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
   const int kb0 = (lo / kBK) * kBK;
   const int nblk = p_last >= 0 ? (p_last / kBK - kb0 / kBK + 1) : 0;
 
-  // Staging map: thread i -> row i / CH of a page, 16-byte chunk i % CH.
-  const int st_r = threadIdx.x / CH, st_c = threadIdx.x % CH;
   const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
   const uint8_t* kpool = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
   const uint8_t* vpool = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes;
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
 
-  // K: rows st_r of pages 0 and 1 of the block; V: key pair (2 st_r, 2 st_r + 1)
-  // spans page st_r / 8, rows 2 (st_r % 8) and 2 (st_r % 8) + 1.
-  uint4 kreg[2], vreg[2];
+  // Staging maps (256 threads, one block = pages A and B of 16 rows):
+  //  K: thread i loads row i / 16, 16-byte chunk i % 16 of both pages;
+  //  V: thread i loads rows 2 kp and 2 kp + 1 (kp = i % 16: key pair of the
+  //     block, page kp / 8) at chunk i / 16, and writes the 8 dwords
+  //     (V[2kp][d], V[2kp+1][d]) of V^T: 64 lanes hit 64 distinct banks.
+  const int k_r = threadIdx.x / CH, k_c = threadIdx.x % CH;
+  const int v_kp = threadIdx.x % 16, v_c = threadIdx.x / 16;
+  const int k_off = k_r * (D * 2) + k_c * 16;
+  const int v_off = 2 * (v_kp & 7) * (D * 2) + v_c * 16;
+  const bool v_pgB = v_kp >= 8;
   auto page_blk = [&](int j) __attribute__((always_inline)) {
     int blk = 0;
     if (j * 16 < n) blk = bt[j];
@@ -153,72 +167,67 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
   };
   // Loads are unconditional (rows at or past n are replaced by zeros when
   // written to LDS) so that nothing waits on them before the LDS write.
-  auto fetch = [&](int kb) __attribute__((always_inline)) {
+  auto fetch = [&](uint4 (&kr)[2], uint4 (&vr)[2], int kb) __attribute__((always_inline)) {
     const int j0 = kb >> 4;
-    const int b0 = page_blk(j0), b1 = page_blk(j0 + 1);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int bb = u ? b1 : b0;
-      kreg[u] = *reinterpret_cast<const uint4*>(kpool + bb * blk_stride + st_r * (D * 2) + st_c * 16);
-    }
-    const int vb = (st_r >> 3) ? b1 : b0;
-    const int vrow = 2 * (st_r & 7);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      vreg[u] = *reinterpret_cast<const uint4*>(vpool + vb * blk_stride + (vrow + u) * (D * 2) + st_c * 16);
+    const int64_t pa = (int64_t)page_blk(j0) * blk_stride, pb = (int64_t)page_blk(j0 + 1) * blk_stride;
+    kr[0] = *reinterpret_cast<const uint4*>(kpool + pa + k_off);
+    kr[1] = *reinterpret_cast<const uint4*>(kpool + pb + k_off);
+    const uint8_t* vp = vpool + (v_pgB ? pb : pa) + v_off;
+    vr[0] = *reinterpret_cast<const uint4*>(vp);
+    vr[1] = *reinterpret_cast<const uint4*>(vp + D * 2);
   };
   auto masked = [](uint4 x, bool keep) __attribute__((always_inline)) {
     const uint32_t m = keep ? 0xFFFFFFFFu : 0u;    // value-level select (no pointer select)
     return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
   };
-  auto stage = [&](int buf, int kb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<uint4*>(&s_k[buf][(16 * u + st_r) * KROW + st_c * 16]) =
-          masked(kreg[u], kb + 16 * u + st_r < n);
-    // V^T: dword (d, key pair kp) at d * VROWW + (kp ^ swz(d)).
-    const int t0 = kb + 2 * st_r;                  // keys t0, t0 + 1 of this thread's pair
-    const uint4 va = masked(vreg[0], t0 < n);
-    const uint4 vc = masked(vreg[1], t0 + 1 < n);
+  auto stage = [&](int buf, const uint4 (&kr)[2], const uint4 (&vr)[2], int kb)
+      __attribute__((always_inline)) {
+    uint4 k0 = kr[0], k1 = kr[1], va = vr[0], vc = vr[1];
+    if (kb + kBK > n) {                            // block crossing n: zero the rows past it
+      k0 = masked(k0, kb + k_r < n);
+      k1 = masked(k1, kb + 16 + k_r < n);
+      va = masked(va, kb + 2 * v_kp < n);
+      vc = masked(vc, kb + 2 * v_kp + 1 < n);
+    }
+    *reinterpret_cast<uint4*>(&s_k[buf][k_r * KROW + k_c * 16]) = k0;
+    *reinterpret_cast<uint4*>(&s_k[buf][(16 + k_r) * KROW + k_c * 16]) = k1;
     const uint32_t a[4] = {va.x, va.y, va.z, va.w};
-    const uint32_t c[4] = {vc.x, vc.y, vc.z, vc.w};
+    const uint32_t b[4] = {vc.x, vc.y, vc.z, vc.w};
+    uint32_t* vt = &s_v[buf][(v_c * 8) * VROWW + v_kp];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int d0 = st_c * 8 + 2 * i;
-      const int swz = 2 * ((d0 >> 4) & 7);
-      s_v[buf][d0 * VROWW + (st_r ^ swz)] = __builtin_amdgcn_perm(c[i], a[i], 0x05040100u);
-      s_v[buf][(d0 + 1) * VROWW + (st_r ^ swz)] = __builtin_amdgcn_perm(c[i], a[i], 0x07060302u);
+      vt[(2 * i) * VROWW] = __builtin_amdgcn_perm(b[i], a[i], 0x05040100u);
+      vt[(2 * i + 1) * VROWW] = __builtin_amdgcn_perm(b[i], a[i], 0x07060302u);
     }
   };
 
+  constexpr uint32_t kOnes = QF == kBF16 ? 0x3F803F80u : 0x3C003C00u;   // (1, 1)
   f32x16_t o[D / 32];
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) o[m] = f32x16_t{};
   float mrow = -INFINITY, lsum = 0.0f;
+  const float c = p.score_scale;
 
-  if (nblk > 0) {
-    fetch(kb0);
-    stage(0, kb0);
-  }
-  __syncthreads();
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int kb = kb0 + bi * kBK;
-    const int buf = bi & 1;
-    const int kb_next = kb0 + min(bi + 1, nblk - 1) * kBK;   // (re-reads the last block at the end)
-    fetch(kb_next);
-    __builtin_amdgcn_sched_barrier(0);
-
+  // One block: S^T, online softmax, O^T update.  buf holds the block's K and
+  // V^T.  Lane reads: K rows col (16 bytes at d = 64 hf + 8 t), V^T rows
+  // d = 32 m + col (8 bytes at key pairs 8 kap + 2 hf and + 4).
+  const uint8_t* k_rd = &s_k[0][col * KROW + 128 * hf];
+  const uint32_t* v_rd = &s_v[0][col * VROWW + 2 * hf];
+  auto block = [&](int buf, int kb) __attribute__((always_inline)) {
     // ---- S^T = K Q^T ----
-    f32x16_t sacc = f32x16_t{};
-    const uint8_t* krow = &s_k[buf][col * KROW + 128 * hf];
+    uint4 ka[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      sacc = mfma32<QF>(*reinterpret_cast<const uint4*>(krow + 16 * t), qr[t], sacc);
+    for (int t = 0; t < 8; ++t) ka[t] = *reinterpret_cast<const uint4*>(k_rd + buf * KBUF + 16 * t);
+    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sacc = mfma32<QF>(ka[t], qr[t], sacc);
 
     // ---- online softmax (row = col; this lane holds keys 8j + 4hf + i) ----
+    // Scores stay unscaled up to the exponent (scale > 0: max(c s) = c max(s)),
+    // which is then one fma per score: exp2(c s - m).
     float sc[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) sc[k] = sacc[k] * p.score_scale;
+    for (int k = 0; k < 16; ++k) sc[k] = sacc[k];
     const bool edge = (kb + kBK - 1 > pos0) || (p.window > 0 && kb <= p_last - p.window);
     if (edge) {
 #pragma unroll
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
     float mx = sc[0];
 #pragma unroll
     for (int k = 1; k < 16; ++k) mx = fmaxf(mx, sc[k]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = half_max(mx) * c;
     const bool need = mx > mrow + kTauP;
     if (__any(need)) {
       const float mn = need ? fmaxf(mrow, mx) : mrow;
@@ -246,31 +255,52 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) o[m][k] *= alpha;
     }
-    const float mu = (mrow == -INFINITY) ? 0.0f : mrow;
+    const float nmu = (mrow == -INFINITY) ? 0.0f : -mrow;
     uint32_t pw[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      pw[k] = pack2<QF>(fast_exp2(sc[2 * k] - mu), fast_exp2(sc[2 * k + 1] - mu));
-      lsum += lo_f<QF>(pw[k]) + hi_f<QF>(pw[k]);
+      pw[k] = pack2<QF>(fast_exp2(fmaf(sc[2 * k], c, nmu)), fast_exp2(fmaf(sc[2 * k + 1], c, nmu)));
+      lsum = dot2<QF>(pw[k], kOnes, lsum);       // row sum of the rounded weights
     }
 
     // ---- O^T += V^T P^T ----
+    const uint32_t* vb = v_rd + buf * (VBUF / 4);
 #pragma unroll
     for (int kap = 0; kap < 2; ++kap) {
       const uint4 pb = make_uint4(pw[4 * kap], pw[4 * kap + 1], pw[4 * kap + 2], pw[4 * kap + 3]);
 #pragma unroll
       for (int m = 0; m < D / 32; ++m) {
-        const int d = 32 * m + col;
-        const int swz = 2 * ((d >> 4) & 7);
-        const uint32_t* vr = &s_v[buf][d * VROWW];
-        const uint2 a0 = *reinterpret_cast<const uint2*>(vr + ((8 * kap + 2 * hf) ^ swz));
-        const uint2 a1 = *reinterpret_cast<const uint2*>(vr + ((8 * kap + 4 + 2 * hf) ^ swz));
+        const uint32_t* vr = vb + 32 * m * VROWW + 8 * kap;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(vr);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 4);
         o[m] = mfma32<QF>(make_uint4(a0.x, a0.y, a1.x, a1.y), pb, o[m]);
       }
     }
+  };
 
+  // Two register sets of staged loads: block bi + 2 is fetched while block bi
+  // is computed and block bi + 1 is written to LDS.
+  uint4 kr0[2], vr0[2], kr1[2], vr1[2];
+  auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
+  if (nblk > 0) {
+    fetch(kr0, vr0, kb_of(0));
+    fetch(kr1, vr1, kb_of(1));
+    stage(0, kr0, vr0, kb_of(0));
+  }
+  __syncthreads();
+  for (int bi = 0; bi < nblk; bi += 2) {
+    fetch(kr0, vr0, kb_of(bi + 2));            // (past the end: re-reads the last block)
     __builtin_amdgcn_sched_barrier(0);
-    stage(buf ^ 1, kb_next);
+    block(0, kb0 + bi * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(1, kr1, vr1, kb_of(bi + 1));
+    __syncthreads();
+    if (bi + 1 >= nblk) break;
+    fetch(kr1, vr1, kb_of(bi + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    block(1, kb0 + (bi + 1) * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(0, kr0, vr0, kb_of(bi + 2));
     __syncthreads();
   }
 
@@ -300,7 +330,8 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipSt
   if (tq < 1) return hipErrorNotSupported;
   PrefillParams x = p;
   x.num_tiles = (p.max_query_len + tq - 1) / tq;
-  const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * x.num_tiles;
+  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+  const int64_t grid = (pairs + 7) / 8 * 8 * x.num_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (q_fmt == kBF16)

@@ -134,6 +134,8 @@ def test_prefill_validation():
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "window": -2})
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "max_query_len": -1})
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "scale": float("inf")})
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "scale": 0.0})
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "scale": -0.1})
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **_prefill_args(Hq=3, Hkv=2))
     _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(D=64))
     _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(kvdt=torch.uint8))
