@@ -39,7 +39,9 @@ sys.path.insert(0, ROOT)
 from workloads import CONFIGS, ELEM_BYTES, make_case, raw_bits  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 matrix-core peak of MI355X
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + seqs/s"
+PREFILL_METRIC = "chunked-prefill paged attention: TFLOP/s (% bf16 MFMA peak) + tokens/s"
 
 
 def measured_traffic(workload: str):
@@ -53,7 +55,7 @@ def measured_traffic(workload: str):
     fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line.startswith(("source_sha256: ", "traffic_bytes_per_call: ")))
     h = hashlib.sha256()
-    for f in ("decode.hip", "kernels.h", "common.h"):
+    for f in ("decode.hip", "common.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_183_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if fields.get("source_sha256") != h.hexdigest():
@@ -76,6 +78,135 @@ def decode_bytes(case) -> dict:
     other = 2 * B * Hq * D * qb + pages * 4 + B * 4
     write = B * Hkv * D * (2 * qb + 2 * eb) + B * 8
     return dict(kv=kv, decode=kv + other, write=write, kept_tokens=kept)
+
+
+def prefill_work(case) -> dict:
+    """Algorithmic work of one chunked-prefill call: kept (query token, key)
+    pairs, their flops (4 D per pair and query head: q.k and p.v), and the
+    bytes of q, out and each sequence's K/V range read once."""
+    import numpy as np
+    Q = np.diff(case.query_start_loc.numpy()).astype(np.int64)
+    n = case.context_lens.numpy().astype(np.int64)
+    W = case.window
+    pairs = 0
+    kv_tokens = 0
+    for s in range(len(n)):
+        if Q[s] == 0:
+            continue
+        p = n[s] - Q[s] + np.arange(Q[s])
+        lo = np.maximum(0, p - W + 1) if W > 0 else np.zeros_like(p)
+        pairs += int(np.sum(p - lo + 1))
+        kv_tokens += int(n[s] - lo[0])
+    Hq, Hkv, D = case.num_q_heads, case.num_kv_heads, case.head_dim
+    flops = pairs * Hq * 4 * D
+    byts = 2 * int(Q.sum()) * Hq * D * 2 + kv_tokens * Hkv * D * 2 * 2
+    return dict(pairs=pairs, flops=flops, bytes=byts, tokens=int(Q.sum()))
+
+
+def cpu_baseline_prefill(case, seconds: float) -> dict:
+    """The fp64 oracle, unchanged, on whole sequences of the chunked-prefill
+    batch (every query row of each), for about ``seconds``."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import scatter as S
+    cores = min(16, len(os.sched_getaffinity(0)))
+    pool0 = raw_bits(case.sentinel_pool())
+    slots = case.fill_slots.numpy()
+    kp = S.cache_write_fast(pool0, raw_bits(case.fill_k), slots, case.kv_src_dtype, case.kv_dtype)
+    vp = S.cache_write_fast(pool0, raw_bits(case.fill_v), slots, case.kv_src_dtype, case.kv_dtype)
+    del pool0
+    qsl = case.query_start_loc.numpy()
+    qb = raw_bits(case.q)
+    t0 = time.time()
+    done, flops = [], 0
+    Hq, D, W = case.num_q_heads, case.head_dim, case.window
+    n = case.context_lens.numpy()
+    s = 0
+    per = 64                                   # query rows per sequence in the sample
+    while s < case.num_seqs and (time.time() - t0 < seconds or not done):
+        batch = list(range(s, min(case.num_seqs, s + cores)))
+        rows = {}
+        for j in batch:
+            Qj = int(qsl[j + 1] - qsl[j])
+            rows[j] = list(range(max(0, Qj - per), Qj))           # the chunk's last rows
+        A.prefill(qb, case.q_dtype, kp, vp, case.kv_dtype, case.block_tables.numpy(), qsl,
+                  n, case.scale, W, rows=rows, workers=cores)
+        for j in batch:
+            Qj = int(qsl[j + 1] - qsl[j])
+            pp = n[j] - Qj + np.asarray(rows[j], dtype=np.int64)
+            lo = np.maximum(0, pp - W + 1) if W > 0 else np.zeros_like(pp)
+            flops += int(np.sum(pp - lo + 1)) * Hq * 4 * D
+        done += batch
+        s += len(batch)
+    dt = time.time() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"the last {per} query rows (all heads) of sequences 0..{done[-1]} of the "
+                      f"chunked-prefill batch ({len(done)} of {case.num_seqs}), {dt:.1f} s"}
+
+
+def measured_prefill_traffic(workload: str):
+    """HBM bytes per prefill call from the committed counter summary, or None
+    when there is none or the prefill kernel's sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line.startswith(("source_sha256: ", "traffic_bytes_per_call: ")))
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "common.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_183_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_call"])
+
+
+def bench_prefill(case, steps: int, warmup: int) -> dict:
+    """Time the chunked-prefill call on ``case`` (K/V written by the library's
+    cache write first, untimed) with HIP events around each call."""
+    import paged_kv_cache_183_amd as P
+    dev = torch.device("cuda", 0)
+    view = lambda t: t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16)  # noqa: E731
+    kc, vc = case.sentinel_pool().to(dev), case.sentinel_pool().to(dev)
+    P.vllm_paged_cache_write(case.fill_k.to(dev), case.fill_v.to(dev), case.fill_slots.to(dev),
+                             view(kc), view(vc))
+    q = case.q.to(dev)
+    out = torch.empty_like(q)
+    bt, qsl, ctx = (case.block_tables.to(dev), case.query_start_loc.to(dev),
+                    case.context_lens.to(dev))
+
+    def call():
+        P.vllm_paged_attn_prefill(out, q, view(kc), view(vc), bt, qsl, ctx, case.max_query_len,
+                                  case.scale, case.window)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ms = [a.elapsed_time(b) for a, b in evs]
+    mean = sum(ms) / len(ms)
+    w = prefill_work(case)
+    tf = w["flops"] / (mean * 1e-3) / 1e12
+    return {"workload": case.name, "ms_per_call": round(mean, 5),
+            "p10_ms": round(float(np.percentile(ms, 10)), 5),
+            "p90_ms": round(float(np.percentile(ms, 90)), 5),
+            "wall_ms_per_call": round(wall * 1e3, 5),
+            "tflops": round(tf, 2), "tokens_per_s": round(w["tokens"] / (mean * 1e-3), 1),
+            "flops_per_call": w["flops"], "kept_pairs": w["pairs"], "bytes_per_call": w["bytes"],
+            "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_prefill_traffic(case.name)}}
 
 
 def cpu_baseline(case, seconds: float) -> dict:
@@ -127,6 +258,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies rotated over steps (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the chunked-prefill measurement appended to the decode line")
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graphs instead of launching every call eagerly")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -147,9 +280,9 @@ def main():
               f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
         sys.exit(2)
     cfg = CONFIGS[args.config]
-    if cfg["kind"] != "decode":
-        print("bench.py times decode workloads", file=sys.stderr)
-        sys.exit(2)
+    if cfg["kind"] == "prefill":
+        main_prefill(args)
+        return
 
     case = make_case(args.config)
     by = decode_bytes(case)
@@ -281,6 +414,41 @@ def main():
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(case.name)},
+        "cpu_baseline": cpu,
+    }
+    if not args.no_prefill:
+        # The matrix-core variant of the path, on the chunked-prefill workload.
+        res["prefill"] = bench_prefill(make_case(4), steps=min(args.steps, 20), warmup=3)
+    print(json.dumps(res), flush=True)
+
+
+def main_prefill(args):
+    """Standalone line for the chunked-prefill workload (matrix-core roof)."""
+    case = make_case(args.config)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(case, args.cpu_seconds)
+    torch.cuda.set_device(0)
+    r = bench_prefill(case, steps=args.steps, warmup=args.warmup)
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": r["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["wall_ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.q_dtype,
+        "data": "synthetic",
+        "config": {"workload": case.name, "num_seqs": case.num_seqs, "sum_q": int(case.query_start_loc[-1]),
+                   "q_heads": case.num_q_heads,
+                   "kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "block_size": 16,
+                   "window": case.window, "kept_pairs": r["kept_pairs"],
+                   "flops_per_step": r["flops_per_call"], "seed": args.config, "launch": "eager"},
+        "tokens_per_s": r["tokens_per_s"],
+        "prefill_call_ms": {"mean": r["ms_per_call"], "p10": r["p10_ms"], "p90": r["p90_ms"]},
+        "roofline": r["roofline"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
