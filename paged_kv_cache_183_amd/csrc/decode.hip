@@ -568,89 +568,82 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Log-sum-exp merge of the pieces of units cut by chunk boundaries.  One
-// workgroup per unit; the unit's record (first slot, piece count) comes from
-// the decode kernel.  All loads of a round are independent: each thread
-// fetches the (max, sum) of one piece and, for its output elements, the
-// normalized outputs of up to kMergeBatch pieces.
+// Log-sum-exp merge of the pieces of units cut by chunk boundaries.  The
+// G x D outputs of a unit are split into slices of kMergeThreads, one
+// workgroup per (unit, slice) and one output per thread; the unit's record
+// (first slot, piece count) comes from the decode kernel.  All loads of a
+// round are unconditional and independent (padding pieces past the count
+// re-read the last piece and get weight 0), so a round of up to 64 pieces has
+// all its loads in flight at once.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeBatch = 32;        // pieces merged per round
+
+template <int D, int G>
+constexpr int kMergeSlices = (G * D + kMergeThreads - 1) / kMergeThreads;
+
+template <int D, int G, int NB>
+__device__ __forceinline__ void merge_rounds(const DecodeParams& p, int64_t sl0, int npieces, int e,
+                                             float (&s_m)[64][G], float (&s_l)[64][G], float& M,
+                                             float& den, float& acc) {
+  const int t = threadIdx.x;
+  const int64_t fk = sl0 >> 1;
+  // slot of piece k: the first piece sits in the slot its wave recorded, the
+  // later ones open the following chunks (slot 0 of each)
+  auto slot = [&](int k) __attribute__((always_inline)) { return k == 0 ? sl0 : (fk + k) * 2; };
+  const int h = e / D;
+  for (int k0 = 0; k0 < npieces; k0 += NB) {
+    const int last = npieces - 1 - k0;          // last valid index of this round
+    for (int i = t; i < NB * G; i += kMergeThreads) {
+      const int k = i / G, hh = i - k * G;
+      const int64_t j = slot(k0 + min(k, last)) * G + hh;
+      const float m = p.ws_m[j], l = p.ws_l[j];
+      s_m[k][hh] = k <= last ? m : -INFINITY;
+      s_l[k][hh] = k <= last ? l : 0.0f;
+    }
+    float o[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) o[k] = p.ws_o[slot(k0 + min(k, last)) * (G * D) + e];
+    __syncthreads();
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) Mn = fmaxf(Mn, s_m[k][h]);
+    const float a = (M == -INFINITY) ? 0.0f : fast_exp2(M - Mn);
+    den *= a;
+    acc *= a;
+    M = Mn;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const float w = s_l[k][h] * fast_exp2(s_m[k][h] - M);   // 0 for padding pieces
+      den += w;
+      acc = fmaf(w, o[k], acc);
+    }
+    __syncthreads();
+  }
+}
 
 template <int D, int G, int QF>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
-  constexpr int R = (G * D + kMergeThreads - 1) / kMergeThreads;   // outputs per thread
-  __shared__ float s_m[kMergeBatch][G], s_l[kMergeBatch][G];
+  constexpr int S = kMergeSlices<D, G>;
+  __shared__ float s_m[64][G], s_l[64][G];
   const int ngc = p.group / G;
   const int NY = p.num_kv_heads * ngc;
-  const int u = blockIdx.x;
+  const int u = blockIdx.x / S;
+  const int e_raw = (blockIdx.x - u * S) * kMergeThreads + threadIdx.x;
+  const int e = min(e_raw, G * D - 1);
   const int npieces = p.ws_unit[(int64_t)u * 2 + 1];
   if (npieces == 0) return;                   // finished inside one chunk, or empty
   const int64_t sl0 = p.ws_unit[(int64_t)u * 2];
-  const int64_t fk = sl0 >> 1;
   const int s = u / NY;
   const int y = u - s * NY;
   const int hk = y / ngc;
   const int h0 = hk * p.group + (y - hk * ngc) * G;
-  uint16_t* out = static_cast<uint16_t*>(p.out) + ((int64_t)s * p.num_q_heads + h0) * D;
-  const int t = threadIdx.x;
-  auto slot = [&](int k) __attribute__((always_inline)) { return k == 0 ? sl0 : (fk + k) * 2; };
-
-  float M[G], den[G], acc[R];
-#pragma unroll
-  for (int h = 0; h < G; ++h) { M[h] = -INFINITY; den[h] = 0.0f; }
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-  for (int k0 = 0; k0 < npieces; k0 += kMergeBatch) {
-    const int cnt = min(kMergeBatch, npieces - k0);
-    if (t < cnt * G) {
-      const int k = t / G, h = t - k * G;
-      const int64_t i = slot(k0 + k) * G + h;
-      s_m[k][h] = p.ws_m[i];
-      s_l[k][h] = p.ws_l[i];
-    }
-    float o[R][kMergeBatch];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int e = min(t + r * kMergeThreads, G * D - 1);
-      const int h = e / D, d = e - h * D;
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k)
-        o[r][k] = k < cnt ? p.ws_o[(slot(k0 + k) * G + h) * D + d] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float Mn = M[h];
-      for (int k = 0; k < cnt; ++k) Mn = fmaxf(Mn, s_m[k][h]);
-      const float a = (M[h] == -INFINITY) ? 0.0f : fast_exp2(M[h] - Mn);
-      den[h] *= a;
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (min(t + r * kMergeThreads, G * D - 1) / D == h) acc[r] *= a;
-      M[h] = Mn;
-    }
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      if (k < cnt) {
-        float w[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          w[h] = s_l[k][h] * fast_exp2(s_m[k][h] - M[h]);
-          den[h] += w[h];
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int h = min(t + r * kMergeThreads, G * D - 1) / D;
-          acc[r] = fmaf(w[h], o[r][k], acc[r]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = t + r * kMergeThreads;
-    if (e < G * D) out[e] = f32_to_16<QF>(acc[r] / den[e / D] * p.out_scale);
+  float M = -INFINITY, den = 0.0f, acc = 0.0f;
+  if (npieces <= 16)
+    merge_rounds<D, G, 16>(p, sl0, npieces, e, s_m, s_l, M, den, acc);
+  else
+    merge_rounds<D, G, 64>(p, sl0, npieces, e, s_m, s_l, M, den, acc);
+  if (e_raw < G * D) {
+    uint16_t* out = static_cast<uint16_t*>(p.out) + ((int64_t)s * p.num_q_heads + h0) * D;
+    out[e] = f32_to_16<QF>(acc / den * p.out_scale);
   }
 }
 
@@ -777,8 +770,9 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_
   }
   hipError_t e = hipLaunchKernel(k, dim3(p.num_workers / kNW), dim3(kNW * 64), args, 0, stream);
   if (e != hipSuccess) return e;
-  const int units = p.num_seqs * p.num_kv_heads * (p.group / p.head_chunk);
-  return hipLaunchKernel(mk, dim3(units), dim3(kMergeThreads), args, 0, stream);
+  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * (p.group / p.head_chunk);
+  const int64_t slices = (p.head_chunk * head_dim + kMergeThreads - 1) / kMergeThreads;
+  return hipLaunchKernel(mk, dim3((unsigned)(units * slices)), dim3(kMergeThreads), args, 0, stream);
 }
 
 }  // namespace vp
