@@ -99,7 +99,8 @@ typedef struct vllm_attn_opts {
                                are merged with the log-sum-exp rule by a second kernel */
   int32_t flags;            /* reserved, must be 0 */
   void* workspace;          /* device scratch of the decode (piece records, page prefix,
-                               partial results of cut sequences), 256-byte aligned; needs no
+                               partial results of cut sequences, a spare page read by
+                               prefetches past the end), 256-byte aligned; needs no
                                initialisation; calls that share a workspace must not overlap.
                                NULL = the library allocates one stream-ordered
                                (hipMallocAsync / hipFreeAsync on hip_stream) for the call */

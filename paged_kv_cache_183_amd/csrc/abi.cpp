@@ -166,13 +166,14 @@ vllm_status pick_chunk_tokens(int32_t requested, int32_t* tokens) {
 struct DecodePlan {
   int32_t head_chunk, units_per_seq, chunk_pages;
   int64_t pages_bound, max_chunks;
-  size_t cnt_off, pre_off, o_off, m_off, l_off, bytes;
+  size_t cnt_off, pre_off, o_off, m_off, l_off, spare_off, bytes;
 };
 
 // Workspace layout of a decode: per-unit piece records (2 ints per unit),
-// page prefix (B + 3 ints), then the partial outputs, maxima and sums of up
-// to 2 pieces per chunk.  The kernels rewrite every part they read, so the
-// workspace needs no initialisation.
+// page prefix (B + 3 ints), the partial outputs, maxima and sums of up to 2
+// pieces per chunk, then one spare page that the prefetch past the end of a
+// stretch of pages reads (its values are never used).  The kernels rewrite
+// every part whose values they use, so the workspace needs no initialisation.
 vllm_status plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t max_blocks,
                         int32_t chunk_tokens, DecodePlan* dp) {
   DecodePlan x{};
@@ -198,7 +199,8 @@ vllm_status plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t m
   x.o_off = x.pre_off + up((size_t)(B + 3) * 4);
   x.m_off = x.o_off + up(pieces * (size_t)D * 4);
   x.l_off = x.m_off + up(pieces * 4);
-  x.bytes = x.l_off + up(pieces * 4);
+  x.spare_off = x.l_off + up(pieces * 4);
+  x.bytes = x.spare_off + up((size_t)16 * (size_t)D * 2);
   *dp = x;
   return VLLM_OK;
 }
@@ -408,6 +410,7 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
   p.ws_o = reinterpret_cast<float*>(base + dp.o_off);
   p.ws_m = reinterpret_cast<float*>(base + dp.m_off);
   p.ws_l = reinterpret_cast<float*>(base + dp.l_off);
+  p.ws_spare = base + dp.spare_off;
   hipError_t e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
   if (owned) {
     hipError_t e2 = hipFreeAsync(ws, stream);

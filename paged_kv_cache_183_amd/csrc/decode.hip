@@ -38,8 +38,9 @@
 //    accumulation; the row sums use the same rounded probabilities.
 //  * The next page's K is loaded as soon as Q.K has consumed the registers,
 //    and the next V as soon as P.V has; these loads are unconditional (past
-//    the end they re-read the last page) so that the compiler can keep the
-//    buffers in flight across iterations.
+//    the end of the stretch they read a spare page of the workspace, which
+//    stays in L2) so that the compiler can keep the buffers in flight across
+//    iterations.
 #include <cstdlib>
 #include <utility>
 
@@ -324,6 +325,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
       const uint8_t* kbase = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
       const uint8_t* vbase = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes +
                              rv * ROWB + cv * CB;
+      const uint8_t* spare = static_cast<const uint8_t*>(p.ws_spare);
+      const uint8_t* spare_v = spare + rv * ROWB + cv * CB;
       const int count = i1 - i0;
       // Block ids, 64 pages per lane vector; the next 64 are fetched one
       // batch ahead so that reading them never waits on the page loads.
@@ -342,13 +345,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
         }
         return __builtin_amdgcn_readlane(bt_cur, jj - bt_base);
       };
-      auto load_k = [&](int blk, LT (&kd)[NKI]) __attribute__((always_inline)) {
-        const uint8_t* kp = kbase + blk * blk_stride;
+      // kp: the page's K base (this kv-head); vp: its V base plus this lane's offset
+      auto load_k = [&](const uint8_t* kp, LT (&kd)[NKI]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NKI; ++k) kd[k] = ld_stream<LT>(kp + koff[k]);
       };
-      auto load_v = [&](int blk, LT (&vd)[NKI]) __attribute__((always_inline)) {
-        const uint8_t* vp = vbase + blk * blk_stride;
+      auto load_v = [&](const uint8_t* vp, LT (&vd)[NKI]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NKI; ++k) vd[k] = ld_stream<LT>(vp + k * RPIV * ROWB);
       };
@@ -368,8 +370,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int u = 0; u < PD; ++u) {
         const int b0 = blk_of(min(u, count - 1));
-        load_k(b0, kd[u]);
-        load_v(b0, vd[u]);
+        load_k(u < count ? kbase + b0 * blk_stride : spare, kd[u]);
+        load_v(u < count ? vbase + b0 * blk_stride : spare_v, vd[u]);
       }
       for (int jb = 0; jb < count; jb += PD) {
 #pragma unroll
@@ -378,7 +380,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
           const bool valid = jj < count;
           const int t0 = (sr.lo_page + i0 + min(jj, count - 1)) * 16;
           const bool full = (t0 >= sr.lo) && (t0 + 16 <= sr.n);
+          // page loaded into this buffer next; past the end of the stretch
+          // the loads read the spare page instead (kept hot in L2, its
+          // values are never used)
+          const bool past = jj + PD >= count;
           const int bn = blk_of(min(jj + PD, count - 1));
+          const uint8_t* knext = past ? spare : kbase + bn * blk_stride;
+          const uint8_t* vnext = past ? spare_v : vbase + bn * blk_stride;
           float sc[TPL][G];
           if (valid) {
             // ---- Q.K (K role) ----
@@ -403,7 +411,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-          load_k(bn, kd[u]);
+          load_k(knext, kd[u]);
           __builtin_amdgcn_sched_barrier(0);
           if (valid) {
 #pragma unroll
@@ -499,7 +507,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-          load_v(bn, vd[u]);
+          load_v(vnext, vd[u]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

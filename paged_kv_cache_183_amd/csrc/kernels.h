@@ -42,6 +42,7 @@ struct DecodeParams {
   float* ws_m;                 // [2 * max_chunks, G]    running max, log2 units
   float* ws_l;                 // [2 * max_chunks, G]    sum of exp2(s - m)
   int32_t* ws_unit;            // [B * units][2]: slot of the first piece, number of pieces
+  const void* ws_spare;        // one page (16 x D 16-bit) read by prefetches past the end
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;

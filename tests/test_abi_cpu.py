@@ -100,7 +100,8 @@ def test_decode_validation():
 
 def test_workspace_size():
     # piece records (2 ints per unit) + page prefix (B + 3 ints) + 2 pieces
-    # per chunk of G x (D + 2) floats, each region rounded up to 256 bytes
+    # per chunk of G x (D + 2) floats + one spare page, each region rounded
+    # up to 256 bytes
     def expect(B, Hq, Hkv, D, mb, part):
         g = Hq // Hkv
         gc = g if g <= 8 else max(c for c in range(1, 9) if g % c == 0)
@@ -110,7 +111,8 @@ def test_workspace_size():
         up = lambda v: (v + 255) // 256 * 256
         pieces = chunks * 2 * gc
         units = B * Hkv * (g // gc)
-        return up(units * 8) + up((B + 3) * 4) + up(pieces * D * 4) + 2 * up(pieces * 4)
+        return (up(units * 8) + up((B + 3) * 4) + up(pieces * D * 4) + 2 * up(pieces * 4)
+                + up(16 * D * 2))
     for args in [(4, 4, 2, 64, 3, 0), (32, 32, 8, 128, 256, 0), (16, 40, 8, 128, 2048, 0),
                  (4, 4, 2, 64, 3, 16), (32, 32, 8, 128, 256, 512), (3, 16, 1, 128, 10, 0)]:
         assert P.vllm_paged_attn_workspace_size(*args) == expect(*args), args
