@@ -44,10 +44,11 @@ METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + seqs/s"
 PREFILL_METRIC = "chunked-prefill paged attention: TFLOP/s (% bf16 MFMA peak) + tokens/s"
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode call (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy)
-    from the committed counter summary of this workload, or None when there is
-    none or the decode kernel's sources changed since the counters were taken."""
+def measured_traffic(workload: str, sources=("decode.hip", "common.h")):
+    """HBM bytes per call (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy)
+    from the committed counter summary ``profiles/<workload>_hbm_counters.txt``,
+    or None when there is none or the kernel sources changed since the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.txt")
     if not os.path.exists(path):
@@ -55,7 +56,7 @@ def measured_traffic(workload: str):
     fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line.startswith(("source_sha256: ", "traffic_bytes_per_call: ")))
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h"):
+    for f in sources:
         with open(os.path.join(ROOT, "paged_kv_cache_183_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if fields.get("source_sha256") != h.hexdigest():
@@ -63,8 +64,9 @@ def measured_traffic(workload: str):
     return int(fields["traffic_bytes_per_call"])
 
 
-def decode_bytes(case) -> dict:
-    """Algorithmic bytes of one decode call and of one step's cache write."""
+def decode_bytes(case, shared_tokens: int = 0) -> dict:
+    """Algorithmic bytes of one decode call and of one step's cache write.
+    ``unique_*`` count the K/V of a prefix shared by every sequence once."""
     eb = ELEM_BYTES[case.kv_dtype]
     qb = 2
     B, Hq, D, Hkv = case.num_seqs, case.num_q_heads, case.head_dim, case.num_kv_heads
@@ -77,7 +79,11 @@ def decode_bytes(case) -> dict:
     kv = kept * Hkv * D * eb * 2
     other = 2 * B * Hq * D * qb + pages * 4 + B * 4
     write = B * Hkv * D * (2 * qb + 2 * eb) + B * 8
-    return dict(kv=kv, decode=kv + other, write=write, kept_tokens=kept)
+    # a prefix shared by every sequence: its bytes counted once
+    shared = int(shared_tokens)
+    unique_kv = kv - (B - 1) * shared * Hkv * D * eb * 2 if shared and case.window == 0 else kv
+    return dict(kv=kv, decode=kv + other, write=write, kept_tokens=kept, unique_kv=unique_kv,
+                unique_decode=unique_kv + other)
 
 
 def prefill_work(case) -> dict:
@@ -144,24 +150,6 @@ def cpu_baseline_prefill(case, seconds: float) -> dict:
                       f"chunked-prefill batch ({len(done)} of {case.num_seqs}), {dt:.1f} s"}
 
 
-def measured_prefill_traffic(workload: str):
-    """HBM bytes per prefill call from the committed counter summary, or None
-    when there is none or the prefill kernel's sources changed since."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.txt")
-    if not os.path.exists(path):
-        return None
-    fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
-                  if line.startswith(("source_sha256: ", "traffic_bytes_per_call: ")))
-    h = hashlib.sha256()
-    for f in ("prefill.hip", "common.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_183_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if fields.get("source_sha256") != h.hexdigest():
-        return None
-    return int(fields["traffic_bytes_per_call"])
-
-
 def bench_prefill(case, steps: int, warmup: int) -> dict:
     """Time the chunked-prefill call on ``case`` (K/V written by the library's
     cache write first, untimed) with HIP events around each call."""
@@ -206,7 +194,7 @@ def bench_prefill(case, steps: int, warmup: int) -> dict:
             "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_prefill_traffic(case.name)}}
+                         "traffic": measured_traffic(case.name, ("prefill.hip", "common.h"))}}
 
 
 def cpu_baseline(case, seconds: float) -> dict:
@@ -258,6 +246,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies rotated over steps (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="decode a prefix-shared workload without reading the shared pages once")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill measurement appended to the decode line")
     ap.add_argument("--graph", action="store_true",
@@ -285,7 +275,8 @@ def main():
         return
 
     case = make_case(args.config)
-    by = decode_bytes(case)
+    shared_tokens = 0 if args.no_shared_prefix else int(cfg.get("shared_tokens", 0))
+    by = decode_bytes(case, shared_tokens)
     # CPU baseline first: it forks worker processes, which must happen
     # before this process initialises the GPU.
     cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
@@ -314,8 +305,15 @@ def main():
     out = torch.empty_like(q)
     bt, ctx = case.block_tables.to(dev), case.context_lens.to(dev)
     part = args.partition or case.partition
-    ws_bytes = P.vllm_paged_attn_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
-                                                case.head_dim, case.block_tables.shape[1], part)
+    shared_pages = shared_tokens // 16
+    if shared_pages:
+        ws_bytes = P.vllm_paged_attn_shared_prefix_workspace_size(
+            case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+            case.block_tables.shape[1], shared_pages, part)
+    else:
+        ws_bytes = P.vllm_paged_attn_workspace_size(case.num_seqs, case.num_q_heads,
+                                                    case.num_kv_heads, case.head_dim,
+                                                    case.block_tables.shape[1], part)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -327,9 +325,15 @@ def main():
 
     def decode(r):
         kc, vc = pools[r]
-        P.vllm_paged_attn_decode(out, q, view(kc), view(vc), bt, ctx, case.scale, case.window,
-                                 k_scale=case.k_scale, v_scale=case.v_scale,
-                                 partition_size=part, workspace=ws)
+        if shared_pages:
+            P.vllm_paged_attn_decode_shared_prefix(out, q, view(kc), view(vc), bt, ctx,
+                                                   shared_pages, case.scale, case.window,
+                                                   k_scale=case.k_scale, v_scale=case.v_scale,
+                                                   partition_size=part, workspace=ws)
+        else:
+            P.vllm_paged_attn_decode(out, q, view(kc), view(vc), bt, ctx, case.scale, case.window,
+                                     k_scale=case.k_scale, v_scale=case.v_scale,
+                                     partition_size=part, workspace=ws)
 
     for i in range(max(args.warmup, R)):          # eager warm-up (also checks every replica)
         write(i % R)
@@ -382,7 +386,9 @@ def main():
 
     step_bytes = by["decode"] + by["write"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = by["decode"] / (dec_avg * 1e-3) / 1e9
+    # roofline on the bytes the path must move: with the shared prefix read
+    # once, its K/V count once
+    achieved = (by["unique_decode"] if shared_pages else by["decode"]) / (dec_avg * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -402,6 +408,8 @@ def main():
                    "context_lens": cfg.get("ctx_range") or cfg.get("ctx_list"),
                    "kept_tokens": by["kept_tokens"], "kv_bytes_per_step": by["kv"],
                    "bytes_per_step": step_bytes, "partition_tokens": part or "auto",
+                   "shared_prefix_pages": shared_pages,
+                   "unique_kv_bytes_per_step": by["unique_kv"],
                    "pool_replicas": R, "seed": args.config,
                    "launch": "hip_graph_replay" if args.graph else "eager"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
@@ -410,10 +418,15 @@ def main():
                            "p10": round(float(np.percentile(dec_ms, 10)), 5),
                            "p50": round(float(np.percentile(dec_ms, 50)), 5),
                            "p90": round(float(np.percentile(dec_ms, 90)), 5)},
-        "roofline": {"bound": "hbm", "kernel": "decode call (decode_kernel + decode_merge_kernel)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("decode call (attn_tile_kernel shared-prefix pass + decode_kernel + "
+                                "decode_merge_kernel), unique bytes" if shared_pages else
+                                "decode call (decode_kernel + decode_merge_kernel)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(case.name)},
+                     "traffic": (measured_traffic(case.name + "_shared_prefix",
+                                                  ("decode.hip", "prefill.hip", "common.h"))
+                                 if shared_pages else measured_traffic(case.name))},
         "cpu_baseline": cpu,
     }
     if not args.no_prefill:

@@ -179,6 +179,45 @@ size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t partition_size);
 
 /*
+ * Decode with a prefix shared by the whole batch read once ("cascade"): the
+ * same result as vllm_paged_attn_decode, for batches whose sequences all map
+ * their first `shared_pages` logical pages to the same physical pages (a
+ * prefix hit binds a new sequence's block table to existing pages:
+ * "Building and Deploying vllm.cpp", Step 3).  Those pages are read from
+ * sequence 0's table (the other sequences' first shared_pages entries are not
+ * read) once per kv-head for the whole batch: every sequence's query is
+ * scored against them together on the matrix cores, in splits of 16 pages.
+ * The rest of each sequence is decoded as usual, and the parts are merged with
+ * the log-sum-exp rule.  Keys of the shared pages are kept per sequence as in
+ * decode: t < n (a sequence shorter than the prefix uses its first n tokens)
+ * and t >= n - window.  The probabilities of the shared part are rounded to
+ * q's 16-bit format before the product with V, as in decode.
+ *   shared_pages  0 .. max_blocks_per_seq (0: same as vllm_paged_attn_decode)
+ *   scale         > 0 when shared_pages > 0
+ *   other arguments as vllm_paged_attn_decode; the workspace must hold
+ *   vllm_paged_attn_shared_prefix_workspace_size bytes.
+ * Supported: as vllm_paged_attn_decode, with D = 128 when shared_pages > 0.
+ */
+vllm_status vllm_paged_attn_decode_shared_prefix(vllm_tensor* out, const vllm_tensor* q,
+                                                 const vllm_tensor* k_cache,
+                                                 const vllm_tensor* v_cache,
+                                                 const vllm_tensor* block_tables,
+                                                 const vllm_tensor* context_lens,
+                                                 int32_t shared_pages, float scale, int32_t window,
+                                                 const vllm_attn_opts* opts, void* hip_stream);
+
+/*
+ * Bytes of workspace vllm_paged_attn_decode_shared_prefix needs for these
+ * sizes (sizes and partition_size only).  Returns 0 for invalid arguments
+ * (including head_dim other than 128, or shared_pages outside
+ * [0, max_blocks_per_seq]).
+ */
+size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_blocks_per_seq, int32_t shared_pages,
+                                                    int32_t partition_size);
+
+/*
  * Chunked-prefill attention on matrix cores: sequence s has Q_s =
  * query_start_loc[s+1] - query_start_loc[s] query tokens (rows
  * query_start_loc[s] .. query_start_loc[s+1]-1 of q) at positions

@@ -11,7 +11,10 @@ from .binding import (  # noqa: F401
     vllm_abi_version,
     vllm_last_error,
     vllm_paged_attn_decode,
+    vllm_paged_attn_decode_shared_prefix,
     vllm_paged_attn_prefill,
-    vllm_paged_attn_workspace_size,
+    vllm_paged_attn_shared_prefix_workspace_size,
+    vllm_paged_attn_workspace_size, vllm_paged_attn_decode_shared_prefix,
+    vllm_paged_attn_shared_prefix_workspace_size,
     vllm_paged_cache_write,
 )

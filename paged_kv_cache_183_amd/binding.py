@@ -32,6 +32,7 @@ BLOCK_SIZE = 16
 
 EXPORTED = ["vllm_abi_version", "vllm_last_error", "vllm_paged_cache_write",
             "vllm_paged_attn_decode", "vllm_paged_attn_workspace_size",
+            "vllm_paged_attn_decode_shared_prefix", "vllm_paged_attn_shared_prefix_workspace_size",
             "vllm_paged_attn_prefill"]
 
 
@@ -69,6 +70,12 @@ def _load():
                                            ctypes.c_void_p]
     lib.vllm_paged_attn_workspace_size.restype = ctypes.c_size_t
     lib.vllm_paged_attn_workspace_size.argtypes = [ctypes.c_int32] * 6
+    lib.vllm_paged_attn_decode_shared_prefix.restype = ctypes.c_int
+    lib.vllm_paged_attn_decode_shared_prefix.argtypes = [T, T, T, T, T, T, ctypes.c_int32,
+                                                         ctypes.c_float, ctypes.c_int32, O,
+                                                         ctypes.c_void_p]
+    lib.vllm_paged_attn_shared_prefix_workspace_size.restype = ctypes.c_size_t
+    lib.vllm_paged_attn_shared_prefix_workspace_size.argtypes = [ctypes.c_int32] * 7
     lib.vllm_paged_attn_prefill.restype = ctypes.c_int
     lib.vllm_paged_attn_prefill.argtypes = [T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float,
                                             ctypes.c_int32, O, ctypes.c_void_p]
@@ -156,6 +163,28 @@ def vllm_paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _check(LIB.vllm_paged_attn_decode(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
                                       ctypes.c_int32(window), ctypes.byref(o),
                                       ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_paged_attn_shared_prefix_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 max_blocks_per_seq, shared_pages,
+                                                 partition_size=0) -> int:
+    return int(LIB.vllm_paged_attn_shared_prefix_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, shared_pages,
+        partition_size))
+
+
+def vllm_paged_attn_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
+                                         shared_pages, scale, window=0, k_scale=0.0, v_scale=0.0,
+                                         partition_size=0, workspace=None, stream=None) -> None:
+    """Decode attention into ``out`` [B, Hq, D] with the first ``shared_pages``
+    pages of every sequence (sequence 0's) read once for the batch."""
+    args = [tensor_desc(x) for x in (out, q, k_cache, v_cache, block_tables, context_lens)]
+    o = _opts(k_scale, v_scale, partition_size, workspace)
+    _check(LIB.vllm_paged_attn_decode_shared_prefix(*[ctypes.byref(a) for a in args],
+                                                    ctypes.c_int32(shared_pages),
+                                                    ctypes.c_float(scale), ctypes.c_int32(window),
+                                                    ctypes.byref(o),
+                                                    ctypes.c_void_p(_stream(stream))))
 
 
 def vllm_paged_attn_prefill(out, q, k_cache, v_cache, block_tables, query_start_loc,

@@ -166,16 +166,20 @@ vllm_status pick_chunk_tokens(int32_t requested, int32_t* tokens) {
 struct DecodePlan {
   int32_t head_chunk, units_per_seq, chunk_pages;
   int64_t pages_bound, max_chunks;
-  size_t cnt_off, pre_off, o_off, m_off, l_off, spare_off, bytes;
+  int32_t num_splits;
+  size_t cnt_off, pre_off, o_off, m_off, l_off, spare_off, po_off, pm_off, pl_off, uo_off, um_off,
+      ul_off, bytes;
 };
 
 // Workspace layout of a decode: per-unit piece records (2 ints per unit),
 // page prefix (B + 3 ints), the partial outputs, maxima and sums of up to 2
-// pieces per chunk, then one spare page that the prefetch past the end of a
-// stretch of pages reads (its values are never used).  The kernels rewrite
+// pieces per chunk, one spare page that the prefetch past the end of a
+// stretch of pages reads (its values are never used), then (shared prefix
+// only) the partial outputs, maxima and sums of the prefix splits and of the
+// units decoded whole inside one chunk.  The kernels rewrite
 // every part whose values they use, so the workspace needs no initialisation.
 vllm_status plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t max_blocks,
-                        int32_t chunk_tokens, DecodePlan* dp) {
+                        int32_t chunk_tokens, int32_t shared_pages, DecodePlan* dp) {
   DecodePlan x{};
   x.head_chunk = vp::decode_head_chunk((int)(Hq / Hkv));
   x.units_per_seq = (int32_t)(Hkv * (Hq / Hkv / x.head_chunk));
@@ -200,7 +204,18 @@ vllm_status plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t m
   x.m_off = x.o_off + up(pieces * (size_t)D * 4);
   x.l_off = x.m_off + up(pieces * 4);
   x.spare_off = x.l_off + up(pieces * 4);
-  x.bytes = x.spare_off + up((size_t)16 * (size_t)D * 2);
+  // shared-prefix partials: [splits, B, Hq] rows of D outputs, max and sum
+  x.num_splits = (shared_pages + vp::kPrefixSplitPages - 1) / vp::kPrefixSplitPages;
+  const size_t prow = (size_t)x.num_splits * (size_t)B * (size_t)Hq;
+  x.po_off = x.spare_off + up((size_t)16 * (size_t)D * 2);
+  x.pm_off = x.po_off + up(prow * (size_t)D * 4);
+  x.pl_off = x.pm_off + up(prow * 4);
+  // whole-unit partials (shared prefix only): [units, G] rows
+  const size_t urow = shared_pages > 0 ? (size_t)B * (size_t)x.units_per_seq * x.head_chunk : 0;
+  x.uo_off = x.pl_off + up(prow * 4);
+  x.um_off = x.uo_off + up(urow * (size_t)D * 4);
+  x.ul_off = x.um_off + up(urow * 4);
+  x.bytes = x.ul_off + up(urow * 4);
   *dp = x;
   return VLLM_OK;
 }
@@ -294,16 +309,38 @@ size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
   DecodePlan dp;
   if (pick_chunk_tokens(partition_size, &chunk_tokens) != VLLM_OK ||
       plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, chunk_tokens,
-                  &dp) != VLLM_OK)
+                  0, &dp) != VLLM_OK)
     return 0;
   return dp.bytes;
 }
 
-vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
-                                   const vllm_tensor* k_cache, const vllm_tensor* v_cache,
-                                   const vllm_tensor* block_tables,
-                                   const vllm_tensor* context_lens, float scale, int32_t window,
-                                   const vllm_attn_opts* opts, void* hip_stream) {
+size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_blocks_per_seq, int32_t shared_pages,
+                                                    int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      head_dim != 128 || max_blocks_per_seq < 0 || shared_pages < 0 ||
+      shared_pages > max_blocks_per_seq)
+    return 0;
+  int32_t chunk_tokens = 0;
+  DecodePlan dp;
+  if (pick_chunk_tokens(partition_size, &chunk_tokens) != VLLM_OK ||
+      plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, chunk_tokens,
+                  shared_pages, &dp) != VLLM_OK)
+    return 0;
+  return dp.bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Decode, optionally with the first shared_pages pages of every sequence
+// handled by the shared-prefix pass (read once per kv-head for the batch).
+vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor* k_cache,
+                       const vllm_tensor* v_cache, const vllm_tensor* block_tables,
+                       const vllm_tensor* context_lens, int32_t shared_pages, float scale,
+                       int32_t window, const vllm_attn_opts* opts, void* hip_stream) {
   VP_TRY(check_tensor(out, "out", 3));
   VP_TRY(check_tensor(q, "q", 3));
   VP_TRY(check_tensor(k_cache, "k_cache", 4));
@@ -353,7 +390,14 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
   VP_TRY(pick_chunk_tokens(opts ? opts->partition_size : 0, &chunk_tokens));
   const int64_t max_blocks = block_tables->shape[1];
   DecodePlan dp;
-  VP_TRY(plan_decode(B, Hq, Hkv, D, max_blocks, chunk_tokens, &dp));
+  if (shared_pages < 0 || shared_pages > max_blocks)
+    return fail(VLLM_ERR_INVALID_ARG, "shared_pages %d outside [0, max_blocks_per_seq = %lld]",
+                (int)shared_pages, (long long)max_blocks);
+  if (shared_pages > 0 && D != 128)
+    return fail(VLLM_ERR_UNSUPPORTED, "shared prefix: head_dim %lld, supported 128", (long long)D);
+  if (shared_pages > 0 && !(scale > 0.0f))
+    return fail(VLLM_ERR_INVALID_ARG, "shared prefix: scale must be positive");
+  VP_TRY(plan_decode(B, Hq, Hkv, D, max_blocks, chunk_tokens, shared_pages, &dp));
   if (B == 0) return ok();
   if (opts && opts->workspace && opts->workspace_bytes < dp.bytes)
     return fail(VLLM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, dp.bytes);
@@ -411,13 +455,69 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
   p.ws_m = reinterpret_cast<float*>(base + dp.m_off);
   p.ws_l = reinterpret_cast<float*>(base + dp.l_off);
   p.ws_spare = base + dp.spare_off;
-  hipError_t e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
+  hipError_t e = hipSuccess;
+  if (shared_pages > 0) {
+    vp::PrefillParams sp{};
+    sp.q = q->data;
+    sp.k_cache = k_cache->data;
+    sp.v_cache = v_cache->data;
+    sp.block_tables = p.block_tables;
+    sp.context_lens = p.context_lens;
+    sp.num_seqs = (int32_t)B;
+    sp.num_q_heads = (int32_t)Hq;
+    sp.num_kv_heads = (int32_t)Hkv;
+    sp.group = (int32_t)(Hq / Hkv);
+    sp.bt_stride = (int32_t)max_blocks;
+    sp.num_blocks = (int32_t)NB;
+    sp.window = window;
+    sp.score_scale = p.score_scale;
+    sp.shared_pages = shared_pages;
+    sp.split_pages = vp::kPrefixSplitPages;
+    sp.num_splits = dp.num_splits;
+    sp.pfx_o = reinterpret_cast<float*>(base + dp.po_off);
+    sp.pfx_m = reinterpret_cast<float*>(base + dp.pm_off);
+    sp.pfx_l = reinterpret_cast<float*>(base + dp.pl_off);
+    e = vp::launch_shared_prefix(sp, (int)D, kv_fmt, q_fmt, stream);
+    p.skip_tokens = shared_pages * 16;
+    p.num_splits = dp.num_splits;
+    p.pfx_o = sp.pfx_o;
+    p.pfx_m = sp.pfx_m;
+    p.pfx_l = sp.pfx_l;
+    p.ws_uo = reinterpret_cast<float*>(base + dp.uo_off);
+    p.ws_um = reinterpret_cast<float*>(base + dp.um_off);
+    p.ws_ul = reinterpret_cast<float*>(base + dp.ul_off);
+  }
+  if (e == hipSuccess) e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
   if (owned) {
     hipError_t e2 = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = e2;
   }
   VP_TRY(hip_status(e, "decode launch"));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
+                                   const vllm_tensor* k_cache, const vllm_tensor* v_cache,
+                                   const vllm_tensor* block_tables,
+                                   const vllm_tensor* context_lens, float scale, int32_t window,
+                                   const vllm_attn_opts* opts, void* hip_stream) {
+  return run_decode(out, q, k_cache, v_cache, block_tables, context_lens, 0, scale, window, opts,
+                    hip_stream);
+}
+
+vllm_status vllm_paged_attn_decode_shared_prefix(vllm_tensor* out, const vllm_tensor* q,
+                                                 const vllm_tensor* k_cache,
+                                                 const vllm_tensor* v_cache,
+                                                 const vllm_tensor* block_tables,
+                                                 const vllm_tensor* context_lens,
+                                                 int32_t shared_pages, float scale, int32_t window,
+                                                 const vllm_attn_opts* opts, void* hip_stream) {
+  return run_decode(out, q, k_cache, v_cache, block_tables, context_lens, shared_pages, scale,
+                    window, opts, hip_stream);
 }
 
 vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,

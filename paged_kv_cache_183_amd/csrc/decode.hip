@@ -184,6 +184,11 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int s) {
     return r;
   }
   r.lo = p.window > 0 ? max(0, r.n - p.window) : 0;
+  r.lo = max(r.lo, p.skip_tokens);             // shared prefix: decoded by its own pass
+  if (r.lo >= r.n) {
+    r.lo = 0; r.lo_page = 0; r.np = 0;
+    return r;
+  }
   r.lo_page = r.lo >> 4;
   r.np = ((r.n + 15) >> 4) - r.lo_page;
   return r;
@@ -267,11 +272,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
                                       : max((int64_t)1, (T + p.num_workers - 1) / p.num_workers);
   const int64_t num_chunks = (T + C - 1) / C;
 
-  // Sequences with no key to attend to get all-zero output rows.
+  // Sequences with no key to attend to get all-zero output rows (with a
+  // shared prefix the merge writes their rows from the prefix partials).
   for (int sq = blockIdx.x; sq < B; sq += gridDim.x) {
     if (pre[sq + 1] == pre[sq]) {
-      uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)sq * p.num_q_heads * D;
-      for (int i = threadIdx.x; i < p.num_q_heads * D; i += kNW * 64) o[i] = 0;
+      if (p.skip_tokens == 0) {
+        uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)sq * p.num_q_heads * D;
+        for (int i = threadIdx.x; i < p.num_q_heads * D; i += kNW * 64) o[i] = 0;
+      }
       for (int i = threadIdx.x; i < NY; i += kNW * 64) p.ws_unit[((int64_t)sq * NY + i) * 2 + 1] = 0;
     }
   }
@@ -306,7 +314,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
       const int i0 = (int)(off - (int64_t)y * sr.np);
       const int i1 = (int)min((int64_t)sr.np, i0 + (g_end - g));
       const int slot = first_seg ? 0 : 1;
-      const bool complete = (i0 == 0) && (i1 == sr.np);
+      // A unit finished inside this chunk writes its output directly, or,
+      // when shared-prefix partials still have to be merged in, its partial
+      // to a slot of its own (a chunk may hold several whole units).
+      const bool whole = (i0 == 0) && (i1 == sr.np);
+      const bool complete = whole && p.skip_tokens == 0;
       const int hk = y / ngc;
       const int h0 = hk * p.group + (y - hk * ngc) * G;
 
@@ -539,12 +551,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
           }
         }
       } else {
+        const int64_t unit = (int64_t)s * NY + y;
         const int64_t sl = chunk * 2 + slot;
+        float* wo = whole ? p.ws_uo + unit * G * D : p.ws_o + sl * G * D;
+        float* wm = whole ? p.ws_um + unit * G : p.ws_m + sl * G;
+        float* wl = whole ? p.ws_ul + unit * G : p.ws_l + sl * G;
         if (rv == 0) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             const float inv = 1.0f / l[h];
-            float* o = p.ws_o + (sl * G + h) * D + cv * 8;
+            float* o = wo + h * D + cv * 8;
             *reinterpret_cast<float4*>(o) =
                 make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
             *reinterpret_cast<float4*>(o + 4) =
@@ -554,20 +570,22 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
         if (lane == 0) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            p.ws_m[sl * G + h] = m[h];
-            p.ws_l[sl * G + h] = l[h];
+            wm[h] = m[h];
+            wl[h] = l[h];
           }
         }
       }
       // The wave holding page 0 of the unit records where its pieces are:
-      // (slot of the first piece, number of pieces), or 0 pieces if done.
+      // (slot of the first piece, number of pieces), or 0 pieces if done
+      // (a unit inside one chunk with a shared prefix has 1 piece).
       if (i0 == 0 && lane == 0) {
         int npieces = 0;
         if (!complete) {
           const int64_t base = g;                 // = NY * pre[s] + y * np
           npieces = (int)((base + sr.np - 1) / C - base / C + 1);
         }
-        p.ws_unit[((int64_t)s * NY + y) * 2] = (int32_t)(chunk * 2 + slot);
+        // (first slot -1: the single piece sits in the unit's own slot)
+        p.ws_unit[((int64_t)s * NY + y) * 2] = whole ? -1 : (int32_t)(chunk * 2 + slot);
         p.ws_unit[((int64_t)s * NY + y) * 2 + 1] = npieces;
       }
       g += i1 - i0;
@@ -589,27 +607,55 @@ template <int D, int G>
 constexpr int kMergeSlices = (G * D + kMergeThreads - 1) / kMergeThreads;
 
 template <int D, int G, int NB>
-__device__ __forceinline__ void merge_rounds(const DecodeParams& p, int64_t sl0, int npieces, int e,
+__device__ __forceinline__ void merge_rounds(const DecodeParams& p, int64_t unit, int64_t sl0,
+                                             int nsuf, int npieces, int64_t prow, int e,
                                              float (&s_m)[64][G], float (&s_l)[64][G], float& M,
                                              float& den, float& acc) {
   const int t = threadIdx.x;
   const int64_t fk = sl0 >> 1;
-  // slot of piece k: the first piece sits in the slot its wave recorded, the
-  // later ones open the following chunks (slot 0 of each)
-  auto slot = [&](int k) __attribute__((always_inline)) { return k == 0 ? sl0 : (fk + k) * 2; };
+  const int64_t split_rows = (int64_t)p.num_seqs * p.num_q_heads;
+  // Piece k < nsuf: a piece of the decode (the first sits in the slot its
+  // wave recorded, or in the unit's own slot when that is -1; the later ones
+  // open the following chunks, slot 0 of each); piece nsuf + i: split i of
+  // the shared-prefix partials.  Returns the row index of head 0 of the unit
+  // in the piece's (o, m, l) arrays.
+  auto ml_row = [&](int k, const float*& op, const float*& mp, const float*& lp)
+      __attribute__((always_inline)) {
+    if (k < nsuf) {
+      if (sl0 < 0) {
+        op = p.ws_uo;
+        mp = p.ws_um;
+        lp = p.ws_ul;
+        return unit * G;
+      }
+      op = p.ws_o;
+      mp = p.ws_m;
+      lp = p.ws_l;
+      return (k == 0 ? sl0 : (fk + k) * 2) * G;
+    }
+    op = p.pfx_o;
+    mp = p.pfx_m;
+    lp = p.pfx_l;
+    return (int64_t)(k - nsuf) * split_rows + prow;
+  };
   const int h = e / D;
   for (int k0 = 0; k0 < npieces; k0 += NB) {
     const int last = npieces - 1 - k0;          // last valid index of this round
     for (int i = t; i < NB * G; i += kMergeThreads) {
       const int k = i / G, hh = i - k * G;
-      const int64_t j = slot(k0 + min(k, last)) * G + hh;
-      const float m = p.ws_m[j], l = p.ws_l[j];
+      const float *op, *mp, *lp;
+      const int64_t j = ml_row(k0 + min(k, last), op, mp, lp) + hh;
+      const float m = mp[j], l = lp[j];
       s_m[k][hh] = k <= last ? m : -INFINITY;
       s_l[k][hh] = k <= last ? l : 0.0f;
     }
     float o[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) o[k] = p.ws_o[slot(k0 + min(k, last)) * (G * D) + e];
+    for (int k = 0; k < NB; ++k) {
+      const float *op, *mp, *lp;
+      const int64_t r0 = ml_row(k0 + min(k, last), op, mp, lp);
+      o[k] = op[r0 * D + e];
+    }
     __syncthreads();
     float Mn = M;
 #pragma unroll
@@ -618,9 +664,10 @@ __device__ __forceinline__ void merge_rounds(const DecodeParams& p, int64_t sl0,
     den *= a;
     acc *= a;
     M = Mn;
+    const float Mu = (M == -INFINITY) ? 0.0f : M;   // (every piece so far empty)
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const float w = s_l[k][h] * fast_exp2(s_m[k][h] - M);   // 0 for padding pieces
+      const float w = s_l[k][h] * fast_exp2(s_m[k][h] - Mu);  // 0 for padding / empty pieces
       den += w;
       acc = fmaf(w, o[k], acc);
     }
@@ -637,21 +684,25 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int u = blockIdx.x / S;
   const int e_raw = (blockIdx.x - u * S) * kMergeThreads + threadIdx.x;
   const int e = min(e_raw, G * D - 1);
-  const int npieces = p.ws_unit[(int64_t)u * 2 + 1];
+  const int nsuf = p.ws_unit[(int64_t)u * 2 + 1];
+  const int npieces = nsuf + p.num_splits;
   if (npieces == 0) return;                   // finished inside one chunk, or empty
   const int64_t sl0 = p.ws_unit[(int64_t)u * 2];
   const int s = u / NY;
   const int y = u - s * NY;
   const int hk = y / ngc;
   const int h0 = hk * p.group + (y - hk * ngc) * G;
+  const int64_t prow = (int64_t)s * p.num_q_heads + h0;    // row of head h0 in the prefix partials
   float M = -INFINITY, den = 0.0f, acc = 0.0f;
   if (npieces <= 16)
-    merge_rounds<D, G, 16>(p, sl0, npieces, e, s_m, s_l, M, den, acc);
+    merge_rounds<D, G, 16>(p, u, sl0, nsuf, npieces, prow, e, s_m, s_l, M, den, acc);
+  else if (npieces <= 32)
+    merge_rounds<D, G, 32>(p, u, sl0, nsuf, npieces, prow, e, s_m, s_l, M, den, acc);
   else
-    merge_rounds<D, G, 64>(p, sl0, npieces, e, s_m, s_l, M, den, acc);
+    merge_rounds<D, G, 64>(p, u, sl0, nsuf, npieces, prow, e, s_m, s_l, M, den, acc);
   if (e_raw < G * D) {
-    uint16_t* out = static_cast<uint16_t*>(p.out) + ((int64_t)s * p.num_q_heads + h0) * D;
-    out[e] = f32_to_16<QF>(acc / den * p.out_scale);
+    uint16_t* out = static_cast<uint16_t*>(p.out) + prow * D;
+    out[e] = f32_to_16<QF>(den > 0.0f ? acc / den * p.out_scale : 0.0f);
   }
 }
 

@@ -56,6 +56,17 @@ struct DecodeParams {
   int32_t max_chunks;          // capacity of the partial arrays (chunks)
   float score_scale;           // scale * log2(e) * k_scale
   float out_scale;             // v_scale (1 for 16-bit pools)
+  // Shared prefix (0 = none): keys below skip_tokens are left to the
+  // shared-prefix pass; every unit then goes through the merge, which also
+  // takes the num_splits prefix partials of each row.
+  int32_t skip_tokens;
+  int32_t num_splits;
+  float* ws_uo;                // [units, G, D] partials of whole units (shared prefix only)
+  float* ws_um;                // [units, G]
+  float* ws_ul;                // [units, G]
+  const float* pfx_o;
+  const float* pfx_m;
+  const float* pfx_l;
 };
 
 // kv_fmt: kF16 / kBF16 / kE4M3; q_fmt: kF16 / kBF16.
@@ -79,11 +90,25 @@ struct PrefillParams {
   int32_t num_blocks;
   int32_t max_query_len;
   int32_t window;
-  int32_t num_tiles;           // token tiles per sequence (set by launch_prefill)
-  float score_scale;           // scale * log2(e)
+  int32_t num_tiles;           // row tiles (set by the launchers)
+  float score_scale;           // scale * log2(e) (* k_scale for FP8 pools)
+  // shared-prefix partials (launch_shared_prefix only): the first
+  // shared_pages pages of every sequence, in splits of split_pages pages
+  int32_t shared_pages;
+  int32_t split_pages;
+  int32_t num_splits;
+  float* pfx_o;                // [num_splits, B, Hq, D] normalized partial outputs
+  float* pfx_m;                // [num_splits, B, Hq] running max, log2 units (-inf: empty)
+  float* pfx_l;                // [num_splits, B, Hq] sum of exp2(s - m)
 };
 
+// Chunked prefill: q_fmt = pool format (kF16 / kBF16).
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipStream_t stream);
+// Shared-prefix partials: kv_fmt = q_fmt or kE4M3.
+hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
+                                hipStream_t stream);
+// Pages per split of the shared-prefix pass.
+constexpr int kPrefixSplitPages = 16;
 
 // Decode work split: at most this many waves, each taking at least
 // kMinChunkPages pages when the chunk size is automatic.

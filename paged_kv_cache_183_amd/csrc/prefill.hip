@@ -1,20 +1,35 @@
-// Chunked-prefill attention on the matrix cores of gfx950.  Sequence s has
-// Q_s new query tokens at positions n - Q_s .. n - 1 of its n cached tokens
-// (their K/V are already in the block-paged pool); the query row at position
-// p attends to keys t <= p with t > p - window (window 0: no lower bound).
-// This is the paged attention of the vllm.cpp model forward (repository
-// listing, "What's implemented") for a chunk of several query tokens, with
-// the sliding window of its local-attention section; the pages give no kernel
-// design, this one is built for CDNA4.
+// Attention tiles on the matrix cores of gfx950, in two uses:
 //
-// Work: a workgroup takes TQ = 128 / g consecutive query tokens of one
-// sequence and the g query heads of one kv-head: 128 rows, 32 per wave.  It
-// walks the kept keys in blocks of 32 (two 16-token pages), staged through
-// LDS once for its four waves:
+// Chunked prefill.  Sequence s has Q_s new query tokens at positions
+// n - Q_s .. n - 1 of its n cached tokens (their K/V are already in the
+// block-paged pool); the query row at position p attends to keys t <= p with
+// t > p - window (window 0: no lower bound).  This is the paged attention of
+// the vllm.cpp model forward (repository listing, "What's implemented") for a
+// chunk of several query tokens, with the sliding window of its
+// local-attention section.
+//
+// Shared prefix.  Every sequence of a decode batch maps its first P logical
+// pages to the same physical pages (a prefix hit binds a new sequence's block
+// table to existing pages, "Building and Deploying vllm.cpp", Step 3).  The
+// decode queries of all sequences (one row per sequence and query head) are
+// scored against those pages together, so each shared page is read once per
+// kv-head instead of once per sequence; the result is a (max, sum, output)
+// partial per row and split of the prefix, merged later with the rest of the
+// sequence by the log-sum-exp rule.
+//
+// The pages give no kernel design; this one is built for CDNA4.
+//
+// Work: a workgroup takes 128 query rows, 32 per wave, and one kv-head: in
+// prefill TQ = 128 / g consecutive tokens of one sequence times the g query
+// heads; for the shared prefix 128 consecutive (sequence, query head) rows
+// and one split of the prefix pages.  Every row has its own kept key range
+// [lo, hi); the workgroup walks the union of its rows' ranges in blocks of 32
+// keys (two 16-token pages), staged through LDS once for its four waves:
 //  * K block row-major ([key][D], rows padded by 16 bytes);
 //  * V block transposed ([D][key pair], rows padded to 18 dwords), so that
 //    the P.V operand of a lane is two 8-byte reads; the staging writes and
-//    these reads hit distinct banks.
+//    these reads hit distinct banks.  FP8 pages are converted exactly to q's
+//    16-bit format when staged.
 // Global loads run two blocks ahead of the matrix cores.
 // Per block and wave, on v_mfma_f32_32x32x16 (bf16 or f16, fp32 accumulate):
 //  * S^T = K Q^T: the output column of a lane is its query row, so each lane
@@ -23,12 +38,12 @@
 //    row combined with one lane exchange; the running max only moves when a
 //    score exceeds it by more than 2^8;
 //  * P is rounded to q's 16-bit format (the row sums, on v_dot2 against
-//    ones, use the rounded values)
-//    and used in place as the B operand of O^T += V^T P^T: the contraction
-//    over keys follows the same key order in both operands, so no transpose
-//    of P is needed and O^T keeps each query row in one lane as well.
-// Keys at or past n (page tails, padding pages) are staged as zeros and
-// masked, and their block-table entries are never read.
+//    ones, use the rounded values) and used in place as the B operand of
+//    O^T += V^T P^T: the contraction over keys follows the same key order in
+//    both operands, so no transpose of P is needed and O^T keeps each query
+//    row in one lane as well.
+// Keys past every row's range (page tails, padding pages) are staged as zeros
+// and masked, and their block-table entries are never read.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,7 +52,7 @@ namespace vp {
 namespace {
 
 constexpr int kPW = 4;                 // waves per workgroup
-constexpr int kRows = 32 * kPW;        // query rows (token, head) per workgroup
+constexpr int kRows = 32 * kPW;        // query rows per workgroup
 constexpr int kBK = 32;                // keys per block
 constexpr float kTauP = 8.0f;          // rescale headroom, log2 units
 
@@ -79,125 +94,200 @@ __device__ __forceinline__ float half_max(float x) {
   return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
 }
 
+// Raw pool data of one 8-element chunk: 16 bytes for 16-bit pools, 8 for FP8.
+template <int KF> struct Raw { using T = uint4; };
+template <> struct Raw<kE4M3> { using T = uint2; };
+
+// The chunk as 8 values of q's 16-bit format (FP8 codes converted exactly).
+template <int KF, int QF>
+__device__ __forceinline__ uint4 to_q16(const typename Raw<KF>::T& x) {
+  if constexpr (KF != kE4M3) {
+    return x;
+  } else if constexpr (QF == kF16) {
+    return make_uint4(bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, false)),
+                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, true)),
+                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, false)),
+                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, true)));
+  } else {
+    return make_uint4(bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false)),
+                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true)),
+                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false)),
+                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true)));
+  }
+}
+
 }  // namespace
 
-template <int D, int QF>
-__global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
+// PFX = false: chunked prefill, normalized output rows.  PFX = true: shared
+// prefix, (max, sum, normalized output) partials per row and split.
+template <int D, int QF, int KF, bool PFX>
+__global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   static_assert(D == 128, "head_dim 128");
-  constexpr int CH = D / 8;                    // 16-byte chunks per K/V row
+  constexpr int CH = D / 8;                    // 8-element chunks per K/V row
+  constexpr int EB = KF == kE4M3 ? 1 : 2;      // bytes per pool element
   constexpr int KROW = D * 2 + 16;             // bytes per LDS K row
   constexpr int VROWW = kBK / 2 + 2;           // dwords per LDS V^T row (18)
   constexpr int KBUF = kBK * KROW;             // bytes per K buffer
   constexpr int VBUF = D * VROWW * 4;          // bytes per V^T buffer
-  constexpr int64_t kPageBytes = 16 * D * 2;
+  constexpr int64_t kPageBytes = 16 * D * EB;
+  using RawT = typename Raw<KF>::T;
   static_assert(kPW * 64 == 16 * CH, "staging map: one thread per (row-of-page, chunk)");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][KBUF];
   __shared__ __attribute__((aligned(16))) uint32_t s_v[2][VBUF / 4];
+  __shared__ int s_red[3];
 
   const int g = p.group;
-  const int tq = kRows / g;                    // query tokens per workgroup
-  // Workgroup -> (sequence, kv-head, token tile).  Workgroups go to the 8
-  // XCDs round-robin; (sequence, kv-head) pair u runs on XCD u % 8 with all
-  // its tiles (they share K/V in that XCD's L2), so every XCD sees every
-  // sequence and the XCDs get even work.  Later tiles attend to more keys and
-  // are dispatched first.
-  const int ntiles = p.num_tiles;
-  const int b = blockIdx.x;
-  const int xcd = b % 8, k = b / 8;
-  const int u = (k / ntiles) * 8 + xcd;
-  if (u >= p.num_seqs * p.num_kv_heads) return;
-  const int tile = ntiles - 1 - (k % ntiles);
-  const int s = u / p.num_kv_heads;
-  const int hk = u - s * p.num_kv_heads;
-
-  // (clamped to the rows of q, so that no value of query_start_loc leads
-  // outside q / out)
-  const int q_begin = min(max(p.query_start_loc[s], 0), p.num_tokens);
-  const int Qs = min(max(p.query_start_loc[s + 1], q_begin), p.num_tokens) - q_begin;
-  const int q0 = tile * tq;
-  if (q0 >= Qs) return;
-  const int nt = min(tq, Qs - q0);             // tokens of this tile
-  const int n = min(p.context_lens[s], p.bt_stride * 16);
-  const int pos0 = n - Qs + q0;                // position of the tile's first token
-  const int p_last = pos0 + nt - 1;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, hf = lane >> 5;
-  const int row = wave * 32 + col;             // row of this lane's query (0..127)
-  const bool row_ok = row < nt * g;
-  const int tok = min(row, nt * g - 1) / g;
-  const int head = min(row, nt * g - 1) - tok * g;
-  const int ppos = pos0 + tok;                 // query position of the row
+  const int row = wave * 32 + col;             // this lane's query row in the workgroup
+
+  // Workgroup -> (pair u, tile).  Workgroups go to the 8 XCDs round-robin;
+  // pair u runs on XCD u % 8 with all its tiles, which read the same K/V
+  // (they share it in that XCD's L2), and the XCDs get even work.  Later
+  // tiles attend to more keys (prefill) and are dispatched first.
+  //   prefill: u = (sequence, kv-head), tiles of TQ tokens;
+  //   shared prefix: u = (kv-head, split), tiles of 128 (sequence, head) rows.
+  const int ntiles = p.num_tiles;
+  const int npairs = PFX ? p.num_kv_heads * p.num_splits : p.num_seqs * p.num_kv_heads;
+  const int b = blockIdx.x;
+  const int xcd = b % 8, kk = b / 8;
+  const int u = (kk / ntiles) * 8 + xcd;
+  if (u >= npairs) return;
+  const int tile = ntiles - 1 - (kk % ntiles);
+
+  int hk, seq_tbl;                             // kv-head, sequence whose table is read
+  int key_begin, key_end;                      // keys of this workgroup, before row ranges
+  int r_lo, r_hi;                              // this row's kept keys [r_lo, r_hi)
+  bool row_ok;
+  int64_t q_off;                               // element offset of this row in q (and out)
+  int split = 0;
+  if constexpr (!PFX) {
+    const int s = u / p.num_kv_heads;
+    hk = u - s * p.num_kv_heads;
+    seq_tbl = s;
+    const int tq = kRows / g;                  // query tokens per workgroup
+    // (clamped to the rows of q, so that no value of query_start_loc leads
+    // outside q / out)
+    const int q_begin = min(max(p.query_start_loc[s], 0), p.num_tokens);
+    const int Qs = min(max(p.query_start_loc[s + 1], q_begin), p.num_tokens) - q_begin;
+    const int q0 = tile * tq;
+    if (q0 >= Qs) return;
+    const int nt = min(tq, Qs - q0);           // tokens of this tile
+    const int n = min(p.context_lens[s], p.bt_stride * 16);
+    const int pos0 = n - Qs + q0;              // position of the tile's first token
+    row_ok = row < nt * g;
+    const int tok = min(row, nt * g - 1) / g;
+    const int head = min(row, nt * g - 1) - tok * g;
+    const int ppos = pos0 + tok;               // query position of the row
+    r_hi = ppos + 1;
+    r_lo = p.window > 0 ? max(0, ppos - p.window + 1) : 0;
+    key_begin = p.window > 0 ? max(0, pos0 - p.window + 1) : 0;
+    key_end = pos0 + nt;
+    q_off = ((int64_t)(q_begin + q0 + tok) * p.num_q_heads + hk * g + head) * D;
+  } else {
+    hk = u / p.num_splits;
+    split = u - hk * p.num_splits;
+    seq_tbl = 0;                               // the shared pages, as sequence 0 maps them
+    key_begin = split * p.split_pages * 16;
+    key_end = min(p.shared_pages, (split + 1) * p.split_pages) * 16;
+    const int rows_total = p.num_seqs * g;
+    if (tile * kRows >= rows_total) return;
+    const int rg = tile * kRows + row;
+    row_ok = rg < rows_total;
+    const int rgc = min(rg, rows_total - 1);
+    const int s = rgc / g;
+    const int head = rgc - s * g;
+    const int n = min(p.context_lens[s], p.bt_stride * 16);
+    const int lo = p.window > 0 ? max(0, n - p.window) : 0;
+    r_lo = max(lo, key_begin);
+    r_hi = min(n, key_end);
+    q_off = ((int64_t)s * p.num_q_heads + hk * g + head) * D;
+  }
+
+  // Over the workgroup's rows: the largest lower and the smallest and largest
+  // upper bounds.  A block inside every row's range needs no per-key mask;
+  // keys at or past every row's range are staged as zeros.
+  if (threadIdx.x == 0) {
+    s_red[0] = INT32_MIN;
+    s_red[1] = INT32_MAX;
+    s_red[2] = INT32_MIN;
+  }
+  __syncthreads();
+  if (row_ok && hf == 0) {
+    atomicMax(&s_red[0], r_lo);
+    atomicMin(&s_red[1], r_hi);
+    atomicMax(&s_red[2], r_hi);
+  }
+  __syncthreads();
+  const int max_lo = __builtin_amdgcn_readfirstlane(s_red[0]);
+  const int min_hi = __builtin_amdgcn_readfirstlane(s_red[1]);
+  const int n_valid = min(key_end, __builtin_amdgcn_readfirstlane(s_red[2]));
+  const int kb0 = (key_begin / kBK) * kBK;
+  const int nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
 
   // Q operand: lane (row, hf) holds d = 64 hf + 8 t + i for k-step t.
   uint4 qr[8];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)(q_begin + q0 + tok) * p.num_q_heads + hk * g + head) * D + 64 * hf;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + q_off + 64 * hf;
 #pragma unroll
     for (int t = 0; t < 8; ++t) qr[t] = *reinterpret_cast<const uint4*>(qp + 8 * t);
   }
 
-  // Key blocks [kb0, kb_end) in steps of 32.
-  int lo = 0;
-  if (p.window > 0) lo = max(0, pos0 - p.window + 1);
-  const int kb0 = (lo / kBK) * kBK;
-  const int nblk = p_last >= 0 ? (p_last / kBK - kb0 / kBK + 1) : 0;
-
-  const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
+  const int32_t* bt = p.block_tables + (int64_t)seq_tbl * p.bt_stride;
   const uint8_t* kpool = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
   const uint8_t* vpool = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes;
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
 
   // Staging maps (256 threads, one block = pages A and B of 16 rows):
-  //  K: thread i loads row i / 16, 16-byte chunk i % 16 of both pages;
+  //  K: thread i loads row i / 16, chunk i % 16 of both pages;
   //  V: thread i loads rows 2 kp and 2 kp + 1 (kp = i % 16: key pair of the
   //     block, page kp / 8) at chunk i / 16, and writes the 8 dwords
   //     (V[2kp][d], V[2kp+1][d]) of V^T: 64 lanes hit 64 distinct banks.
   const int k_r = threadIdx.x / CH, k_c = threadIdx.x % CH;
   const int v_kp = threadIdx.x % 16, v_c = threadIdx.x / 16;
-  const int k_off = k_r * (D * 2) + k_c * 16;
-  const int v_off = 2 * (v_kp & 7) * (D * 2) + v_c * 16;
+  const int k_off = k_r * (D * EB) + k_c * 8 * EB;
+  const int v_off = 2 * (v_kp & 7) * (D * EB) + v_c * 8 * EB;
   const bool v_pgB = v_kp >= 8;
   auto page_blk = [&](int j) __attribute__((always_inline)) {
     int blk = 0;
-    if (j * 16 < n) blk = bt[j];
+    if (j * 16 < n_valid) blk = bt[j];
     return (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
   };
-  // Loads are unconditional (rows at or past n are replaced by zeros when
-  // written to LDS) so that nothing waits on them before the LDS write.
-  auto fetch = [&](uint4 (&kr)[2], uint4 (&vr)[2], int kb) __attribute__((always_inline)) {
+  // Loads are unconditional (rows at or past n_valid are replaced by zeros
+  // when written to LDS) so that nothing waits on them before the LDS write.
+  auto fetch = [&](RawT (&kr)[2], RawT (&vr)[2], int kb) __attribute__((always_inline)) {
     const int j0 = kb >> 4;
     const int64_t pa = (int64_t)page_blk(j0) * blk_stride, pb = (int64_t)page_blk(j0 + 1) * blk_stride;
-    kr[0] = *reinterpret_cast<const uint4*>(kpool + pa + k_off);
-    kr[1] = *reinterpret_cast<const uint4*>(kpool + pb + k_off);
+    kr[0] = *reinterpret_cast<const RawT*>(kpool + pa + k_off);
+    kr[1] = *reinterpret_cast<const RawT*>(kpool + pb + k_off);
     const uint8_t* vp = vpool + (v_pgB ? pb : pa) + v_off;
-    vr[0] = *reinterpret_cast<const uint4*>(vp);
-    vr[1] = *reinterpret_cast<const uint4*>(vp + D * 2);
+    vr[0] = *reinterpret_cast<const RawT*>(vp);
+    vr[1] = *reinterpret_cast<const RawT*>(vp + D * EB);
   };
   auto masked = [](uint4 x, bool keep) __attribute__((always_inline)) {
     const uint32_t m = keep ? 0xFFFFFFFFu : 0u;    // value-level select (no pointer select)
     return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
   };
-  auto stage = [&](int buf, const uint4 (&kr)[2], const uint4 (&vr)[2], int kb)
+  auto stage = [&](int buf, const RawT (&kr)[2], const RawT (&vr)[2], int kb)
       __attribute__((always_inline)) {
-    uint4 k0 = kr[0], k1 = kr[1], va = vr[0], vc = vr[1];
-    if (kb + kBK > n) {                            // block crossing n: zero the rows past it
-      k0 = masked(k0, kb + k_r < n);
-      k1 = masked(k1, kb + 16 + k_r < n);
-      va = masked(va, kb + 2 * v_kp < n);
-      vc = masked(vc, kb + 2 * v_kp + 1 < n);
+    uint4 k0 = to_q16<KF, QF>(kr[0]), k1 = to_q16<KF, QF>(kr[1]);
+    uint4 va = to_q16<KF, QF>(vr[0]), vc = to_q16<KF, QF>(vr[1]);
+    if (kb + kBK > n_valid) {                  // block crossing n_valid: zero the rows past it
+      k0 = masked(k0, kb + k_r < n_valid);
+      k1 = masked(k1, kb + 16 + k_r < n_valid);
+      va = masked(va, kb + 2 * v_kp < n_valid);
+      vc = masked(vc, kb + 2 * v_kp + 1 < n_valid);
     }
     *reinterpret_cast<uint4*>(&s_k[buf][k_r * KROW + k_c * 16]) = k0;
     *reinterpret_cast<uint4*>(&s_k[buf][(16 + k_r) * KROW + k_c * 16]) = k1;
     const uint32_t a[4] = {va.x, va.y, va.z, va.w};
-    const uint32_t b[4] = {vc.x, vc.y, vc.z, vc.w};
+    const uint32_t bb[4] = {vc.x, vc.y, vc.z, vc.w};
     uint32_t* vt = &s_v[buf][(v_c * 8) * VROWW + v_kp];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      vt[(2 * i) * VROWW] = __builtin_amdgcn_perm(b[i], a[i], 0x05040100u);
-      vt[(2 * i + 1) * VROWW] = __builtin_amdgcn_perm(b[i], a[i], 0x07060302u);
+      vt[(2 * i) * VROWW] = __builtin_amdgcn_perm(bb[i], a[i], 0x05040100u);
+      vt[(2 * i + 1) * VROWW] = __builtin_amdgcn_perm(bb[i], a[i], 0x07060302u);
     }
   };
 
@@ -228,16 +318,14 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
     float sc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) sc[k] = sacc[k];
-    const bool edge = (kb + kBK - 1 > pos0) || (p.window > 0 && kb <= p_last - p.window);
+    const bool edge = kb < max_lo || kb + kBK > min_hi;
     if (edge) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = kb + 8 * j + 4 * hf + i;
-          bool keep = t <= ppos;
-          if (p.window > 0) keep = keep && (t > ppos - p.window);
-          if (!keep) sc[4 * j + i] = -INFINITY;
+          if (t < r_lo || t >= r_hi) sc[4 * j + i] = -INFINITY;
         }
     }
     float mx = sc[0];
@@ -280,7 +368,7 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
 
   // Two register sets of staged loads: block bi + 2 is fetched while block bi
   // is computed and block bi + 1 is written to LDS.
-  uint4 kr0[2], vr0[2], kr1[2], vr1[2];
+  RawT kr0[2], vr0[2], kr1[2], vr1[2];
   auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
   if (nblk > 0) {
     fetch(kr0, vr0, kb_of(0));
@@ -304,12 +392,12 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
     __syncthreads();
   }
 
-  // ---- finalize: out[row][d], d = 32 m + 8 j + 4 hf + i ----
+  // ---- finalize: row values at d = 32 m + 8 j + 4 hf + i ----
   const float lt = lsum + __shfl_xor(lsum, 32);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (row_ok) {
-    uint16_t* op = static_cast<uint16_t*>(p.out) +
-                   ((int64_t)(q_begin + q0 + tok) * p.num_q_heads + hk * g + head) * D + 4 * hf;
+  if (!row_ok) return;
+  if constexpr (!PFX) {
+    uint16_t* op = static_cast<uint16_t*>(p.out) + q_off + 4 * hf;
 #pragma unroll
     for (int m = 0; m < D / 32; ++m)
 #pragma unroll
@@ -321,7 +409,31 @@ __global__ __launch_bounds__(kPW * 64) void prefill_kernel(PrefillParams p) {
                             ((uint32_t)f32_to_16<QF>(o[m][k + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(op + 32 * m + 8 * j) = make_uint2(w0, w1);
       }
+  } else {
+    // partial rows [split][sequence][query head]; an empty row stores
+    // (-inf, 0, 0), which the merge weighs 0
+    const int64_t pr = (int64_t)split * p.num_seqs * p.num_q_heads + q_off / D;
+    float* op = p.pfx_o + pr * D + 4 * hf;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * j;
+        *reinterpret_cast<float4*>(op + 32 * m + 8 * j) =
+            make_float4(o[m][k] * inv, o[m][k + 1] * inv, o[m][k + 2] * inv, o[m][k + 3] * inv);
+      }
+    if (hf == 0) {
+      p.pfx_m[pr] = lt > 0.0f ? mrow : -INFINITY;
+      p.pfx_l[pr] = lt;
+    }
   }
+}
+
+template <int QF, int KF, bool PFX>
+static hipError_t launch_tiles(const PrefillParams& x, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_tile_kernel<128, QF, KF, PFX>), dim3((unsigned)grid), dim3(kPW * 64), 0,
+                     stream, x);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipStream_t stream) {
@@ -334,11 +446,25 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipSt
   const int64_t grid = (pairs + 7) / 8 * 8 * x.num_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  if (q_fmt == kBF16)
-    hipLaunchKernelGGL((prefill_kernel<128, kBF16>), dim3((unsigned)grid), dim3(kPW * 64), 0, stream, x);
-  else
-    hipLaunchKernelGGL((prefill_kernel<128, kF16>), dim3((unsigned)grid), dim3(kPW * 64), 0, stream, x);
-  return hipGetLastError();
+  return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, false>(x, grid, stream)
+                        : launch_tiles<kF16, kF16, false>(x, grid, stream);
+}
+
+hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
+                                hipStream_t stream) {
+  if (head_dim != 128) return hipErrorNotSupported;
+  PrefillParams x = p;
+  x.num_tiles = (int)(((int64_t)p.num_seqs * p.group + kRows - 1) / kRows);
+  const int64_t pairs = (int64_t)p.num_kv_heads * p.num_splits;
+  const int64_t grid = (pairs + 7) / 8 * 8 * x.num_tiles;
+  if (grid == 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (kv_fmt == kE4M3)
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, true>(x, grid, stream)
+                          : launch_tiles<kF16, kE4M3, true>(x, grid, stream);
+  if (kv_fmt != q_fmt) return hipErrorNotSupported;
+  return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, true>(x, grid, stream)
+                        : launch_tiles<kF16, kF16, true>(x, grid, stream);
 }
 
 }  // namespace vp
