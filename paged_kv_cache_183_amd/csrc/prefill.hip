@@ -30,7 +30,7 @@
 //    the P.V operand of a lane is two 8-byte reads; the staging writes and
 //    these reads hit distinct banks.  FP8 pages are converted exactly to q's
 //    16-bit format when staged.
-// Global loads run two blocks ahead of the matrix cores.
+// Global loads run one block ahead of the matrix cores.
 // Per block and wave, on v_mfma_f32_32x32x16 (bf16 or f16, fp32 accumulate):
 //  * S^T = K Q^T: the output column of a lane is its query row, so each lane
 //    holds 16 scores of one row (keys 8j + 4h + i, h = lane / 32);
@@ -320,6 +320,7 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
     for (int k = 0; k < 16; ++k) sc[k] = sacc[k];
     const bool edge = kb < max_lo || kb + kBK > min_hi;
     if (edge) {
+      asm volatile("");                        // keep this a branch (rarely taken)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -366,29 +367,23 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
     }
   };
 
-  // Two register sets of staged loads: block bi + 2 is fetched while block bi
-  // is computed and block bi + 1 is written to LDS.
-  RawT kr0[2], vr0[2], kr1[2], vr1[2];
+  // Block bi + 1 is fetched into registers while block bi is computed, then
+  // written to the other LDS buffer.  (A single-block loop body keeps the
+  // accumulators in place; unrolling by two made the compiler copy them.)
+  RawT kr[2], vr[2];
   auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
   if (nblk > 0) {
-    fetch(kr0, vr0, kb_of(0));
-    fetch(kr1, vr1, kb_of(1));
-    stage(0, kr0, vr0, kb_of(0));
+    fetch(kr, vr, kb_of(0));
+    stage(0, kr, vr, kb_of(0));
   }
   __syncthreads();
-  for (int bi = 0; bi < nblk; bi += 2) {
-    fetch(kr0, vr0, kb_of(bi + 2));            // (past the end: re-reads the last block)
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int buf = bi & 1;
+    fetch(kr, vr, kb_of(bi + 1));              // (past the end: re-reads the last block)
     __builtin_amdgcn_sched_barrier(0);
-    block(0, kb0 + bi * kBK);
+    block(buf, kb0 + bi * kBK);
     __builtin_amdgcn_sched_barrier(0);
-    stage(1, kr1, vr1, kb_of(bi + 1));
-    __syncthreads();
-    if (bi + 1 >= nblk) break;
-    fetch(kr1, vr1, kb_of(bi + 3));
-    __builtin_amdgcn_sched_barrier(0);
-    block(1, kb0 + (bi + 1) * kBK);
-    __builtin_amdgcn_sched_barrier(0);
-    stage(0, kr0, vr0, kb_of(bi + 2));
+    stage(buf ^ 1, kr, vr, kb_of(bi + 1));
     __syncthreads();
   }
 
