@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define VLLM_PAGED_ABI_VERSION 1
+#define VLLM_PAGED_ABI_VERSION 2
 #define VLLM_PAGED_BLOCK_SIZE 16
 
 typedef enum vllm_status {
@@ -71,7 +71,9 @@ typedef enum vllm_dtype {
   VLLM_DTYPE_FP8_E4M3 = 3,    /* OCP FP8 E4M3 (bias 7, max 448, NaN 0x7F/0xFF, no infinities) */
   VLLM_DTYPE_I32 = 4,
   VLLM_DTYPE_I64 = 5,
-  VLLM_DTYPE_F32 = 6
+  VLLM_DTYPE_F32 = 6,
+  VLLM_DTYPE_FP8_E5M2 = 7     /* OCP FP8 E5M2 (bias 15, max 57344, infinities 0x7C/0xFC,
+                                 NaN S.11111.xx with xx != 0) */
 } vllm_dtype;
 
 /* A dense tensor view: `data` is a device pointer, `shape` and `stride`
@@ -105,6 +107,12 @@ typedef struct vllm_attn_opts {
                                NULL = the library allocates one stream-ordered
                                (hipMallocAsync / hipFreeAsync on hip_stream) for the call */
   size_t workspace_bytes;   /* size of `workspace`; see vllm_paged_attn_workspace_size */
+  /* appended in ABI version 2 (callers must be built against this header;
+     check vllm_abi_version() >= 2): */
+  const float* k_scales;    /* FP8 pools only: device pointer to Hkv fp32 scales, one per
+                               kv-head (K value of head h = code * k_scales[h]), read on the
+                               device, must be finite and > 0; NULL = k_scale for every head */
+  const float* v_scales;    /* the same for V; NULL = v_scale for every head */
 } vllm_attn_opts;
 
 /* The ABI version this library was built with (VLLM_PAGED_ABI_VERSION). */
@@ -120,15 +128,17 @@ const char* vllm_last_error(void);
  *   k_cache[s / 16, h, s % 16, :] = enc(k[i, h, :])   for every kv-head h,
  *   v_cache[s / 16, h, s % 16, :] = enc(v[i, h, :]).
  * Negative slots mark padding tokens and are skipped.  enc is the identity
- * (bit copy) when the pool has the input's dtype; for an FP8_E4M3 pool it is
- * the OCP E4M3 code of (x / scale) with x converted exactly to fp32, one
- * correctly-rounded fp32 division by k_scale (v_scale) from opts, saturation
- * to +-448 (infinities included), round-to-nearest-even, NaN -> 0x7F with
- * the input's sign.  Bit-exact.
+ * (bit copy) when the pool has the input's dtype; for an FP8 pool it is the
+ * OCP E4M3 (E5M2) code of (x / scale) with x converted exactly to fp32, one
+ * correctly-rounded fp32 division by the scale of the token's kv-head from
+ * opts, saturation to +-448 (+-57344; infinities included),
+ * round-to-nearest-even, NaN -> 0x7F with the input's sign.  Bit-exact.
+ * (FP8 E4M3/E5M2 KV: "Building and Deploying vllm.cpp", Step 6 table.)
  *   k, v         [T, Hkv, D]  F16 or BF16 (both the same dtype)
  *   slot_mapping [T]          I64
- *   k_cache, v_cache [num_blocks, Hkv, 16, D]  the input's dtype or FP8_E4M3
- *   opts         nullable; k_scale / v_scale used for FP8 pools only
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D]  the input's dtype, FP8_E4M3 or FP8_E5M2
+ *   opts         nullable; k_scale / v_scale (or per-head k_scales / v_scales)
+ *                used for FP8 pools only
  * Supported: D a multiple of 8, D <= 512.  T = 0 is a no-op.
  */
 vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
@@ -149,7 +159,8 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
  * used (they may hold NaN).
  *   out          [B, Hq, D]  dtype of q (written; 16-byte aligned)
  *   q            [B, Hq, D]  F16 or BF16
- *   k_cache, v_cache [num_blocks, Hkv, 16, D]  q's dtype, or FP8_E4M3
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D]  q's dtype, FP8_E4M3 or FP8_E5M2
+ *                (FP8 values: code * the scale of the kv-head, from opts)
  *   block_tables [B, max_blocks_per_seq]  I32
  *   context_lens [B]  I32
  *   scale        softmax scale applied to q.k (e.g. 1/sqrt(D))

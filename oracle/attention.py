@@ -109,8 +109,8 @@ def _decode_seq_job(s):
 
 def decode(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
            kv_fmt: str, block_tables: np.ndarray, context_lens: np.ndarray,
-           scale: float, window: int = 0, k_scale: float = 1.0,
-           v_scale: float = 1.0, seqs: Optional[list] = None, workers: int = 1,
+           scale: float, window: int = 0, k_scale=1.0,
+           v_scale=1.0, seqs: Optional[list] = None, workers: int = 1,
            return_weights: bool = False):
     """Paged decode attention.  q: raw bits [B, Hq, D]; pools: raw bits
     [num_blocks, Hkv, 16, D].  Returns float64 [len(seqs), Hq, D] (all
@@ -143,7 +143,7 @@ def decode(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
 def decode_partials(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
                     kv_fmt: str, block_tables: np.ndarray, context_lens: np.ndarray,
                     scale: float, window: int, partition: int,
-                    k_scale: float = 1.0, v_scale: float = 1.0):
+                    k_scale=1.0, v_scale=1.0):
     """Per-partition (m, l, o) of a decode: shapes [B, Hq, P], [B, Hq, P],
     [B, Hq, P, D] with P = ceil(max context / partition)."""
     B, Hq, D = q.shape
@@ -217,7 +217,7 @@ def _prefill_one(args):
 def prefill(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
             kv_fmt: str, block_tables: np.ndarray, query_start_loc: np.ndarray,
             context_lens: np.ndarray, scale: float, window: int = 0,
-            k_scale: float = 1.0, v_scale: float = 1.0,
+            k_scale=1.0, v_scale=1.0,
             rows: Optional[dict] = None, workers: int = 1) -> np.ndarray:
     """Chunked-prefill attention.  q: raw bits [sumQ, Hq, D].  Returns float64
     [sumQ, Hq, D]; with ``rows`` = {seq: [row indices within the chunk]} only

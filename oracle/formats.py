@@ -10,11 +10,21 @@
   state that fp8 pages hold one byte per element (Step 3, CLI configuration
   table, ``--kv-cache-dtype``).
 
+* E5M2: the OCP format "E5M2" of the same specification: 1 sign bit, 5
+  exponent bits with bias 15, 2 mantissa bits, IEEE-style infinities
+  (S.11111.00) and NaNs (S.11111.xx, xx != 0), largest finite magnitude
+  S.11110.11 = 57344, subnormals 2^-14 * m/4.
+
 Encoding rule (the plainest reading; the pages do not fix rounding): the
 16-bit input is converted exactly to fp32, divided by the fp32 scale with one
-correctly-rounded IEEE division, saturated to +-448 (infinities included),
-then rounded to the nearest E4M3 value with ties going to the even code; NaN
-becomes 0x7F with the input's sign; a zero result keeps the input's sign.
+correctly-rounded IEEE division, saturated to the largest finite magnitude
+(448 for E4M3, 57344 for E5M2; infinities included, so a cache never turns a
+finite input into an infinity), then rounded to the nearest representable
+value with ties going to the even code; NaN becomes 0x7F with the input's
+sign (a NaN code in both formats); a zero result keeps the input's sign.
+
+Scales: one fp32 scale per tensor, or one per kv-head (an array of Hkv
+values applied along the head axis of [.., Hkv, .., D] arrays).
 
 This file is test infrastructure (see the package docstring).
 """
@@ -23,6 +33,8 @@ from __future__ import annotations
 import numpy as np
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
+FP8_FORMATS = ("e4m3", "e5m2")
 
 
 def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -102,15 +114,88 @@ def e4m3_quantize_bits(bits: np.ndarray, fmt: str, scale: float) -> np.ndarray:
     return e4m3_encode_f32(y)
 
 
-def kv_bits_to_f64(bits: np.ndarray, fmt: str, scale: float = 1.0) -> np.ndarray:
+def e5m2_value(code: int) -> float:
+    """Value of one E5M2 code, straight from the format definition."""
+    s = -1.0 if (code >> 7) & 1 else 1.0
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    if e == 0x1F:
+        return s * float("inf") if m == 0 else float("nan")
+    if e == 0:
+        return s * (2.0 ** -14) * (m / 4.0)
+    return s * (2.0 ** (e - 15)) * (1.0 + m / 4.0)
+
+
+E5M2_TABLE = np.array([e5m2_value(c) for c in range(256)], dtype=np.float64)
+_POS_VALUES_E5M2 = E5M2_TABLE[:0x7C]        # finite non-negative magnitudes 0x00 .. 0x7B
+
+
+def e5m2_to_f64(codes: np.ndarray) -> np.ndarray:
+    """E5M2 codes -> float64 (exact)."""
+    return E5M2_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def _encode_sat_rne(y: np.ndarray, pos_values: np.ndarray, vmax: float) -> np.ndarray:
+    """float32 values -> codes of a sign-magnitude 8-bit format whose finite
+    non-negative magnitudes are ``pos_values`` (ascending, code = index):
+    saturate to +-vmax, nearest, ties to the even code, NaN -> 0x7F."""
+    y = np.asarray(y, dtype=np.float32)
+    sign = np.signbit(y).astype(np.uint8) << np.uint8(7)
+    a = np.abs(y.astype(np.float64))
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, np.minimum(a, vmax))
+    top = len(pos_values) - 1
+    hi_idx = np.minimum(np.searchsorted(pos_values, a, side="left"), top)
+    lo_idx = np.maximum(hi_idx - 1, 0)
+    lo_v, hi_v = pos_values[lo_idx], pos_values[hi_idx]
+    mid = (lo_v + hi_v) / 2.0
+    exact = hi_v == a
+    pick_hi = np.where(a > mid, True, np.where(a < mid, False, (hi_idx % 2) == 0))
+    code = np.where(exact | pick_hi, hi_idx, lo_idx).astype(np.uint8)
+    code = np.where(nan, np.uint8(0x7F), code)
+    return (code | sign).astype(np.uint8)
+
+
+def e5m2_encode_f32(y: np.ndarray) -> np.ndarray:
+    """float32 values -> E5M2 codes: saturate to +-57344, nearest, ties-to-even."""
+    return _encode_sat_rne(y, _POS_VALUES_E5M2, E5M2_MAX)
+
+
+def fp8_quantize_bits(bits: np.ndarray, src_fmt: str, fp8_fmt: str, scale: float) -> np.ndarray:
+    """16-bit input bits -> FP8 codes of (x / scale), with the rule above."""
+    x = bits16_to_f32(bits, src_fmt)
+    with np.errstate(all="ignore"):
+        y = x / np.float32(scale)        # one IEEE fp32 division
+    if fp8_fmt == "e4m3":
+        return e4m3_encode_f32(y)
+    if fp8_fmt == "e5m2":
+        return e5m2_encode_f32(y)
+    raise ValueError(fp8_fmt)
+
+
+def scale_along_heads(scale, ndim: int, head_axis: int) -> np.ndarray:
+    """A per-tensor scale (number) or per-kv-head scales ([Hkv]) shaped to
+    broadcast against an array of ``ndim`` dims whose heads lie on
+    ``head_axis``."""
+    sc = np.asarray(scale, dtype=np.float64)
+    if sc.ndim == 0:
+        return sc
+    shape = [1] * ndim
+    shape[head_axis] = sc.size
+    return sc.reshape(shape)
+
+
+def kv_bits_to_f64(bits: np.ndarray, fmt: str, scale=1.0, head_axis: int = 1) -> np.ndarray:
     """Pool bits -> float64 values.  fp8 pools are dequantized as
-    value(code) * scale in fp64; 16-bit pools ignore the scale."""
+    value(code) * scale in fp64 (scale: a number, or [Hkv] along
+    ``head_axis``); 16-bit pools ignore the scale."""
     if fmt == "f16":
         return f16_bits_to_f64(bits)
     if fmt == "bf16":
         return bf16_bits_to_f64(bits)
-    if fmt == "e4m3":
-        return e4m3_to_f64(bits) * float(scale)
+    if fmt in FP8_FORMATS:
+        vals = e4m3_to_f64(bits) if fmt == "e4m3" else e5m2_to_f64(bits)
+        return vals * scale_along_heads(scale, np.ndim(bits), head_axis)
     raise ValueError(fmt)
 
 

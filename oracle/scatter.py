@@ -9,8 +9,9 @@ and Deploying vllm.cpp", Step 3: technical mechanics of the radix cache and
 the ``--block-size 16`` launch flags); the slot convention is the plainest
 encoding of (page, row) for such a pool.
 
-16-bit pools receive the input bits unchanged; E4M3 pools receive the code
-of (x / scale) by the rule in ``oracle.formats``.
+16-bit pools receive the input bits unchanged; FP8 pools (E4M3 or E5M2)
+receive the code of (x / scale) by the rule in ``oracle.formats``, with one
+scale per tensor or one per kv-head.
 
 This file is test infrastructure (see the package docstring).
 """
@@ -18,30 +19,42 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e4m3_quantize_bits
+from .formats import FP8_FORMATS, fp8_quantize_bits
 
 BLOCK = 16
 
 _CODE_TABLES = {}
 
 
-def e4m3_code_table(src_fmt: str, scale: float) -> np.ndarray:
-    """The E4M3 code of every one of the 65,536 16-bit inputs, each computed by
-    ``formats.e4m3_quantize_bits``.  The input domain is finite, so encoding
+def fp8_code_table(src_fmt: str, fp8_fmt: str, scale: float) -> np.ndarray:
+    """The FP8 code of every one of the 65,536 16-bit inputs, each computed by
+    ``formats.fp8_quantize_bits``.  The input domain is finite, so encoding
     by lookup in this table is the same function, only memoized."""
-    key = (src_fmt, float(np.float32(scale)))
+    key = (src_fmt, fp8_fmt, float(np.float32(scale)))
     if key not in _CODE_TABLES:
         every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-        _CODE_TABLES[key] = e4m3_quantize_bits(every, src_fmt, scale)
+        _CODE_TABLES[key] = fp8_quantize_bits(every, src_fmt, fp8_fmt, scale)
     return _CODE_TABLES[key]
 
 
-def encode_rows(bits: np.ndarray, src_fmt: str, cache_fmt: str, scale: float) -> np.ndarray:
-    """What the pool stores for input rows ``bits`` (raw 16-bit patterns)."""
+def e4m3_code_table(src_fmt: str, scale: float) -> np.ndarray:
+    return fp8_code_table(src_fmt, "e4m3", scale)
+
+
+def encode_rows(bits: np.ndarray, src_fmt: str, cache_fmt: str, scale=1.0) -> np.ndarray:
+    """What the pool stores for input rows ``bits`` (raw 16-bit patterns,
+    [T, Hkv, D]); ``scale`` is a number or [Hkv] per-head scales."""
     if cache_fmt == src_fmt:
         return np.asarray(bits, dtype=np.uint16).copy()
-    if cache_fmt == "e4m3":
-        return e4m3_code_table(src_fmt, scale)[np.asarray(bits, dtype=np.uint16)]
+    if cache_fmt in FP8_FORMATS:
+        b = np.asarray(bits, dtype=np.uint16)
+        sc = np.asarray(scale, dtype=np.float64)
+        if sc.ndim == 0:
+            return fp8_code_table(src_fmt, cache_fmt, float(sc))[b]
+        out = np.empty(b.shape, dtype=np.uint8)
+        for h in range(b.shape[1]):
+            out[:, h] = fp8_code_table(src_fmt, cache_fmt, float(sc[h]))[b[:, h]]
+        return out
     raise ValueError(f"unsupported {src_fmt} -> {cache_fmt}")
 
 

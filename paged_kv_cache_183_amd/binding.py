@@ -26,7 +26,7 @@ VLLM_ERR_WORKSPACE = 4
 VLLM_ERR_HIP = 5
 
 # vllm_dtype
-DT_F16, DT_BF16, DT_FP8_E4M3, DT_I32, DT_I64, DT_F32 = 1, 2, 3, 4, 5, 6
+DT_F16, DT_BF16, DT_FP8_E4M3, DT_I32, DT_I64, DT_F32, DT_FP8_E5M2 = 1, 2, 3, 4, 5, 6, 7
 
 BLOCK_SIZE = 16
 
@@ -44,7 +44,8 @@ class VllmTensor(ctypes.Structure):
 class VllmAttnOpts(ctypes.Structure):
     _fields_ = [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("partition_size", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
 
 
 class VllmError(RuntimeError):
@@ -85,13 +86,14 @@ def _load():
 LIB = _load()
 
 _TORCH_DT = {torch.float16: DT_F16, torch.bfloat16: DT_BF16, torch.float8_e4m3fn: DT_FP8_E4M3,
-             torch.uint8: DT_FP8_E4M3, torch.int32: DT_I32, torch.int64: DT_I64,
-             torch.float32: DT_F32}
+             torch.float8_e5m2: DT_FP8_E5M2, torch.uint8: DT_FP8_E4M3, torch.int32: DT_I32,
+             torch.int64: DT_I64, torch.float32: DT_F32}
 
 
 def tensor_desc(t: Optional[torch.Tensor], dtype: Optional[int] = None) -> VllmTensor:
     """C descriptor of a torch tensor (data pointer, dtype, shape, strides).
-    uint8 tensors are taken as raw FP8-E4M3 codes."""
+    uint8 tensors are taken as raw FP8-E4M3 codes (view E5M2 pools as
+    torch.float8_e5m2)."""
     d = VllmTensor()
     if t is None:
         return d
@@ -119,10 +121,20 @@ def _check(status: int):
         raise VllmError(status, LIB.vllm_last_error().decode())
 
 
+def _scale_fields(x):
+    """A per-tensor scale (number) -> (scale, NULL); per-head scales (a
+    float32 device tensor of Hkv values) -> (0, pointer)."""
+    if isinstance(x, torch.Tensor):
+        if x.dtype != torch.float32 or not x.is_contiguous():
+            raise ValueError("per-head scales must be a contiguous float32 tensor")
+        return 0.0, x.data_ptr()
+    return float(x), None
+
+
 def _opts(k_scale=0.0, v_scale=0.0, partition_size=0, workspace=None) -> VllmAttnOpts:
     o = VllmAttnOpts()
-    o.k_scale = k_scale
-    o.v_scale = v_scale
+    o.k_scale, o.k_scales = _scale_fields(k_scale)
+    o.v_scale, o.v_scales = _scale_fields(v_scale)
     o.partition_size = partition_size
     o.flags = 0
     if workspace is not None:

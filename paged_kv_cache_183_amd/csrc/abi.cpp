@@ -47,6 +47,7 @@ const char* dtype_name(int32_t d) {
     case VLLM_DTYPE_F16: return "F16";
     case VLLM_DTYPE_BF16: return "BF16";
     case VLLM_DTYPE_FP8_E4M3: return "FP8_E4M3";
+    case VLLM_DTYPE_FP8_E5M2: return "FP8_E5M2";
     case VLLM_DTYPE_I32: return "I32";
     case VLLM_DTYPE_I64: return "I64";
     case VLLM_DTYPE_F32: return "F32";
@@ -63,7 +64,7 @@ int64_t numel(const vllm_tensor* t) {
 int elem_bytes(int32_t d) {
   switch (d) {
     case VLLM_DTYPE_F16: case VLLM_DTYPE_BF16: return 2;
-    case VLLM_DTYPE_FP8_E4M3: return 1;
+    case VLLM_DTYPE_FP8_E4M3: case VLLM_DTYPE_FP8_E5M2: return 1;
     case VLLM_DTYPE_I32: case VLLM_DTYPE_F32: return 4;
     case VLLM_DTYPE_I64: return 8;
     default: return 0;
@@ -134,8 +135,26 @@ int fmt_of(int32_t d) {
     case VLLM_DTYPE_F16: return vp::kF16;
     case VLLM_DTYPE_BF16: return vp::kBF16;
     case VLLM_DTYPE_FP8_E4M3: return vp::kE4M3;
+    case VLLM_DTYPE_FP8_E5M2: return vp::kE5M2;
     default: return -1;
   }
+}
+
+bool is_fp8_dtype(int32_t d) { return d == VLLM_DTYPE_FP8_E4M3 || d == VLLM_DTYPE_FP8_E5M2; }
+
+// Per-kv-head scale arrays: device memory, 4-byte aligned (their Hkv values
+// are read on the device).
+vllm_status check_scales(const vllm_attn_opts* opts) {
+  if (!opts) return VLLM_OK;
+  if (opts->k_scales) {
+    VP_TRY(check_align(opts->k_scales, "k_scales", 4));
+    VP_TRY(check_device_ptr(opts->k_scales, "k_scales"));
+  }
+  if (opts->v_scales) {
+    VP_TRY(check_align(opts->v_scales, "v_scales", 4));
+    VP_TRY(check_device_ptr(opts->v_scales, "v_scales"));
+  }
+  return VLLM_OK;
 }
 
 vllm_status scale_of(float s, const char* name, float* out) {
@@ -258,7 +277,7 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
     return fail(VLLM_ERR_UNSUPPORTED, "k: dtype %s, expected F16 or BF16", dtype_name(k->dtype));
   VP_TRY(check_dtype(v, "v", k->dtype));
   VP_TRY(check_dtype(slot_mapping, "slot_mapping", VLLM_DTYPE_I64));
-  if (k_cache->dtype != k->dtype && k_cache->dtype != VLLM_DTYPE_FP8_E4M3)
+  if (k_cache->dtype != k->dtype && !is_fp8_dtype(k_cache->dtype))
     return fail(VLLM_ERR_UNSUPPORTED, "k_cache: dtype %s with %s input", dtype_name(k_cache->dtype),
                 dtype_name(k->dtype));
   VP_TRY(check_dtype(v_cache, "v_cache", k_cache->dtype));
@@ -266,13 +285,14 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
     return fail(VLLM_ERR_UNSUPPORTED, "head_dim %lld: must be a positive multiple of 8, <= 512", (long long)D);
   if ((double)T * (double)Hkv * (double)(D / 8) >= 4294967295.0)
     return fail(VLLM_ERR_UNSUPPORTED, "too many tokens for one call");
-  const bool to_fp8 = k_cache->dtype == VLLM_DTYPE_FP8_E4M3;
+  const bool to_fp8 = is_fp8_dtype(k_cache->dtype);
   float ks = 1.0f, vs = 1.0f;
   if (to_fp8) {
     VP_TRY(scale_of(opts ? opts->k_scale : 0.0f, "k_scale", &ks));
     VP_TRY(scale_of(opts ? opts->v_scale : 0.0f, "v_scale", &vs));
   }
   if (T == 0 || Hkv == 0) return ok();
+  if (to_fp8) VP_TRY(check_scales(opts));
   VP_TRY(check_data(k, "k", 16));
   VP_TRY(check_data(v, "v", 16));
   VP_TRY(check_data(slot_mapping, "slot_mapping", 8));
@@ -294,7 +314,10 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
   p.head_dim = (int32_t)D;
   p.k_scale = ks;
   p.v_scale = vs;
-  VP_TRY(hip_status(vp::launch_cache_write(p, fmt_of(k->dtype), to_fp8, (hipStream_t)hip_stream),
+  p.k_scales = (to_fp8 && opts) ? opts->k_scales : nullptr;
+  p.v_scales = (to_fp8 && opts) ? opts->v_scales : nullptr;
+  VP_TRY(hip_status(vp::launch_cache_write(p, fmt_of(k->dtype), fmt_of(k_cache->dtype),
+                                           (hipStream_t)hip_stream),
                     "cache_write launch"));
   return ok();
 }
@@ -370,7 +393,7 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   if (q->dtype != VLLM_DTYPE_F16 && q->dtype != VLLM_DTYPE_BF16)
     return fail(VLLM_ERR_UNSUPPORTED, "q: dtype %s, expected F16 or BF16", dtype_name(q->dtype));
   VP_TRY(check_dtype(out, "out", q->dtype));
-  if (k_cache->dtype != q->dtype && k_cache->dtype != VLLM_DTYPE_FP8_E4M3)
+  if (k_cache->dtype != q->dtype && !is_fp8_dtype(k_cache->dtype))
     return fail(VLLM_ERR_UNSUPPORTED, "k_cache: dtype %s with %s queries", dtype_name(k_cache->dtype),
                 dtype_name(q->dtype));
   VP_TRY(check_dtype(v_cache, "v_cache", k_cache->dtype));
@@ -380,7 +403,7 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
     return fail(VLLM_ERR_UNSUPPORTED, "head_dim %lld: supported 64, 128", (long long)D);
   if (NB > INT32_MAX || block_tables->shape[1] > INT32_MAX / 16 || B > 65535 || Hq > 65535)
     return fail(VLLM_ERR_UNSUPPORTED, "sizes beyond the supported range");
-  const bool fp8 = k_cache->dtype == VLLM_DTYPE_FP8_E4M3;
+  const bool fp8 = is_fp8_dtype(k_cache->dtype);
   float ks = 1.0f, vs = 1.0f;
   if (fp8) {
     VP_TRY(scale_of(opts ? opts->k_scale : 0.0f, "k_scale", &ks));
@@ -407,6 +430,7 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   VP_TRY(check_data(v_cache, "v_cache", fp8 ? 8 : 16));
   VP_TRY(check_data(block_tables, "block_tables", 4));
   VP_TRY(check_data(context_lens, "context_lens", 4));
+  if (fp8) VP_TRY(check_scales(opts));
 
   hipStream_t stream = (hipStream_t)hip_stream;
   const int kv_fmt = fmt_of(k_cache->dtype), q_fmt = fmt_of(q->dtype);
@@ -435,8 +459,11 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   p.num_workers = std::max<int32_t>(vp::kDecodeWaves,
                                     (p.num_workers + vp::kDecodeWaves - 1) / vp::kDecodeWaves *
                                         vp::kDecodeWaves);
-  p.score_scale = scale * 1.4426950408889634f * ks;
+  p.score_base = scale * 1.4426950408889634f;
+  p.score_scale = p.score_base * ks;
   p.out_scale = vs;
+  p.k_scales = (fp8 && opts) ? opts->k_scales : nullptr;
+  p.v_scales = (fp8 && opts) ? opts->v_scales : nullptr;
 
   void* ws = nullptr;
   bool owned = false;
@@ -471,6 +498,8 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
     sp.num_blocks = (int32_t)NB;
     sp.window = window;
     sp.score_scale = p.score_scale;
+    sp.score_base = p.score_base;
+    sp.k_scales = p.k_scales;
     sp.shared_pages = shared_pages;
     sp.split_pages = vp::kPrefixSplitPages;
     sp.num_splits = dp.num_splits;

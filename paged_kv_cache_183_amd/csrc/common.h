@@ -84,6 +84,51 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
   return sign | code;                                // never reaches 0x7F below 448
 }
 
+// Encoder written from the OCP specification for E5M2 (bias 15, 2 mantissa
+// bits, max finite 57344, infinities S.11111.00, NaN S.11111.xx) with the
+// same rule: saturate to +-57344 (infinities included), round to nearest with
+// ties to the even code, NaN -> 0x7F | sign, zero keeps its sign.
+__device__ __forceinline__ uint32_t e5m2_from_f32(float y) {
+  const uint32_t u = bitcast<uint32_t>(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+  if (a >= 0x47600000u) return sign | 0x7Bu;         // >= 57344 (and inf): saturate
+  if (a < 0x38800000u) {                             // below 2^-14: spacing 2^-16
+    // |y| * 2^16 is exact; round it to the nearest even integer (0..4).
+    float r = __builtin_rintf(bitcast<float>(a) * 65536.0f);
+    return sign | (uint32_t)r;                       // 4 is the code of 2^-14
+  }
+  const uint32_t e = (a >> 23) - 127u + 15u;         // 1 .. 30
+  const uint32_t mant = a & 0x7FFFFFu;
+  const uint32_t keep = mant >> 21;                  // top 2 mantissa bits
+  const uint32_t rest = mant & 0x1FFFFFu;            // 21 dropped bits
+  uint32_t code = (e << 2) | keep;
+  code += (rest > 0x100000u) || (rest == 0x100000u && (keep & 1u));
+  return sign | code;                                // never passes 0x7B below 57344
+}
+
+template <int KF>
+__device__ __forceinline__ uint32_t fp8_from_f32(float y) {
+  static_assert(KF == kE4M3 || KF == kE5M2, "FP8 format");
+  if constexpr (KF == kE4M3) return e4m3_from_f32(y);
+  else return e5m2_from_f32(y);
+}
+
+// Two 8-bit codes (bytes 2 HI and 2 HI + 1 of w) -> two values of q's 16-bit
+// format, exactly (gfx950 conversions; both FP8 formats embed in fp16 and bf16).
+template <int KF, int QF, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_q16(uint32_t w) {
+  if constexpr (KF == kE4M3 && QF == kF16)
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  else if constexpr (KF == kE4M3)
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else if constexpr (QF == kF16)
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI));
+  else
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+}
+
 // ---- cross-lane sums within 16-lane rows (DPP) ---------------------------------
 
 template <int CTRL>

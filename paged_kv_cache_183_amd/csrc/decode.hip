@@ -55,6 +55,7 @@ constexpr int kScanMax = 2048;     // sequences whose page prefix fits in LDS
 
 template <int KF> struct KvChunk { using T = uint4; };      // 8 x 16-bit
 template <> struct KvChunk<kE4M3> { using T = uint2; };     // 8 x fp8
+template <> struct KvChunk<kE5M2> { using T = uint2; };
 
 // Streaming (non-temporal) loads: every KV byte is read once per call.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -75,18 +76,13 @@ __device__ __forceinline__ uint2 ld_stream<uint2>(const uint8_t* ptr) {
 // 8 K elements -> 4 packed pairs in q's format.
 template <int KF, int QF>
 __device__ __forceinline__ void k_pairs(const typename KvChunk<KF>::T& x, uint32_t (&w)[4]) {
-  if constexpr (KF != kE4M3) {
+  if constexpr (!is_fp8(KF)) {
     w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-  } else if constexpr (QF == kF16) {
-    w[0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, false));
-    w[1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, true));
-    w[2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, false));
-    w[3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, true));
   } else {
-    w[0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false));
-    w[1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true));
-    w[2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false));
-    w[3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true));
+    w[0] = fp8x2_to_q16<KF, QF, false>(x.x);
+    w[1] = fp8x2_to_q16<KF, QF, true>(x.x);
+    w[2] = fp8x2_to_q16<KF, QF, false>(x.y);
+    w[3] = fp8x2_to_q16<KF, QF, true>(x.y);
   }
 }
 
@@ -116,7 +112,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 template <int KF, int QF>
 __device__ __forceinline__ void v_pairs(const typename KvChunk<KF>::T& a,
                                         const typename KvChunk<KF>::T& b, uint32_t (&o)[8]) {
-  if constexpr (KF != kE4M3) {
+  if constexpr (!is_fp8(KF)) {
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
     const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -133,17 +129,10 @@ __device__ __forceinline__ void v_pairs(const typename KvChunk<KF>::T& a,
       // each byte pair exactly to two 16-bit values.
       const uint32_t w01 = __builtin_amdgcn_perm(bw[i], aw[i], 0x05010400u);
       const uint32_t w23 = __builtin_amdgcn_perm(bw[i], aw[i], 0x07030602u);
-      if constexpr (QF == kF16) {
-        o[4 * i + 0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, false));
-        o[4 * i + 1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w01, 1.0f, true));
-        o[4 * i + 2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, false));
-        o[4 * i + 3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w23, 1.0f, true));
-      } else {
-        o[4 * i + 0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w01, 1.0f, false));
-        o[4 * i + 1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w01, 1.0f, true));
-        o[4 * i + 2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w23, 1.0f, false));
-        o[4 * i + 3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w23, 1.0f, true));
-      }
+      o[4 * i + 0] = fp8x2_to_q16<KF, QF, false>(w01);
+      o[4 * i + 1] = fp8x2_to_q16<KF, QF, true>(w01);
+      o[4 * i + 2] = fp8x2_to_q16<KF, QF, false>(w23);
+      o[4 * i + 3] = fp8x2_to_q16<KF, QF, true>(w23);
     }
   }
 }
@@ -321,6 +310,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
       const bool complete = whole && p.skip_tokens == 0;
       const int hk = y / ngc;
       const int h0 = hk * p.group + (y - hk * ngc) * G;
+      // FP8 scales of this kv-head (per-head arrays, else the per-tensor ones)
+      const float sscale = p.k_scales ? p.score_base * p.k_scales[hk] : p.score_scale;
+      const float oscale = p.v_scales ? p.v_scales[hk] : p.out_scale;
 
       // ---- one segment: pages [i0, i1) of unit (s, y) ----
       uint4 qv[G][CPL];
@@ -429,7 +421,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
 #pragma unroll
             for (int rg = 0; rg < TPL; ++rg)
 #pragma unroll
-              for (int h = 0; h < G; ++h) sc[rg][h] = group_sum<LPR>(sc[rg][h]) * p.score_scale;
+              for (int h = 0; h < G; ++h) sc[rg][h] = group_sum<LPR>(sc[rg][h]) * sscale;
             if (!full) {
 #pragma unroll
               for (int rg = 0; rg < TPL; ++rg) {
@@ -539,7 +531,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
         if (rv == 0) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float inv = p.out_scale / l[h];
+            const float inv = oscale / l[h];
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -702,7 +694,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     merge_rounds<D, G, 64>(p, u, sl0, nsuf, npieces, prow, e, s_m, s_l, M, den, acc);
   if (e_raw < G * D) {
     uint16_t* out = static_cast<uint16_t*>(p.out) + prow * D;
-    out[e] = f32_to_16<QF>(den > 0.0f ? acc / den * p.out_scale : 0.0f);
+    const float oscale = p.v_scales ? p.v_scales[hk] : p.out_scale;
+    out[e] = f32_to_16<QF>(den > 0.0f ? acc / den * oscale : 0.0f);
   }
 }
 
@@ -746,11 +739,15 @@ static const void* decode_kernel_for(int D, int kv_fmt, int q_fmt, int gc) {
     if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<128, kBF16, kBF16>(gc);
     if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<128, kE4M3, kF16>(gc);
     if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<128, kE4M3, kBF16>(gc);
+    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<128, kE5M2, kF16>(gc);
+    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<128, kE5M2, kBF16>(gc);
   } else if (D == 64) {
     if (kv_fmt == kF16 && q_fmt == kF16) return pick<64, kF16, kF16>(gc);
     if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<64, kBF16, kBF16>(gc);
     if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<64, kE4M3, kF16>(gc);
     if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<64, kE4M3, kBF16>(gc);
+    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<64, kE5M2, kF16>(gc);
+    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<64, kE5M2, kBF16>(gc);
   }
   return nullptr;
 }
@@ -789,10 +786,10 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
     cus = v;
   }
   // workgroups resident per CU, queried once per kernel variant
-  static constexpr int kVariants = 2 * 3 * 2 * 8;
+  static constexpr int kVariants = 2 * 4 * 2 * 8;
   static int occ_cache[kVariants] = {0};
   int per_cu = 4;
-  const int vi = ((head_dim == 128) * 3 + kv_fmt) * 16 + q_fmt * 8 + (head_chunk - 1);
+  const int vi = ((head_dim == 128) * 4 + kv_fmt) * 16 + q_fmt * 8 + (head_chunk - 1);
   if (vi >= 0 && vi < kVariants && occ_cache[vi] > 0) {
     per_cu = occ_cache[vi];
   } else if (const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, head_chunk)) {

@@ -8,7 +8,9 @@
 namespace vp {
 
 // Storage formats handled by the kernels.
-enum Fmt : int { kF16 = 0, kBF16 = 1, kE4M3 = 2 };
+enum Fmt : int { kF16 = 0, kBF16 = 1, kE4M3 = 2, kE5M2 = 3 };
+
+constexpr bool is_fp8(int f) { return f == kE4M3 || f == kE5M2; }
 
 struct CacheWriteParams {
   const void* k;               // [T, Hkv, D] 16-bit
@@ -23,11 +25,14 @@ struct CacheWriteParams {
   uint32_t items_per_head;     // D / 8
   int32_t num_kv_heads;
   int32_t head_dim;
-  float k_scale;               // FP8 pools: stored code = e4m3(x / k_scale)
+  float k_scale;               // FP8 pools: stored code = fp8(x / k_scale)
   float v_scale;
+  const float* k_scales;       // FP8 pools: [Hkv] per-head scales, or null for k_scale
+  const float* v_scales;
 };
 
-hipError_t launch_cache_write(const CacheWriteParams& p, int src_fmt, bool to_fp8,
+// dst_fmt: src_fmt (bit copy), kE4M3 or kE5M2.
+hipError_t launch_cache_write(const CacheWriteParams& p, int src_fmt, int dst_fmt,
                               hipStream_t stream);
 
 struct DecodeParams {
@@ -56,6 +61,9 @@ struct DecodeParams {
   int32_t max_chunks;          // capacity of the partial arrays (chunks)
   float score_scale;           // scale * log2(e) * k_scale
   float out_scale;             // v_scale (1 for 16-bit pools)
+  float score_base;            // scale * log2(e)
+  const float* k_scales;       // FP8 pools: [Hkv] per-head scales (null: k_scale)
+  const float* v_scales;       // FP8 pools: [Hkv] per-head scales (null: v_scale)
   // Shared prefix (0 = none): keys below skip_tokens are left to the
   // shared-prefix pass; every unit then goes through the merge, which also
   // takes the num_splits prefix partials of each row.
@@ -69,7 +77,7 @@ struct DecodeParams {
   const float* pfx_l;
 };
 
-// kv_fmt: kF16 / kBF16 / kE4M3; q_fmt: kF16 / kBF16.
+// kv_fmt: kF16 / kBF16 / kE4M3 / kE5M2; q_fmt: kF16 / kBF16.
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt,
                          hipStream_t stream);
 
@@ -92,6 +100,8 @@ struct PrefillParams {
   int32_t window;
   int32_t num_tiles;           // row tiles (set by the launchers)
   float score_scale;           // scale * log2(e) (* k_scale for FP8 pools)
+  float score_base;            // scale * log2(e)
+  const float* k_scales;       // FP8 pools: [Hkv] per-head K scales (null: folded in score_scale)
   // shared-prefix partials (launch_shared_prefix only): the first
   // shared_pages pages of every sequence, in splits of split_pages pages
   int32_t shared_pages;
@@ -104,7 +114,7 @@ struct PrefillParams {
 
 // Chunked prefill: q_fmt = pool format (kF16 / kBF16).
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipStream_t stream);
-// Shared-prefix partials: kv_fmt = q_fmt or kE4M3.
+// Shared-prefix partials: kv_fmt = q_fmt, kE4M3 or kE5M2.
 hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
                                 hipStream_t stream);
 // Pages per split of the shared-prefix pass.

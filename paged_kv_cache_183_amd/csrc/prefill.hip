@@ -28,8 +28,8 @@
 //  * K block row-major ([key][D], rows padded by 16 bytes);
 //  * V block transposed ([D][key pair], rows padded to 18 dwords), so that
 //    the P.V operand of a lane is two 8-byte reads; the staging writes and
-//    these reads hit distinct banks.  FP8 pages are converted exactly to q's
-//    16-bit format when staged.
+//    these reads hit distinct banks.  FP8 pages (E4M3 or E5M2) are converted
+//    exactly to q's 16-bit format when staged.
 // Global loads run one block ahead of the matrix cores.
 // Per block and wave, on v_mfma_f32_32x32x16 (bf16 or f16, fp32 accumulate):
 //  * S^T = K Q^T: the output column of a lane is its query row, so each lane
@@ -97,22 +97,16 @@ __device__ __forceinline__ float half_max(float x) {
 // Raw pool data of one 8-element chunk: 16 bytes for 16-bit pools, 8 for FP8.
 template <int KF> struct Raw { using T = uint4; };
 template <> struct Raw<kE4M3> { using T = uint2; };
+template <> struct Raw<kE5M2> { using T = uint2; };
 
 // The chunk as 8 values of q's 16-bit format (FP8 codes converted exactly).
 template <int KF, int QF>
 __device__ __forceinline__ uint4 to_q16(const typename Raw<KF>::T& x) {
-  if constexpr (KF != kE4M3) {
+  if constexpr (!is_fp8(KF)) {
     return x;
-  } else if constexpr (QF == kF16) {
-    return make_uint4(bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, false)),
-                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, true)),
-                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, false)),
-                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, true)));
   } else {
-    return make_uint4(bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false)),
-                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true)),
-                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false)),
-                      bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true)));
+    return make_uint4(fp8x2_to_q16<KF, QF, false>(x.x), fp8x2_to_q16<KF, QF, true>(x.x),
+                      fp8x2_to_q16<KF, QF, false>(x.y), fp8x2_to_q16<KF, QF, true>(x.y));
   }
 }
 
@@ -124,7 +118,7 @@ template <int D, int QF, int KF, bool PFX>
 __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   static_assert(D == 128, "head_dim 128");
   constexpr int CH = D / 8;                    // 8-element chunks per K/V row
-  constexpr int EB = KF == kE4M3 ? 1 : 2;      // bytes per pool element
+  constexpr int EB = is_fp8(KF) ? 1 : 2;       // bytes per pool element
   constexpr int KROW = D * 2 + 16;             // bytes per LDS K row
   constexpr int VROWW = kBK / 2 + 2;           // dwords per LDS V^T row (18)
   constexpr int KBUF = kBK * KROW;             // bytes per K buffer
@@ -296,7 +290,8 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) o[m] = f32x16_t{};
   float mrow = -INFINITY, lsum = 0.0f;
-  const float c = p.score_scale;
+  // scale * log2(e), times the K scale of this kv-head for FP8 pools
+  const float c = p.k_scales ? p.score_base * p.k_scales[hk] : p.score_scale;
 
   // One block: S^T, online softmax, O^T update.  buf holds the block's K and
   // V^T.  Lane reads: K rows col (16 bytes at d = 64 hf + 8 t), V^T rows
@@ -457,6 +452,9 @@ hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt
   if (kv_fmt == kE4M3)
     return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, true>(x, grid, stream)
                           : launch_tiles<kF16, kE4M3, true>(x, grid, stream);
+  if (kv_fmt == kE5M2)
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE5M2, true>(x, grid, stream)
+                          : launch_tiles<kF16, kE5M2, true>(x, grid, stream);
   if (kv_fmt != q_fmt) return hipErrorNotSupported;
   return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, true>(x, grid, stream)
                         : launch_tiles<kF16, kF16, true>(x, grid, stream);

@@ -9,10 +9,21 @@ DEV = "cuda"
 
 
 def pool_view(pool_bits: torch.Tensor, kv_dtype: str) -> torch.Tensor:
-    """Typed view of a raw-bits pool (int16 -> f16/bf16; uint8 stays FP8 codes)."""
+    """Typed view of a raw-bits pool (int16 -> f16/bf16; uint8 stays E4M3
+    codes; E5M2 codes are viewed as torch.float8_e5m2)."""
     if kv_dtype == "e4m3":
         return pool_bits
+    if kv_dtype == "e5m2":
+        return pool_bits.view(torch.float8_e5m2)
     return pool_bits.view(STORAGE_TORCH[kv_dtype])
+
+
+def dev_scale(x, dev=DEV):
+    """A per-tensor scale stays a number; per-head scales become a float32
+    device tensor."""
+    if isinstance(x, (tuple, list)):
+        return torch.tensor(x, dtype=torch.float32, device=dev)
+    return x
 
 
 def gpu_fill(case, dev=DEV):
@@ -21,7 +32,7 @@ def gpu_fill(case, dev=DEV):
     vc = case.sentinel_pool().to(dev)
     P.vllm_paged_cache_write(case.fill_k.to(dev), case.fill_v.to(dev), case.fill_slots.to(dev),
                              pool_view(kc, case.kv_dtype), pool_view(vc, case.kv_dtype),
-                             k_scale=case.k_scale, v_scale=case.v_scale)
+                             k_scale=dev_scale(case.k_scale), v_scale=dev_scale(case.v_scale))
     return kc, vc
 
 
@@ -33,7 +44,7 @@ def gpu_decode(case, kc, vc, partition=0, workspace=None, q=None, bt=None, ctx=N
     ctx = (case.context_lens if ctx is None else ctx).to(dev)
     P.vllm_paged_attn_decode(out, q, pool_view(kc, case.kv_dtype), pool_view(vc, case.kv_dtype),
                              bt, ctx, case.scale, case.window if window is None else window,
-                             k_scale=case.k_scale, v_scale=case.v_scale,
+                             k_scale=dev_scale(case.k_scale), v_scale=dev_scale(case.v_scale),
                              partition_size=partition, workspace=workspace)
     return out
 
@@ -59,11 +70,11 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.uint8).numpy()
 
 
-TOL = {"f16": 2e-3, "bf16": 8e-3, "e4m3": 3e-2}
+TOL = {"f16": 2e-3, "bf16": 8e-3, "e4m3": 3e-2, "e5m2": 3e-2}
 
 
 def tol_for(case) -> float:
-    return TOL["e4m3"] if case.kv_dtype == "e4m3" else TOL[case.q_dtype]
+    return TOL[case.kv_dtype] if case.kv_dtype in ("e4m3", "e5m2") else TOL[case.q_dtype]
 
 
 # Explicit mantissa bits of the 16-bit output formats.

@@ -23,10 +23,11 @@ def contiguous_kv(case, s, kp=None, vp=None):
     quantized by the oracle's codec first."""
     rows = case.seq_rows[s].numpy()
     kb, vb = raw_bits(case.fill_k)[rows], raw_bits(case.fill_v)[rows]
-    if case.kv_dtype == "e4m3":
-        kq = scatter.encode_rows(kb, case.kv_src_dtype, "e4m3", case.k_scale)
-        vq = scatter.encode_rows(vb, case.kv_src_dtype, "e4m3", case.v_scale)
-        return kv_bits_to_f64(kq, "e4m3", case.k_scale), kv_bits_to_f64(vq, "e4m3", case.v_scale)
+    if case.kv_dtype in ("e4m3", "e5m2"):
+        kq = scatter.encode_rows(kb, case.kv_src_dtype, case.kv_dtype, case.k_scale)
+        vq = scatter.encode_rows(vb, case.kv_src_dtype, case.kv_dtype, case.v_scale)
+        return (kv_bits_to_f64(kq, case.kv_dtype, case.k_scale),
+                kv_bits_to_f64(vq, case.kv_dtype, case.v_scale))
     return kv_bits_to_f64(kb, case.kv_dtype), kv_bits_to_f64(vb, case.kv_dtype)
 
 

@@ -13,7 +13,7 @@ from oracle import attention as A
 from workloads import make_case, raw_bits
 
 from _util import oracle_pools
-from _gpu import gpu_fill, gpu_decode, to_f64, pool_view, assert_close, DEV
+from _gpu import gpu_fill, gpu_decode, to_f64, pool_view, assert_close, dev_scale, DEV
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,8 @@ def shared_decode(case, kc, vc, shared_pages, bt=None, ctx=None, window=None, pa
         out, q, pool_view(kc, case.kv_dtype), pool_view(vc, case.kv_dtype),
         (case.block_tables if bt is None else bt).to(DEV),
         (case.context_lens if ctx is None else ctx).to(DEV), shared_pages, case.scale,
-        case.window if window is None else window, k_scale=case.k_scale, v_scale=case.v_scale,
+        case.window if window is None else window, k_scale=dev_scale(case.k_scale),
+        v_scale=dev_scale(case.v_scale),
         partition_size=partition, workspace=workspace)
     return out
 

@@ -306,3 +306,24 @@ def test_prefill_causal_perturbation():
         i = p - (n - Q)
         assert np.array_equal(out[:i + 1], base[:i + 1])
         assert not np.array_equal(out[i + 1:], base[i + 1:])
+
+
+def test_per_head_scales_map_to_kv_heads():
+    """Decode with per-kv-head FP8 scales: the query heads of kv-head h equal
+    a per-tensor decode with scale[h] (pins the head axis of the scales)."""
+    import numpy as np
+    from workloads import make_case, raw_bits
+    from oracle import attention as A
+    from oracle import scatter as S
+    case = make_case(1, B=3, ctx_range=(5, 60), Hq=6, Hkv=3, kv="e5m2", q="f16", kv_src="f16")
+    pool0 = raw_bits(case.sentinel_pool())
+    slots = case.fill_slots.numpy()
+    kp = S.cache_write_fast(pool0, raw_bits(case.fill_k), slots, "f16", "e5m2", 0.1)
+    vp = S.cache_write_fast(pool0, raw_bits(case.fill_v), slots, "f16", "e5m2", 0.1)
+    ks, vs = np.array([0.5, 0.1, 2.0]), np.array([0.2, 1.5, 0.05])
+    args = (raw_bits(case.q), "f16", kp, vp, "e5m2", case.block_tables.numpy(),
+            case.context_lens.numpy(), case.scale, 0)
+    got = A.decode(*args, ks, vs)
+    for h in range(3):
+        ref = A.decode(*args, float(ks[h]), float(vs[h]))
+        assert np.array_equal(got[:, 2 * h:2 * h + 2], ref[:, 2 * h:2 * h + 2]), h

@@ -97,3 +97,20 @@ def test_fp8_code_table_equals_direct_encoder():
             from oracle.formats import e4m3_quantize_bits
             assert np.array_equal(scatter.encode_rows(bits, fmt, "e4m3", scale),
                                   e4m3_quantize_bits(bits, fmt, scale))
+
+
+def test_per_head_scales_pick_the_head():
+    """With one scale per kv-head, head h of the pool equals a per-tensor
+    write with scale[h] (for both FP8 formats)."""
+    import numpy as np
+    from workloads import make_case, raw_bits
+    from oracle import scatter as S
+    case = make_case(1, B=2, ctx_range=(20, 40), Hq=6, Hkv=3, kv="e4m3", q="f16", kv_src="f16")
+    pool0 = raw_bits(case.sentinel_pool())
+    fk, slots = raw_bits(case.fill_k), case.fill_slots.numpy()
+    scales = (0.05, 0.7, 3.0)
+    for fmt in ("e4m3", "e5m2"):
+        got = S.cache_write_fast(pool0, fk, slots, "f16", fmt, scales)
+        for h, sc in enumerate(scales):
+            ref = S.cache_write(pool0, fk, slots, "f16", fmt, sc)
+            assert np.array_equal(got[:, h], ref[:, h]), (fmt, h)

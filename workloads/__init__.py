@@ -34,9 +34,10 @@ import torch
 BLOCK_SIZE = 16
 
 # Raw NaN bit patterns used to poison unwritten pool slots.
-SENTINEL_BITS = {"f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F}
+SENTINEL_BITS = {"f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F, "e5m2": 0x7F}
 STORAGE_TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
-ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1}
+FP8 = ("e4m3", "e5m2")
 
 # The five synthetic workloads.  Decode configs draw one query token per
 # sequence; the prefill config draws query chunks over cached contexts.
@@ -67,7 +68,7 @@ class Case:
     kind: str                      # "decode" or "prefill"
     q: torch.Tensor                # decode [B, Hq, D]; prefill [sumQ, Hq, D]
     q_dtype: str                   # "f16" | "bf16"
-    kv_dtype: str                  # "f16" | "bf16" | "e4m3"
+    kv_dtype: str                  # "f16" | "bf16" | "e4m3" | "e5m2"
     kv_src_dtype: str              # dtype of fill_k / fill_v ("f16" | "bf16")
     num_blocks: int
     num_kv_heads: int
@@ -79,8 +80,8 @@ class Case:
     context_lens: torch.Tensor     # [B] int32 (includes the query tokens)
     scale: float
     window: int
-    k_scale: float = 1.0
-    v_scale: float = 1.0
+    k_scale: object = 1.0          # FP8: a number, or a tuple of Hkv per-head scales
+    v_scale: object = 1.0
     query_start_loc: Optional[torch.Tensor] = None   # prefill [B+1] int32
     max_query_len: int = 1
     partition: int = 0
@@ -104,9 +105,16 @@ class Case:
         (int16 for 16-bit formats, uint8 for fp8)."""
         shape = (self.num_blocks, self.num_kv_heads, BLOCK_SIZE, self.head_dim)
         bits = SENTINEL_BITS[self.kv_dtype]
-        if self.kv_dtype == "e4m3":
+        if self.kv_dtype in FP8:
             return torch.full(shape, bits, dtype=torch.uint8)
         return torch.full(shape, bits, dtype=torch.int16)
+
+
+def _scale(x):
+    """A per-tensor FP8 scale (number) or per-kv-head scales (a sequence)."""
+    if isinstance(x, (list, tuple)):
+        return tuple(float(v) for v in x)
+    return float(x)
 
 
 def _uniform_int(gen: torch.Generator, lo: int, hi: int, n: int) -> torch.Tensor:
@@ -181,8 +189,8 @@ def _make_decode(cfg, gen) -> Case:
                 fill_slots=torch.cat(slots), block_tables=bt,
                 context_lens=ctx.to(torch.int32), scale=float(cfg["scale"]),
                 window=int(cfg.get("window", 0)),
-                k_scale=float(cfg.get("k_scale", 1.0)),
-                v_scale=float(cfg.get("v_scale", 1.0)),
+                k_scale=_scale(cfg.get("k_scale", 1.0)),
+                v_scale=_scale(cfg.get("v_scale", 1.0)),
                 partition=int(cfg.get("partition", 0)),
                 step_rows=torch.tensor(step_rows, dtype=torch.int64),
                 seq_rows=seq_rows)
@@ -229,8 +237,8 @@ def _make_shared(cfg, gen) -> Case:
                 fill_slots=torch.cat(slots), block_tables=bt,
                 context_lens=ctx.to(torch.int32), scale=float(cfg["scale"]),
                 window=int(cfg.get("window", 0)),
-                k_scale=float(cfg.get("k_scale", 1.0)),
-                v_scale=float(cfg.get("v_scale", 1.0)),
+                k_scale=_scale(cfg.get("k_scale", 1.0)),
+                v_scale=_scale(cfg.get("v_scale", 1.0)),
                 partition=int(cfg.get("partition", 0)),
                 step_rows=torch.tensor(step_rows, dtype=torch.int64),
                 seq_rows=seq_rows)
