@@ -242,5 +242,108 @@ def prefill(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
     return np.concatenate(res, axis=0) if res else np.zeros(q.shape, np.float64)
 
 
+# ---- chunked-local attention -------------------------------------------------
+#
+# Local attention in fixed chunks of L tokens (the local-attention section of
+# the vllm.cpp repository listing, "What's implemented": a chunked-local
+# attention spec, exact virtual Q/K batches and a reusable block-table
+# gather/update plan): the query at position p attends to keys t <= p with
+# floor(t / L) == floor(p / L), i.e. t in [floor(p / L) * L, p].
+
+
+def chunked_local_mask(n: int, Q: int, L: int) -> np.ndarray:
+    """Boolean [Q, n]: query row i (position n - Q + i) keeps key t."""
+    p = (n - Q + np.arange(Q))[:, None]
+    t = np.arange(n)[None, :]
+    return (t <= p) & (t >= (p // L) * L)
+
+
+def prefill_chunked_local(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
+                          kv_fmt: str, block_tables: np.ndarray, query_start_loc: np.ndarray,
+                          context_lens: np.ndarray, scale: float, chunk: int,
+                          k_scale=1.0, v_scale=1.0) -> np.ndarray:
+    """Chunked-local attention of every query row (float64 [sumQ, Hq, D])."""
+    B = len(context_lens)
+    out = np.zeros(q.shape, np.float64)
+    for s in range(B):
+        a, b = int(query_start_loc[s]), int(query_start_loc[s + 1])
+        if b <= a:
+            continue
+        n = int(context_lens[s])
+        K = reassemble(k_pool, kv_fmt, k_scale, block_tables[s], n)
+        V = reassemble(v_pool, kv_fmt, v_scale, block_tables[s], n)
+        qs = q_bits_to_f64(q[a:b], q_fmt)
+        Q, Hq, D = qs.shape
+        Hkv = K.shape[1]
+        g = Hq // Hkv
+        mask = chunked_local_mask(n, Q, chunk)
+        for kv in range(Hkv):
+            qg = qs[:, kv * g:(kv + 1) * g, :]
+            z = scale * np.einsum("rgd,td->rgt", qg, K[:, kv, :])
+            z = np.where(mask[:, None, :], z, -np.inf)
+            out[a:b, kv * g:(kv + 1) * g] = np.einsum("rgt,td->rgd", softmax_rows(z), V[:, kv, :])
+    return out
+
+
+def chunked_local_plan(query_start_loc, context_lens, block_tables, chunk: int, num_virtual: int):
+    """The virtual batch of chunked-local attention: every (sequence, chunk)
+    that holds query tokens becomes one ordinary causal sequence, in
+    (sequence, chunk) order.  Its query rows are the chunk's rows of q (in
+    place), its context runs from the chunk start to its last query token,
+    and its block table is the slice of pages from the chunk start (padded
+    with -1 to chunk / 16 entries).  Unused entries up to ``num_virtual``
+    have no query rows (start = end = sumQ), context 0 and -1 tables.
+
+    Returns (v_query_start_loc [V + 1], v_context_lens [V], v_block_tables
+    [V, chunk / 16]) as int32."""
+    qsl = np.asarray(query_start_loc, np.int64)
+    ctx = np.asarray(context_lens, np.int64)
+    bt = np.asarray(block_tables, np.int64)
+    P = chunk // 16
+    sumq = int(qsl[-1])
+    vq = [0]
+    vctx, vbt = [], []
+    for s in range(len(ctx)):
+        a, b = int(qsl[s]), int(qsl[s + 1])
+        n = int(ctx[s])
+        if b <= a:
+            continue
+        first = n - (b - a)                       # position of the first query token
+        for c in range(first // chunk, (n - 1) // chunk + 1):
+            lo, hi = max(first, c * chunk), min(n - 1, c * chunk + chunk - 1)
+            rows = hi - lo + 1
+            vq.append(vq[-1] + rows)
+            vlen = hi + 1 - c * chunk
+            vctx.append(vlen)
+            row = np.full(P, -1, np.int64)
+            npg = (vlen + 15) // 16
+            row[:npg] = bt[s, c * P:c * P + npg]
+            vbt.append(row)
+    assert len(vctx) <= num_virtual
+    while len(vctx) < num_virtual:
+        vq.append(sumq)
+        vctx.append(0)
+        vbt.append(np.full(P, -1, np.int64))
+    return (np.asarray(vq, np.int32), np.asarray(vctx, np.int32),
+            np.asarray(vbt, np.int32).reshape(num_virtual, P))
+
+
+def dead_pages(context_lens, window: int, chunk: int) -> np.ndarray:
+    """Leading logical pages of each sequence that no query at position >= n
+    (n = context_lens[s], the next token's position) can attend to: with a
+    sliding window W, keys t <= n - W; with chunked-local attention of L,
+    keys below floor(n / L) * L; the larger of the two (0 = off)."""
+    out = []
+    for n in np.asarray(context_lens, np.int64):
+        dead = 0
+        if window > 0:
+            dead = max(dead, int(n) + 1 - window)
+        if chunk > 0:
+            dead = max(dead, (int(n) // chunk) * chunk)
+        out.append(max(0, dead) // 16)
+    return np.asarray(out, np.int32)
+
+
 __all__ = ["reassemble", "decode", "decode_partials", "lse_combine", "prefill",
-           "prefill_mask", "softmax_rows", "decode_window"]
+           "prefill_mask", "softmax_rows", "decode_window", "chunked_local_mask",
+           "prefill_chunked_local", "chunked_local_plan", "dead_pages"]

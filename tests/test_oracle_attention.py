@@ -327,3 +327,94 @@ def test_per_head_scales_map_to_kv_heads():
     for h in range(3):
         ref = A.decode(*args, float(ks[h]), float(vs[h]))
         assert np.array_equal(got[:, 2 * h:2 * h + 2], ref[:, 2 * h:2 * h + 2]), h
+
+
+# ---- chunked-local attention ------------------------------------------------
+
+def brute_chunked_local_seq(q, K, V, scale, L):
+    """Pure-Python chunked-local attention for one sequence: query i at
+    position p = n - Q + i sees keys floor(p / L) * L .. p."""
+    Q, n = len(q), len(K)
+    out = []
+    for i in range(Q):
+        p = n - Q + i
+        lo = (p // L) * L
+        out.append(brute_decode_seq(q[i], K[lo:p + 1], V[lo:p + 1], scale, 0))
+    return out
+
+
+def oracle_chunked_local(case, L, kp=None, vp=None):
+    if kp is None:
+        kp, vp = oracle_pools(case)
+    return A.prefill_chunked_local(raw_bits(case.q), case.q_dtype, kp, vp, case.kv_dtype,
+                                   case.block_tables.numpy(), case.query_start_loc.numpy(),
+                                   case.context_lens.numpy(), case.scale, L)
+
+
+@pytest.mark.parametrize("L", [16, 32])
+def test_chunked_local_vs_brute_force(L):
+    case = make_case(4, B=3, qlen_range=(1, 40), cached_range=(1, 50), Hq=4, Hkv=2, D=64)
+    out = oracle_chunked_local(case, L)
+    qsl = case.query_start_loc.numpy()
+    qf = q_bits_to_f64(raw_bits(case.q), case.q_dtype)
+    for s in range(case.num_seqs):
+        K, V = contiguous_kv(case, s)
+        ref = brute_chunked_local_seq(qf[qsl[s]:qsl[s + 1]].tolist(), K.tolist(), V.tolist(),
+                                      case.scale, L)
+        assert np.max(np.abs(out[qsl[s]:qsl[s + 1]] - np.array(ref))) < 1e-12
+
+
+def test_chunked_local_with_a_chunk_beyond_every_context_is_causal_prefill():
+    case = make_case(4, B=3, qlen_range=(1, 30), cached_range=(1, 60), Hq=4, Hkv=2, D=64, window=0)
+    kp, vp = oracle_pools(case)
+    a = oracle_chunked_local(case, 1024, kp, vp)
+    b = oracle_prefill(case, kp, vp)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_chunked_local_virtual_batch_is_the_same_attention():
+    """Ordinary causal prefill over the plan's virtual batch (chunk-start
+    contexts, gathered table slices, q rows in place) equals chunked-local
+    attention computed directly from its mask."""
+    for L in (16, 48):
+        case = make_case(4, seed=9, B=4, qlen_range=(1, 100), cached_range=(0, 120), Hq=4, Hkv=2,
+                         D=64, window=0)
+        kp, vp = oracle_pools(case)
+        V = case.query_start_loc[-1].item() // L + 2 * case.num_seqs
+        vq, vctx, vbt = A.chunked_local_plan(case.query_start_loc.numpy(), case.context_lens.numpy(),
+                                             case.block_tables.numpy(), L, V)
+        got = A.prefill(raw_bits(case.q), case.q_dtype, kp, vp, case.kv_dtype, vbt, vq, vctx,
+                        case.scale, 0)
+        ref = oracle_chunked_local(case, L, kp, vp)
+        assert np.max(np.abs(got - ref)) < 1e-12, L
+
+
+def test_chunked_local_plan_small_example():
+    """By hand: one sequence, 40 cached + 30 new tokens (positions 40..69),
+    chunks of 32: chunk 1 holds positions 40..63 (24 rows, context 32), chunk
+    2 holds 64..69 (6 rows, context 6)."""
+    bt = np.array([[7, 3, 9, 5, 1, -1]], np.int32)
+    vq, vctx, vbt = A.chunked_local_plan(np.array([0, 30]), np.array([70]), bt, 32, 4)
+    assert vq.tolist() == [0, 24, 30, 30, 30]
+    assert vctx.tolist() == [32, 6, 0, 0]
+    assert vbt.tolist() == [[9, 5], [1, -1], [-1, -1], [-1, -1]]
+
+
+def test_dead_pages():
+    # by hand: n = 100, window 40 -> keys <= 60 dead (61 tokens) -> 3 full pages;
+    # chunk 32 -> chunk start 96 -> 6 pages; both -> 6
+    assert A.dead_pages([100], 40, 0).tolist() == [3]
+    assert A.dead_pages([100], 0, 32).tolist() == [6]
+    assert A.dead_pages([100], 40, 32).tolist() == [6]
+    assert A.dead_pages([10, 0], 40, 0).tolist() == [0, 0]
+    # property: no key a future query keeps lies in a dead page
+    for n in range(0, 200, 7):
+        for W, L in ((40, 0), (0, 32), (17, 48)):
+            d = int(A.dead_pages([n], W, L)[0]) * 16
+            for p in range(n, n + 100):
+                lo = 0
+                if W:
+                    lo = max(lo, p - W + 1)
+                if L:
+                    lo = max(lo, (p // L) * L)
+                assert lo >= d, (n, W, L, p)
