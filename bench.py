@@ -86,20 +86,27 @@ def decode_bytes(case, shared_tokens: int = 0) -> dict:
                 unique_decode=unique_kv + other)
 
 
-def prefill_work(case) -> dict:
+def prefill_work(case, chunk: int = 0) -> dict:
     """Algorithmic work of one chunked-prefill call: kept (query token, key)
     pairs, their flops (4 D per pair and query head: q.k and p.v), and the
-    bytes of q, out and each sequence's K/V range read once."""
+    bytes of q, out and each sequence's K/V range read once.  chunk > 0:
+    chunked-local attention of that chunk (keys floor(p / chunk) * chunk .. p)
+    instead of the sliding window."""
     import numpy as np
     Q = np.diff(case.query_start_loc.numpy()).astype(np.int64)
     n = case.context_lens.numpy().astype(np.int64)
-    W = case.window
+    W = 0 if chunk else case.window
     pairs = 0
     kv_tokens = 0
     for s in range(len(n)):
         if Q[s] == 0:
             continue
         p = n[s] - Q[s] + np.arange(Q[s])
+        if chunk:
+            lo = (p // chunk) * chunk
+            pairs += int(np.sum(p - lo + 1))
+            kv_tokens += int(n[s] - lo[0])          # chunks are disjoint: each key read once
+            continue
         lo = np.maximum(0, p - W + 1) if W > 0 else np.zeros_like(p)
         pairs += int(np.sum(p - lo + 1))
         kv_tokens += int(n[s] - lo[0])
@@ -109,9 +116,10 @@ def prefill_work(case) -> dict:
     return dict(pairs=pairs, flops=flops, bytes=byts, tokens=int(Q.sum()))
 
 
-def cpu_baseline_prefill(case, seconds: float) -> dict:
-    """The fp64 oracle, unchanged, on whole sequences of the chunked-prefill
-    batch (every query row of each), for about ``seconds``."""
+def cpu_baseline_prefill(case, seconds: float, chunk: int = 0) -> dict:
+    """The fp64 oracle, unchanged, on the last query rows of sequences of
+    the chunked-prefill batch, for about ``seconds`` (chunk > 0: its
+    chunked-local attention, one sequence at a time)."""
     import numpy as np
     from oracle import attention as A
     from oracle import scatter as S
@@ -135,24 +143,41 @@ def cpu_baseline_prefill(case, seconds: float) -> dict:
         for j in batch:
             Qj = int(qsl[j + 1] - qsl[j])
             rows[j] = list(range(max(0, Qj - per), Qj))           # the chunk's last rows
-        A.prefill(qb, case.q_dtype, kp, vp, case.kv_dtype, case.block_tables.numpy(), qsl,
-                  n, case.scale, W, rows=rows, workers=cores)
+        if chunk:
+            # the last r rows of sequence j are a sequence of r queries with
+            # the same context
+            for j in batch:
+                r = len(rows[j])
+                b = int(qsl[j + 1])
+                A.prefill_chunked_local(qb[b - r:b], case.q_dtype, kp, vp, case.kv_dtype,
+                                        case.block_tables.numpy()[j:j + 1], np.array([0, r]),
+                                        n[j:j + 1], case.scale, chunk)
+        else:
+            A.prefill(qb, case.q_dtype, kp, vp, case.kv_dtype, case.block_tables.numpy(), qsl,
+                      n, case.scale, W, rows=rows, workers=cores)
         for j in batch:
             Qj = int(qsl[j + 1] - qsl[j])
             pp = n[j] - Qj + np.asarray(rows[j], dtype=np.int64)
-            lo = np.maximum(0, pp - W + 1) if W > 0 else np.zeros_like(pp)
+            if chunk:
+                lo = (pp // chunk) * chunk
+            else:
+                lo = np.maximum(0, pp - W + 1) if W > 0 else np.zeros_like(pp)
             flops += int(np.sum(pp - lo + 1)) * Hq * 4 * D
         done += batch
         s += len(batch)
     dt = time.time() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"the last {per} query rows (all heads) of sequences 0..{done[-1]} of the "
-                      f"chunked-prefill batch ({len(done)} of {case.num_seqs}), {dt:.1f} s"}
+    what = f"chunked-local attention ({chunk}-token chunks) of " if chunk else ""
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": 1 if chunk else cores, "kind": "oracle",
+            "sample": f"{what}the last {per} query rows (all heads) of sequences 0..{done[-1]} of "
+                      f"the chunked-prefill batch ({len(done)} of {case.num_seqs}), {dt:.1f} s"}
 
 
-def bench_prefill(case, steps: int, warmup: int) -> dict:
+def bench_prefill(case, steps: int, warmup: int, chunk: int = 0) -> dict:
     """Time the chunked-prefill call on ``case`` (K/V written by the library's
-    cache write first, untimed) with HIP events around each call."""
+    cache write first, untimed) with HIP events around each call.  chunk > 0:
+    chunked-local attention, one call = the virtual-batch plan + the prefill
+    over the virtual batch."""
     import paged_kv_cache_183_amd as P
     dev = torch.device("cuda", 0)
     view = lambda t: t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16)  # noqa: E731
@@ -167,6 +192,18 @@ def bench_prefill(case, steps: int, warmup: int) -> dict:
     def call():
         P.vllm_paged_attn_prefill(out, q, view(kc), view(vc), bt, qsl, ctx, case.max_query_len,
                                   case.scale, case.window)
+
+    if chunk:
+        V = P.vllm_paged_chunked_local_virtual_count(case.num_seqs, int(case.query_start_loc[-1]),
+                                                     chunk)
+        vq = torch.empty(V + 1, dtype=torch.int32, device=dev)
+        vcx = torch.empty(V, dtype=torch.int32, device=dev)
+        vbt = torch.empty(V, chunk // 16, dtype=torch.int32, device=dev)
+        mq = min(case.max_query_len, chunk)
+
+        def call():  # noqa: F811
+            P.vllm_paged_chunked_local_plan(qsl, ctx, bt, chunk, vq, vcx, vbt)
+            P.vllm_paged_attn_prefill(out, q, view(kc), view(vc), vbt, vq, vcx, mq, case.scale, 0)
 
     for _ in range(warmup):
         call()
@@ -183,9 +220,14 @@ def bench_prefill(case, steps: int, warmup: int) -> dict:
     wall = (time.perf_counter() - t0) / steps
     ms = [a.elapsed_time(b) for a, b in evs]
     mean = sum(ms) / len(ms)
-    w = prefill_work(case)
+    w = prefill_work(case, chunk)
     tf = w["flops"] / (mean * 1e-3) / 1e12
-    return {"workload": case.name, "ms_per_call": round(mean, 5),
+    extra = {}
+    if chunk:
+        nv = int((vcx > 0).sum())
+        extra = {"chunk_size": chunk, "virtual_seqs": nv, "call": "plan + prefill"}
+    return {"workload": case.name + (f"_chunked_local{chunk}" if chunk else ""), **extra,
+            "ms_per_call": round(mean, 5),
             "p10_ms": round(float(np.percentile(ms, 10)), 5),
             "p90_ms": round(float(np.percentile(ms, 90)), 5),
             "wall_ms_per_call": round(wall * 1e3, 5),
@@ -194,7 +236,8 @@ def bench_prefill(case, steps: int, warmup: int) -> dict:
             "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(case.name, ("prefill.hip", "common.h"))}}
+                         "traffic": None if chunk else
+                         measured_traffic(case.name, ("prefill.hip", "common.h"))}}
 
 
 def cpu_baseline(case, seconds: float) -> dict:
@@ -250,6 +293,8 @@ def main():
                     help="decode a prefix-shared workload without reading the shared pages once")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill measurement appended to the decode line")
+    ap.add_argument("--chunk-size", type=int, default=0,
+                    help="prefill workload: chunked-local attention of this chunk (plan + prefill)")
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graphs instead of launching every call eagerly")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -402,7 +447,7 @@ def main():
         "vs_baseline": None,
         "dtype": case.kv_dtype,
         "data": "synthetic",
-        "config": {"workload": case.name, "num_seqs": case.num_seqs,
+        "config": {"workload": r["workload"], "num_seqs": case.num_seqs,
                    "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": 16,
                    "context_lens": cfg.get("ctx_range") or cfg.get("ctx_list"),
@@ -432,15 +477,19 @@ def main():
     if not args.no_prefill:
         # The matrix-core variant of the path, on the chunked-prefill workload.
         res["prefill"] = bench_prefill(make_case(4), steps=min(args.steps, 20), warmup=3)
+        # chunked-local attention (8192-token chunks) on the same batch
+        res["chunked_local"] = bench_prefill(make_case(4), steps=min(args.steps, 20), warmup=3,
+                                             chunk=args.chunk_size or 8192)
     print(json.dumps(res), flush=True)
 
 
 def main_prefill(args):
     """Standalone line for the chunked-prefill workload (matrix-core roof)."""
     case = make_case(args.config)
-    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(case, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(case, args.cpu_seconds,
+                                                                 args.chunk_size)
     torch.cuda.set_device(0)
-    r = bench_prefill(case, steps=args.steps, warmup=args.warmup)
+    r = bench_prefill(case, steps=args.steps, warmup=args.warmup, chunk=args.chunk_size)
     res = {
         "metric": PREFILL_METRIC,
         "value": r["tflops"],
@@ -454,10 +503,11 @@ def main_prefill(args):
         "vs_baseline": None,
         "dtype": case.q_dtype,
         "data": "synthetic",
-        "config": {"workload": case.name, "num_seqs": case.num_seqs, "sum_q": int(case.query_start_loc[-1]),
+        "config": {"workload": r["workload"], "num_seqs": case.num_seqs, "sum_q": int(case.query_start_loc[-1]),
                    "q_heads": case.num_q_heads,
                    "kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "block_size": 16,
-                   "window": case.window, "kept_pairs": r["kept_pairs"],
+                   "window": 0 if args.chunk_size else case.window,
+                   "chunk_size": args.chunk_size or None, "kept_pairs": r["kept_pairs"],
                    "flops_per_step": r["flops_per_call"], "seed": args.config, "launch": "eager"},
         "tokens_per_s": r["tokens_per_s"],
         "prefill_call_ms": {"mean": r["ms_per_call"], "p10": r["p10_ms"], "p90": r["p90_ms"]},

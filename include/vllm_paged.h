@@ -80,7 +80,7 @@ typedef enum vllm_dtype {
  * (in elements, row-major) give the first `ndim` dimensions.  Every tensor
  * passed to this library must be contiguous (stride of the last dimension
  * 1, each other stride the product of the later extents; dimensions of
- * extent 1 may carry any stride). */
+ * extent 1, and tensors with no elements, may carry any strides). */
 typedef struct vllm_tensor {
   void* data;
   int32_t dtype;     /* vllm_dtype */
@@ -236,10 +236,14 @@ size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
  * already in the pool).  Query row at position p attends to keys t <= p with
  * t > p - window (window = 0: no lower bound).  Scores use bf16/f16 matrix
  * products with fp32 accumulation; the softmax probabilities are rounded to
- * q's dtype before the product with V; output rounded to q's dtype.
+ * q's dtype before the product with V; output rounded to q's dtype.  FP8
+ * pools: every E4M3 / E5M2 value is exact in fp16 and bf16, so codes enter
+ * the products unchanged; the K scale multiplies the scores and the V scale
+ * the output (per tensor, or per kv-head through opts->k_scales / v_scales,
+ * as for decode).
  *   out          [sumQ, Hq, D]  dtype of q (written)
  *   q            [sumQ, Hq, D]  F16 or BF16
- *   k_cache, v_cache [num_blocks, Hkv, 16, D]  q's dtype
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D]  q's dtype, FP8_E4M3 or FP8_E5M2
  *   block_tables [B, max_blocks_per_seq]  I32
  *   query_start_loc [B + 1]  I32, non-decreasing, query_start_loc[0] = 0,
  *                    query_start_loc[B] = sumQ
@@ -257,6 +261,67 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
                                     const vllm_tensor* context_lens,
                                     int32_t max_query_len, float scale, int32_t window,
                                     const vllm_attn_opts* opts, void* hip_stream);
+
+/*
+ * Chunked-local attention as a virtual batch (the local-attention section of
+ * the vllm.cpp repository listing, "What's implemented": exact virtual Q/K
+ * batches and a reusable block-table gather/update plan).  Chunked-local
+ * attention of chunk L keeps, for the query at position p, the keys
+ * floor(p / L) * L .. p.  The plan turns every (sequence, chunk) holding query
+ * tokens into one ordinary causal sequence, in (sequence, chunk) order:
+ *   v_query_start_loc[v]  first row of q of virtual sequence v (the rows stay
+ *                         in place, so q and out are used as they are)
+ *   v_context_lens[v]     keys from the chunk start to its last query token
+ *   v_block_tables[v, :]  the pages of the original table from the chunk
+ *                         start, -1 past the virtual context
+ * Entries past the batch's virtual sequences have no rows (start = sumQ),
+ * context 0 and -1 tables.  The plan depends only on the metadata, so one
+ * plan serves every layer.  Running vllm_paged_attn_prefill (max_query_len
+ * min(max_query_len, chunk_size), window 0) or, when every sequence has one
+ * query token, vllm_paged_attn_decode (first B entries) on the virtual batch
+ * gives chunked-local attention.
+ *   query_start_loc [B + 1] I32, context_lens [B] I32 (n >= Q_s),
+ *   block_tables [B, max_blocks_per_seq] I32   (as vllm_paged_attn_prefill)
+ *   chunk_size        tokens per chunk, a positive multiple of 16
+ *   v_query_start_loc [V + 1] I32, v_context_lens [V] I32,
+ *   v_block_tables [V, chunk_size / 16] I32   written; V from
+ *                     vllm_paged_chunked_local_virtual_count
+ * Device values are clamped so that nothing is read or written out of
+ * bounds; inconsistent metadata gives unspecified plans.
+ */
+vllm_status vllm_paged_chunked_local_plan(const vllm_tensor* query_start_loc,
+                                          const vllm_tensor* context_lens,
+                                          const vllm_tensor* block_tables, int32_t chunk_size,
+                                          vllm_tensor* v_query_start_loc,
+                                          vllm_tensor* v_context_lens,
+                                          vllm_tensor* v_block_tables, void* hip_stream);
+
+/* Upper bound V of the virtual sequences of a plan: floor(sumQ / chunk) +
+ * 2 * num_seqs (each sequence's Q_s tokens span at most Q_s / chunk + 2
+ * chunks).  0 for invalid arguments. */
+int64_t vllm_paged_chunked_local_virtual_count(int32_t num_seqs, int32_t num_tokens,
+                                               int32_t chunk_size);
+
+/*
+ * Page recycling for local attention: the leading pages of each sequence that
+ * no query at position >= n (n = context_lens[s], the next token's position)
+ * can attend to -- keys t <= n - window with a sliding window, keys below
+ * floor(n / chunk_size) * chunk_size with chunked-local attention, the larger
+ * of the two -- are reported and their block_tables entries set to -1
+ * (entries already -1 are skipped, so repeated calls report each page once).
+ * Reported ids of sequence s are freed_pages[freed_offsets[s] ..
+ * freed_offsets[s + 1]).  Pages shared with other sequences are reported by
+ * each sequence that drops them: reference counting belongs to the caller's
+ * allocator.  Decode and prefill never read table entries below the kept
+ * range, so recycled entries are never read.
+ *   context_lens [B] I32; block_tables [B, max_blocks_per_seq] I32 (updated)
+ *   window, chunk_size  0 = off; chunk_size a multiple of 16
+ *   freed_offsets [B + 1] I32, freed_pages [B * max_blocks_per_seq] I32 written
+ */
+vllm_status vllm_paged_recycle_pages(const vllm_tensor* context_lens, vllm_tensor* block_tables,
+                                     int32_t window, int32_t chunk_size,
+                                     vllm_tensor* freed_offsets, vllm_tensor* freed_pages,
+                                     void* hip_stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

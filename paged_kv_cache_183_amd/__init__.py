@@ -17,4 +17,7 @@ from .binding import (  # noqa: F401
     vllm_paged_attn_workspace_size, vllm_paged_attn_decode_shared_prefix,
     vllm_paged_attn_shared_prefix_workspace_size,
     vllm_paged_cache_write,
+    vllm_paged_chunked_local_plan,
+    vllm_paged_chunked_local_virtual_count,
+    vllm_paged_recycle_pages,
 )

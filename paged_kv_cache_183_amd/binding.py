@@ -33,7 +33,8 @@ BLOCK_SIZE = 16
 EXPORTED = ["vllm_abi_version", "vllm_last_error", "vllm_paged_cache_write",
             "vllm_paged_attn_decode", "vllm_paged_attn_workspace_size",
             "vllm_paged_attn_decode_shared_prefix", "vllm_paged_attn_shared_prefix_workspace_size",
-            "vllm_paged_attn_prefill"]
+            "vllm_paged_attn_prefill", "vllm_paged_chunked_local_plan",
+            "vllm_paged_chunked_local_virtual_count", "vllm_paged_recycle_pages"]
 
 
 class VllmTensor(ctypes.Structure):
@@ -80,6 +81,13 @@ def _load():
     lib.vllm_paged_attn_prefill.restype = ctypes.c_int
     lib.vllm_paged_attn_prefill.argtypes = [T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float,
                                             ctypes.c_int32, O, ctypes.c_void_p]
+    lib.vllm_paged_chunked_local_plan.restype = ctypes.c_int
+    lib.vllm_paged_chunked_local_plan.argtypes = [T, T, T, ctypes.c_int32, T, T, T, ctypes.c_void_p]
+    lib.vllm_paged_chunked_local_virtual_count.restype = ctypes.c_int64
+    lib.vllm_paged_chunked_local_virtual_count.argtypes = [ctypes.c_int32] * 3
+    lib.vllm_paged_recycle_pages.restype = ctypes.c_int
+    lib.vllm_paged_recycle_pages.argtypes = [T, T, ctypes.c_int32, ctypes.c_int32, T, T,
+                                             ctypes.c_void_p]
     return lib
 
 
@@ -200,12 +208,40 @@ def vllm_paged_attn_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
 
 
 def vllm_paged_attn_prefill(out, q, k_cache, v_cache, block_tables, query_start_loc,
-                            context_lens, max_query_len, scale, window=0, stream=None) -> None:
+                            context_lens, max_query_len, scale, window=0, k_scale=0.0, v_scale=0.0,
+                            stream=None) -> None:
     """Chunked-prefill attention into ``out`` [sumQ, Hq, D]."""
     args = [tensor_desc(x) for x in (out, q, k_cache, v_cache, block_tables, query_start_loc,
                                      context_lens)]
-    o = _opts()
+    o = _opts(k_scale, v_scale)
     _check(LIB.vllm_paged_attn_prefill(*[ctypes.byref(a) for a in args],
                                        ctypes.c_int32(max_query_len), ctypes.c_float(scale),
                                        ctypes.c_int32(window), ctypes.byref(o),
                                        ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_paged_chunked_local_virtual_count(num_seqs, num_tokens, chunk_size) -> int:
+    return int(LIB.vllm_paged_chunked_local_virtual_count(num_seqs, num_tokens, chunk_size))
+
+
+def vllm_paged_chunked_local_plan(query_start_loc, context_lens, block_tables, chunk_size,
+                                  v_query_start_loc, v_context_lens, v_block_tables,
+                                  stream=None) -> None:
+    """Fill the virtual batch of chunked-local attention (int32 device tensors)."""
+    args = [tensor_desc(x) for x in (query_start_loc, context_lens, block_tables)]
+    outs = [tensor_desc(x) for x in (v_query_start_loc, v_context_lens, v_block_tables)]
+    _check(LIB.vllm_paged_chunked_local_plan(*[ctypes.byref(a) for a in args],
+                                             ctypes.c_int32(chunk_size),
+                                             *[ctypes.byref(a) for a in outs],
+                                             ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_paged_recycle_pages(context_lens, block_tables, window, chunk_size, freed_offsets,
+                             freed_pages, stream=None) -> None:
+    """Report (and drop from block_tables) the pages no later query can attend to."""
+    args = [tensor_desc(x) for x in (context_lens, block_tables)]
+    outs = [tensor_desc(x) for x in (freed_offsets, freed_pages)]
+    _check(LIB.vllm_paged_recycle_pages(*[ctypes.byref(a) for a in args], ctypes.c_int32(window),
+                                        ctypes.c_int32(chunk_size),
+                                        *[ctypes.byref(a) for a in outs],
+                                        ctypes.c_void_p(_stream(stream))))

@@ -76,9 +76,13 @@ vllm_status check_tensor(const vllm_tensor* t, const char* name, int ndim) {
   if (!t) return fail(VLLM_ERR_INVALID_ARG, "%s: null tensor descriptor", name);
   if (t->ndim != ndim)
     return fail(VLLM_ERR_INVALID_ARG, "%s: expected rank %d, got %d", name, ndim, (int)t->ndim);
-  int64_t expect = 1;
-  for (int i = ndim - 1; i >= 0; --i) {
+  bool empty = false;
+  for (int i = 0; i < ndim; ++i) {
     if (t->shape[i] < 0) return fail(VLLM_ERR_INVALID_ARG, "%s: negative extent in dim %d", name, i);
+    empty = empty || t->shape[i] == 0;
+  }
+  int64_t expect = 1;
+  for (int i = ndim - 1; i >= 0 && !empty; --i) {      // an empty tensor has no layout
     if (t->shape[i] != 1 && t->stride[i] != expect)
       return fail(VLLM_ERR_INVALID_ARG, "%s: not contiguous (dim %d stride %lld, expected %lld)", name,
                   i, (long long)t->stride[i], (long long)expect);
@@ -590,12 +594,18 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
   if (q->dtype != VLLM_DTYPE_F16 && q->dtype != VLLM_DTYPE_BF16)
     return fail(VLLM_ERR_UNSUPPORTED, "q: dtype %s, expected F16 or BF16", dtype_name(q->dtype));
   VP_TRY(check_dtype(out, "out", q->dtype));
-  if (k_cache->dtype != q->dtype)
-    return fail(VLLM_ERR_UNSUPPORTED, "prefill: k_cache dtype %s must match q (%s)",
+  if (k_cache->dtype != q->dtype && !is_fp8_dtype(k_cache->dtype))
+    return fail(VLLM_ERR_UNSUPPORTED, "prefill: k_cache dtype %s with %s queries",
                 dtype_name(k_cache->dtype), dtype_name(q->dtype));
   VP_TRY(check_dtype(v_cache, "v_cache", k_cache->dtype));
   VP_TRY(check_dtype(block_tables, "block_tables", VLLM_DTYPE_I32));
   VP_TRY(check_dtype(query_start_loc, "query_start_loc", VLLM_DTYPE_I32));
+  const bool fp8 = is_fp8_dtype(k_cache->dtype);
+  float ks = 1.0f, vs = 1.0f;
+  if (fp8) {
+    VP_TRY(scale_of(opts ? opts->k_scale : 0.0f, "k_scale", &ks));
+    VP_TRY(scale_of(opts ? opts->v_scale : 0.0f, "v_scale", &vs));
+  }
   VP_TRY(check_dtype(context_lens, "context_lens", VLLM_DTYPE_I32));
   if (D != 128) return fail(VLLM_ERR_UNSUPPORTED, "prefill head_dim %lld: supported 128", (long long)D);
   if (Hq / Hkv > 128) return fail(VLLM_ERR_UNSUPPORTED, "prefill: group size above 128");
@@ -610,6 +620,7 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
   VP_TRY(check_data(block_tables, "block_tables", 4));
   VP_TRY(check_data(query_start_loc, "query_start_loc", 4));
   VP_TRY(check_data(context_lens, "context_lens", 4));
+  if (fp8) VP_TRY(check_scales(opts));
 
   vp::PrefillParams p{};
   p.q = q->data;
@@ -628,9 +639,112 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
   p.num_blocks = (int32_t)NB;
   p.max_query_len = max_query_len;
   p.window = window;
-  p.score_scale = scale * 1.4426950408889634f;
-  VP_TRY(hip_status(vp::launch_prefill(p, (int)D, fmt_of(q->dtype), (hipStream_t)hip_stream),
+  p.score_base = scale * 1.4426950408889634f;
+  p.score_scale = p.score_base * ks;
+  p.out_scale = vs;
+  p.k_scales = (fp8 && opts) ? opts->k_scales : nullptr;
+  p.v_scales = (fp8 && opts) ? opts->v_scales : nullptr;
+  VP_TRY(hip_status(vp::launch_prefill(p, (int)D, fmt_of(k_cache->dtype), fmt_of(q->dtype),
+                                       (hipStream_t)hip_stream),
                     "prefill launch"));
+  return ok();
+}
+
+int64_t vllm_paged_chunked_local_virtual_count(int32_t num_seqs, int32_t num_tokens,
+                                               int32_t chunk_size) {
+  if (num_seqs < 0 || num_tokens < 0 || chunk_size <= 0 || chunk_size % 16 != 0) return 0;
+  return (int64_t)(num_tokens / chunk_size) + 2 * (int64_t)num_seqs;
+}
+
+vllm_status vllm_paged_chunked_local_plan(const vllm_tensor* query_start_loc,
+                                          const vllm_tensor* context_lens,
+                                          const vllm_tensor* block_tables, int32_t chunk_size,
+                                          vllm_tensor* v_query_start_loc,
+                                          vllm_tensor* v_context_lens,
+                                          vllm_tensor* v_block_tables, void* hip_stream) {
+  VP_TRY(check_tensor(query_start_loc, "query_start_loc", 1));
+  VP_TRY(check_tensor(context_lens, "context_lens", 1));
+  VP_TRY(check_tensor(block_tables, "block_tables", 2));
+  VP_TRY(check_tensor(v_query_start_loc, "v_query_start_loc", 1));
+  VP_TRY(check_tensor(v_context_lens, "v_context_lens", 1));
+  VP_TRY(check_tensor(v_block_tables, "v_block_tables", 2));
+  for (const vllm_tensor* t : {query_start_loc, context_lens, block_tables, (const vllm_tensor*)v_query_start_loc,
+                               (const vllm_tensor*)v_context_lens, (const vllm_tensor*)v_block_tables})
+    if (t->dtype != VLLM_DTYPE_I32) return fail(VLLM_ERR_UNSUPPORTED, "plan tensors must be I32");
+  if (chunk_size <= 0 || chunk_size % 16 != 0)
+    return fail(VLLM_ERR_INVALID_ARG, "chunk_size %d: a positive multiple of 16", (int)chunk_size);
+  const int64_t B = context_lens->shape[0];
+  if (query_start_loc->shape[0] != B + 1 || block_tables->shape[0] != B)
+    return fail(VLLM_ERR_INVALID_ARG, "query_start_loc needs %lld entries and block_tables %lld rows",
+                (long long)(B + 1), (long long)B);
+  const int64_t V = v_context_lens->shape[0];
+  if (v_query_start_loc->shape[0] != V + 1 || v_block_tables->shape[0] != V ||
+      v_block_tables->shape[1] != chunk_size / 16)
+    return fail(VLLM_ERR_INVALID_ARG, "virtual tensors must be [V + 1], [V], [V, chunk_size / 16]");
+  if (B > 65535 || block_tables->shape[1] > INT32_MAX / 16)
+    return fail(VLLM_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  VP_TRY(check_data(query_start_loc, "query_start_loc", 4));
+  VP_TRY(check_data(context_lens, "context_lens", 4));
+  if (B > 0) VP_TRY(check_data(block_tables, "block_tables", 4));
+  VP_TRY(check_data(v_query_start_loc, "v_query_start_loc", 4));
+  if (V > 0) {
+    VP_TRY(check_data(v_context_lens, "v_context_lens", 4));
+    VP_TRY(check_data(v_block_tables, "v_block_tables", 4));
+  }
+  vp::LocalPlanParams p{};
+  p.query_start_loc = static_cast<const int32_t*>(query_start_loc->data);
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.block_tables = static_cast<const int32_t*>(block_tables->data);
+  p.v_query_start_loc = static_cast<int32_t*>(v_query_start_loc->data);
+  p.v_context_lens = static_cast<int32_t*>(v_context_lens->data);
+  p.v_block_tables = static_cast<int32_t*>(v_block_tables->data);
+  p.num_seqs = (int32_t)B;
+  p.num_tokens = -1;                 // sumQ = query_start_loc[B], read on the device
+  p.bt_stride = (int32_t)block_tables->shape[1];
+  p.chunk = chunk_size;
+  p.num_virtual = V;
+  VP_TRY(hip_status(vp::launch_chunked_local_plan(p, (hipStream_t)hip_stream), "plan launch"));
+  return ok();
+}
+
+vllm_status vllm_paged_recycle_pages(const vllm_tensor* context_lens, vllm_tensor* block_tables,
+                                     int32_t window, int32_t chunk_size,
+                                     vllm_tensor* freed_offsets, vllm_tensor* freed_pages,
+                                     void* hip_stream) {
+  VP_TRY(check_tensor(context_lens, "context_lens", 1));
+  VP_TRY(check_tensor(block_tables, "block_tables", 2));
+  VP_TRY(check_tensor(freed_offsets, "freed_offsets", 1));
+  VP_TRY(check_tensor(freed_pages, "freed_pages", 1));
+  for (const vllm_tensor* t : {context_lens, (const vllm_tensor*)block_tables,
+                               (const vllm_tensor*)freed_offsets, (const vllm_tensor*)freed_pages})
+    if (t->dtype != VLLM_DTYPE_I32) return fail(VLLM_ERR_UNSUPPORTED, "recycle tensors must be I32");
+  if (window < 0) return fail(VLLM_ERR_INVALID_ARG, "window must be >= 0");
+  if (chunk_size < 0 || chunk_size % 16 != 0)
+    return fail(VLLM_ERR_INVALID_ARG, "chunk_size %d: 0 or a positive multiple of 16", (int)chunk_size);
+  const int64_t B = context_lens->shape[0], mb = block_tables->shape[1];
+  if (block_tables->shape[0] != B || freed_offsets->shape[0] != B + 1 || freed_pages->shape[0] < B * mb)
+    return fail(VLLM_ERR_INVALID_ARG, "freed_offsets needs %lld entries and freed_pages %lld",
+                (long long)(B + 1), (long long)(B * mb));
+  if (B > 65535 || mb > INT32_MAX / 16 || B * mb > INT32_MAX)
+    return fail(VLLM_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  VP_TRY(check_data(freed_offsets, "freed_offsets", 4));
+  if (B > 0) {
+    VP_TRY(check_data(context_lens, "context_lens", 4));
+    if (mb > 0) {
+      VP_TRY(check_data(block_tables, "block_tables", 4));
+      VP_TRY(check_data(freed_pages, "freed_pages", 4));
+    }
+  }
+  vp::RecycleParams p{};
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.block_tables = static_cast<int32_t*>(block_tables->data);
+  p.freed_offsets = static_cast<int32_t*>(freed_offsets->data);
+  p.freed_pages = static_cast<int32_t*>(freed_pages->data);
+  p.num_seqs = (int32_t)B;
+  p.bt_stride = (int32_t)mb;
+  p.window = window;
+  p.chunk = chunk_size;
+  VP_TRY(hip_status(vp::launch_recycle_pages(p, (hipStream_t)hip_stream), "recycle launch"));
   return ok();
 }
 

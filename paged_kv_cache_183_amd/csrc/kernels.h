@@ -102,6 +102,8 @@ struct PrefillParams {
   float score_scale;           // scale * log2(e) (* k_scale for FP8 pools)
   float score_base;            // scale * log2(e)
   const float* k_scales;       // FP8 pools: [Hkv] per-head K scales (null: folded in score_scale)
+  float out_scale;             // chunked prefill: V scale of FP8 pools, else 1
+  const float* v_scales;       // chunked prefill, FP8 pools: [Hkv] per-head V scales (or null)
   // shared-prefix partials (launch_shared_prefix only): the first
   // shared_pages pages of every sequence, in splits of split_pages pages
   int32_t shared_pages;
@@ -112,13 +114,43 @@ struct PrefillParams {
   float* pfx_l;                // [num_splits, B, Hq] sum of exp2(s - m)
 };
 
-// Chunked prefill: q_fmt = pool format (kF16 / kBF16).
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipStream_t stream);
+// Chunked prefill: kv_fmt = q_fmt, kE4M3 or kE5M2.
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
+                          hipStream_t stream);
 // Shared-prefix partials: kv_fmt = q_fmt, kE4M3 or kE5M2.
 hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
                                 hipStream_t stream);
 // Pages per split of the shared-prefix pass.
 constexpr int kPrefixSplitPages = 16;
+
+struct LocalPlanParams {
+  const int32_t* query_start_loc;  // [B + 1]
+  const int32_t* context_lens;     // [B]
+  const int32_t* block_tables;     // [B, bt_stride]
+  int32_t* v_query_start_loc;      // [num_virtual + 1]
+  int32_t* v_context_lens;         // [num_virtual]
+  int32_t* v_block_tables;         // [num_virtual, chunk / 16]
+  int32_t num_seqs;
+  int32_t num_tokens;              // sumQ, or -1: query_start_loc[B]
+  int32_t bt_stride;
+  int32_t chunk;                   // tokens per local chunk, a multiple of 16
+  int64_t num_virtual;
+};
+
+hipError_t launch_chunked_local_plan(const LocalPlanParams& p, hipStream_t stream);
+
+struct RecycleParams {
+  const int32_t* context_lens;     // [B] tokens cached (the next token's position)
+  int32_t* block_tables;           // [B, bt_stride]: dead entries set to -1
+  int32_t* freed_offsets;          // [B + 1]
+  int32_t* freed_pages;            // [B * bt_stride]
+  int32_t num_seqs;
+  int32_t bt_stride;
+  int32_t window;                  // 0 = off
+  int32_t chunk;                   // 0 = off
+};
+
+hipError_t launch_recycle_pages(const RecycleParams& p, hipStream_t stream);
 
 // Decode work split: at most this many waves, each taking at least
 // kMinChunkPages pages when the chunk size is automatic.

@@ -1,0 +1,153 @@
+// Metadata kernels of local attention (the local-attention section of the
+// vllm.cpp repository listing, "What's implemented": chunked-local attention
+// through exact virtual Q/K batches and a reusable block-table gather/update
+// plan; sliding-window and fixed-chunk page recycling).
+//
+// chunked_local_plan_kernel.  Chunked-local attention of chunk L keeps, for
+// the query at position p, the keys floor(p / L) * L .. p.  Every (sequence,
+// chunk) holding query tokens becomes one ordinary causal sequence of a
+// virtual batch, in (sequence, chunk) order: its query rows are the chunk's
+// rows of q (in place), its context runs from the chunk start to its last
+// query token, and its block table is the slice of the sequence's table from
+// the chunk start (-1 past its context).  The plan depends only on the batch
+// metadata, so one plan serves every layer.
+//
+// recycle_pages_kernel.  Leading pages that no query at position >= n (the
+// next token's) can attend to are reported (compactly, with per-sequence
+// offsets) and their table entries set to -1: keys t <= n - W with a sliding
+// window W, keys below floor(n / L) * L with chunked-local attention of L.
+//
+// Both run as one workgroup: the per-sequence counts are prefix-summed with a
+// block scan, then every thread writes the entries of its own sequences.
+#include "common.h"
+#include "kernels.h"
+
+namespace vp {
+
+namespace {
+
+constexpr int kLT = 1024;     // threads of the metadata workgroup
+
+// Exclusive prefix of per-thread totals over the workgroup; returns this
+// thread's offset and writes the grand total to *total.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t* total) {
+  __shared__ int64_t s[kLT];
+  const int t = threadIdx.x;
+  s[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kLT; off <<= 1) {        // inclusive Hillis-Steele scan
+    const int64_t a = t >= off ? s[t - off] : 0;
+    __syncthreads();
+    s[t] += a;
+    __syncthreads();
+  }
+  *total = s[kLT - 1];
+  const int64_t ex = t > 0 ? s[t - 1] : 0;
+  __syncthreads();
+  return ex;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kLT) void chunked_local_plan_kernel(LocalPlanParams p) {
+  const int B = p.num_seqs;
+  const int L = p.chunk;
+  const int P = L / 16;                         // table entries per virtual sequence
+  const int per = (B + kLT - 1) / kLT;
+  const int s0 = threadIdx.x * per;
+  // rows of q: given, or query_start_loc[B]
+  const int sumq = p.num_tokens >= 0 ? p.num_tokens : max(p.query_start_loc[B], 0);
+  // (clamped so that no value of the metadata leads outside the tables: a
+  // context shorter than its chunk keeps only its last n query rows)
+  auto seq = [&](int s, int& qa, int& qb, int& n) __attribute__((always_inline)) {
+    qa = min(max(p.query_start_loc[s], 0), sumq);
+    qb = min(max(p.query_start_loc[s + 1], qa), sumq);
+    n = min(max(p.context_lens[s], 0), p.bt_stride * 16);
+    if (qb - qa > n) qa = qb - n;
+  };
+  int64_t cnt = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s >= B) break;
+    int qa, qb, n;
+    seq(s, qa, qb, n);
+    if (qb > qa) cnt += (n - 1) / L - (n - (qb - qa)) / L + 1;
+  }
+  int64_t total = 0;
+  int64_t v = block_exclusive_scan(cnt, &total);
+  const int64_t V = p.num_virtual;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s >= B) break;
+    int qa, qb, n;
+    seq(s, qa, qb, n);
+    if (qb <= qa) continue;
+    const int first = n - (qb - qa);            // position of the first query token
+    const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
+    for (int c = first / L; c <= (n - 1) / L; ++c, ++v) {
+      if (v >= V) break;
+      const int lo = max(first, c * L), hi = min(n - 1, c * L + L - 1);
+      const int vlen = hi + 1 - c * L;
+      p.v_query_start_loc[v] = qa + (lo - first);
+      p.v_context_lens[v] = vlen;
+      const int npg = (vlen + 15) / 16;
+      int32_t* row = p.v_block_tables + v * P;
+      for (int j = 0; j < P; ++j) row[j] = j < npg ? bt[c * P + j] : -1;
+    }
+  }
+  // unused virtual sequences: no rows, no keys
+  for (int64_t w = min(total, V) + threadIdx.x; w < V; w += kLT) {
+    p.v_query_start_loc[w] = sumq;
+    p.v_context_lens[w] = 0;
+    for (int j = 0; j < P; ++j) p.v_block_tables[w * P + j] = -1;
+  }
+  if (threadIdx.x == 0) p.v_query_start_loc[V] = sumq;
+}
+
+__global__ __launch_bounds__(kLT) void recycle_pages_kernel(RecycleParams p) {
+  const int B = p.num_seqs;
+  const int per = (B + kLT - 1) / kLT;
+  const int s0 = threadIdx.x * per;
+  auto dead_of = [&](int s) __attribute__((always_inline)) {
+    const int n = max(p.context_lens[s], 0);
+    int dead = 0;
+    if (p.window > 0) dead = max(dead, n + 1 - p.window);
+    if (p.chunk > 0) dead = max(dead, (n / p.chunk) * p.chunk);
+    return min(max(dead, 0) / 16, p.bt_stride);
+  };
+  int64_t cnt = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s >= B) break;
+    const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
+    const int d = dead_of(s);
+    for (int j = 0; j < d; ++j) cnt += bt[j] >= 0;
+  }
+  int64_t total = 0;
+  int64_t off = block_exclusive_scan(cnt, &total);
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s >= B) break;
+    int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
+    p.freed_offsets[s] = (int32_t)off;
+    const int d = dead_of(s);
+    for (int j = 0; j < d; ++j) {
+      if (bt[j] < 0) continue;                  // recycled before
+      p.freed_pages[off++] = bt[j];
+      bt[j] = -1;
+    }
+  }
+  if (threadIdx.x == 0) p.freed_offsets[B] = (int32_t)total;
+}
+
+hipError_t launch_chunked_local_plan(const LocalPlanParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(chunked_local_plan_kernel, dim3(1), dim3(kLT), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_recycle_pages(const RecycleParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(recycle_pages_kernel, dim3(1), dim3(kLT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace vp

@@ -387,16 +387,18 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (!row_ok) return;
   if constexpr (!PFX) {
+    // FP8 pools: the V scale (per tensor or per kv-head) applies once here
+    const float w = inv * (p.v_scales ? p.v_scales[hk] : p.out_scale);
     uint16_t* op = static_cast<uint16_t*>(p.out) + q_off + 4 * hf;
 #pragma unroll
     for (int m = 0; m < D / 32; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = 4 * j;
-        const uint32_t w0 = (uint32_t)f32_to_16<QF>(o[m][k] * inv) |
-                            ((uint32_t)f32_to_16<QF>(o[m][k + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_16<QF>(o[m][k + 2] * inv) |
-                            ((uint32_t)f32_to_16<QF>(o[m][k + 3] * inv) << 16);
+        const uint32_t w0 = (uint32_t)f32_to_16<QF>(o[m][k] * w) |
+                            ((uint32_t)f32_to_16<QF>(o[m][k + 1] * w) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_16<QF>(o[m][k + 2] * w) |
+                            ((uint32_t)f32_to_16<QF>(o[m][k + 3] * w) << 16);
         *reinterpret_cast<uint2*>(op + 32 * m + 8 * j) = make_uint2(w0, w1);
       }
   } else {
@@ -426,7 +428,8 @@ static hipError_t launch_tiles(const PrefillParams& x, int64_t grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
+                          hipStream_t stream) {
   if (head_dim != 128) return hipErrorNotSupported;
   const int tq = kRows / p.group;
   if (tq < 1) return hipErrorNotSupported;
@@ -436,6 +439,13 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int q_fmt, hipSt
   const int64_t grid = (pairs + 7) / 8 * 8 * x.num_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (kv_fmt == kE4M3)
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, false>(x, grid, stream)
+                          : launch_tiles<kF16, kE4M3, false>(x, grid, stream);
+  if (kv_fmt == kE5M2)
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE5M2, false>(x, grid, stream)
+                          : launch_tiles<kF16, kE5M2, false>(x, grid, stream);
+  if (kv_fmt != q_fmt) return hipErrorNotSupported;
   return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, false>(x, grid, stream)
                         : launch_tiles<kF16, kF16, false>(x, grid, stream);
 }

@@ -140,7 +140,12 @@ def test_prefill_validation():
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "scale": -0.1})
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **_prefill_args(Hq=3, Hkv=2))
     _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(D=64))
-    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(kvdt=torch.uint8))
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(kvdt=torch.int32))
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(kvdt=torch.float16))
+    e4 = _prefill_args(kvdt=torch.uint8)                   # E4M3 pools: scales must be > 0
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **e4, k_scale=-1.0)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **e4, v_scale=float("nan"))
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_attn_prefill, **e4)
     _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(dt=torch.float32))
     b = _prefill_args()
     b["query_start_loc"] = torch.tensor([0, 5], dtype=torch.int32)       # needs B + 1 entries
@@ -153,3 +158,68 @@ def test_prefill_validation():
     # nothing to do: no launch, no pointer touched
     P.vllm_paged_attn_prefill(**{**_prefill_args(sumq=0), "query_start_loc":
                                  torch.zeros(3, dtype=torch.int32)}, stream=0)
+
+
+def test_chunked_local_virtual_count():
+    assert P.vllm_paged_chunked_local_virtual_count(3, 100, 32) == 100 // 32 + 6
+    assert P.vllm_paged_chunked_local_virtual_count(0, 0, 16) == 0
+    assert P.vllm_paged_chunked_local_virtual_count(2, 10, 24) == 0        # not a multiple of 16
+    assert P.vllm_paged_chunked_local_virtual_count(-1, 10, 16) == 0
+
+
+def _plan_args(B=2, mb=8, chunk=32, V=None, dt=torch.int32):
+    V = P.vllm_paged_chunked_local_virtual_count(B, 10, chunk) if V is None else V
+    return dict(query_start_loc=torch.zeros(B + 1, dtype=dt), context_lens=torch.zeros(B, dtype=dt),
+                block_tables=torch.zeros(B, mb, dtype=dt), chunk_size=chunk,
+                v_query_start_loc=torch.zeros(V + 1, dtype=torch.int32),
+                v_context_lens=torch.zeros(V, dtype=torch.int32),
+                v_block_tables=torch.zeros(V, max(chunk // 16, 1), dtype=torch.int32))
+
+
+def test_chunked_local_plan_validation():
+    f = P.vllm_paged_chunked_local_plan
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, f, **_plan_args(dt=torch.int64))
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **{**_plan_args(), "chunk_size": 24})
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **{**_plan_args(), "chunk_size": 0})
+    a = _plan_args()
+    a["query_start_loc"] = torch.zeros(2, dtype=torch.int32)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **a)
+    a = _plan_args()
+    a["v_block_tables"] = torch.zeros(a["v_context_lens"].shape[0], 3, dtype=torch.int32)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **a)
+    a = _plan_args()
+    a["v_query_start_loc"] = a["v_query_start_loc"][:-1]
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **a)
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, f, **_plan_args())
+
+
+def _recycle_args(B=3, mb=5, window=0, chunk=32):
+    return dict(context_lens=torch.zeros(B, dtype=torch.int32),
+                block_tables=torch.zeros(B, mb, dtype=torch.int32), window=window, chunk_size=chunk,
+                freed_offsets=torch.zeros(B + 1, dtype=torch.int32),
+                freed_pages=torch.zeros(B * mb, dtype=torch.int32))
+
+
+def test_recycle_pages_validation():
+    f = P.vllm_paged_recycle_pages
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **_recycle_args(window=-1))
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **_recycle_args(chunk=40))
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **_recycle_args(chunk=-16))
+    a = _recycle_args()
+    a["freed_pages"] = a["freed_pages"][:-1]
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **a)
+    a = _recycle_args()
+    a["freed_offsets"] = a["freed_offsets"][:-1]
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, **a)
+    a = _recycle_args()
+    a["block_tables"] = a["block_tables"].long()
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, f, **a)
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, f, **_recycle_args())
+
+
+def test_empty_tensors_carry_any_strides():
+    # a 0-element tensor whose strides are not the contiguous ones is accepted
+    e = torch.empty_strided((0,), (0,), dtype=torch.int32)
+    d = _recycle_args(B=0)
+    d["context_lens"] = e
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_recycle_pages, **d)   # past the layout checks

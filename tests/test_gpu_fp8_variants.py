@@ -132,3 +132,26 @@ def test_e5m2_every_finite_code():
         assert np.all(err <= bound), (ctx, float(np.max(err - bound)))
         if ctx == 1:
             assert np.array_equal(bits(out[0, 0]), np.float16(ref[0, 0]).view(np.uint16))
+
+
+@pytest.mark.parametrize("kv", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_fp8_prefill(kv, qd, per_head):
+    """Chunked prefill over FP8 pools (per-tensor and per-kv-head scales)."""
+    ks = (0.05, 0.2, 0.03, 0.5, 0.08, 0.1, 0.02, 0.3) if per_head else 0.05
+    vs = (0.5, 0.05, 0.09, 0.02, 0.3, 0.07, 0.2, 0.04) if per_head else 0.07
+    case = make_case(4, seed=800 + per_head, B=4, qlen_range=(1, 300), cached_range=(0, 600),
+                     kv=kv, q=qd, kv_src=qd, k_scale=ks, v_scale=vs, window=0 if per_head else 200)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    q = case.q.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    P.vllm_paged_attn_prefill(out, q, pool_view(kc, kv), pool_view(vc, kv),
+                              case.block_tables.to(DEV), case.query_start_loc.to(DEV),
+                              case.context_lens.to(DEV), case.max_query_len, case.scale,
+                              case.window, k_scale=dev_scale(ks), v_scale=dev_scale(vs))
+    ref = A.prefill(raw_bits(case.q), qd, kp, vp, kv, case.block_tables.numpy(),
+                    case.query_start_loc.numpy(), case.context_lens.numpy(), case.scale,
+                    case.window, np.array(ks), np.array(vs))
+    assert_close(case, to_f64(out), ref)
