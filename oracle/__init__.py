@@ -18,10 +18,14 @@ inputs.  Modules:
 * ``attention`` -- paged decode and chunked-prefill attention over K/V
                    reassembled contiguously from the block tables, plus the
                    per-partition (max, sum, output) triples and their
-                   log-sum-exp combination.
+                   log-sum-exp combination; chunked-local attention, its
+                   virtual-batch plan and the dead pages of local attention.
+* ``block_manager`` -- the prefix-caching block manager that builds block
+                   tables and slot mappings: exact block-level trie behind
+                   a chain-hash index, reference counts, LRU leaf eviction.
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 brute force, library special cases, closed forms and invariants; none is left
 "parity unpinned".
 """
-from . import formats, scatter, attention  # noqa: F401
+from . import formats, scatter, attention, block_manager  # noqa: F401

@@ -76,3 +76,70 @@ def test_causal_mask_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(A, "prefill_mask", lambda n, Q, w: orig(n, Q, w) | np.eye(Q, n, k=n - Q + 1, dtype=bool))
     with pytest.raises(AssertionError):
         T.test_prefill_causal_perturbation()
+
+
+# ---- block manager ----------------------------------------------------------
+
+from oracle import block_manager as BM  # noqa: E402
+import test_oracle_block_manager as TB  # noqa: E402
+
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def _all_block_manager_pins():
+    yield TB.test_walkthrough
+    for seed, N, mb in [(1, 64, 16), (2, 40, 12), (3, 400, 24), (4, 24, 8)]:
+        yield lambda seed=seed, N=N, mb=mb: TB.test_random_streams_hold_the_pins(seed, N, mb)
+    yield TB.test_identical_prompts_in_one_batch_cache_once
+    yield TB.test_a_fully_cached_prompt_still_computes_its_last_token
+
+
+def _caught():
+    return any(_fails(f) for f in _all_block_manager_pins())
+
+
+def test_uncapped_hits_are_caught(monkeypatch):
+    monkeypatch.setattr(BM, "max_hit_blocks", lambda n: n // BM.BLOCK)
+    assert _caught()
+
+
+def test_lru_tie_break_towards_parents_is_caught(monkeypatch):
+    monkeypatch.setattr(BM.BlockManager, "eviction_key",
+                        lambda self, b: (int(self.ts[b]), int(self.depth[b]), b))
+    assert _caught()
+
+
+def test_lru_newest_first_is_caught(monkeypatch):
+    monkeypatch.setattr(BM.BlockManager, "eviction_key",
+                        lambda self, b: (-int(self.ts[b]), -int(self.depth[b]), b))
+    assert _caught()
+
+
+def test_release_of_cached_blocks_to_the_free_stack_is_caught(monkeypatch):
+    def release(self, block_tables, num_tokens, now):
+        bt = np.asarray(block_tables, np.int64)
+        for r, n in enumerate(np.asarray(num_tokens, np.int64)):
+            for j in range(BM.ceil_blocks(int(n))):
+                b = int(bt[r, j])
+                self.ref[b] = max(0, self.ref[b] - 1)
+                self.ts[b] = now
+                if self.ref[b] == 0:                     # also pushes cached blocks
+                    self.free.append(b)
+    monkeypatch.setattr(BM.BlockManager, "release", release)
+    assert _caught()
+
+
+def test_hash_without_the_digit_offset_is_caught(monkeypatch):
+    def chain_hash(parent_hash, block_tokens):
+        h = parent_hash
+        for t in block_tokens:
+            h = (h * BM.HASH_BASE + (int(t) & 0xFFFFFFFF)) & BM.MASK64   # digit t, not t + 1
+        return h
+    monkeypatch.setattr(BM, "chain_hash", chain_hash)
+    assert _fails(TB.test_chain_hash_is_the_prefix_polynomial)
