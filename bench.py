@@ -240,6 +240,61 @@ def bench_prefill(case, steps: int, warmup: int, chunk: int = 0) -> dict:
                          measured_traffic(case.name, ("prefill.hip", "common.h"))}}
 
 
+def bench_block_manager(steps: int = 20, num_seqs: int = 256, prompt: int = 1024,
+                        num_blocks: int = 65536) -> dict:
+    """The device block manager on a decode step: ``num_seqs`` running
+    sequences (admitted from shared-prefix prompts of ``prompt`` tokens) each
+    add one token per call.  HIP events around each call on an idle stream
+    include the host's argument checks; the kernel alone is in the
+    rocprofv3 summary."""
+    import numpy as np
+    import paged_kv_cache_183_amd as P
+    from workloads.requests import RequestStream
+    dev = torch.device("cuda", 0)
+    B, mb = num_seqs, (prompt + steps + 15) // 16 + 1
+    state = torch.zeros(P.vllm_block_manager_state_size(num_blocks), dtype=torch.uint8, device=dev)
+    P.vllm_block_manager_init(state, num_blocks)
+    rs = RequestStream(7, families=4, family_len=(prompt // 2, prompt // 2), vocab=32000)
+    prompts = [np.resize(np.array(rs.prompt(), np.int32), prompt) for _ in range(B)]
+    ws = torch.empty(P.vllm_block_manager_workspace_size(B, mb), dtype=torch.uint8, device=dev)
+    rows = torch.full((B, mb), -1, dtype=torch.int32, device=dev)
+    nc = torch.empty(B, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+    toks = d(np.concatenate(prompts))
+    tstart = d(np.arange(B + 1) * prompt)
+    slots = torch.empty(B * prompt, dtype=torch.int64, device=dev)
+    P.vllm_block_manager_schedule(state, num_blocks, toks, tstart, d(np.zeros(B)), tstart, rows,
+                                  slots, nc, status, 1, workspace=ws)
+    # every step's inputs are built before timing
+    gen = np.random.default_rng(8)
+    seqs = [p.tolist() for p in prompts]
+    inputs = []
+    for k in range(steps):
+        for sq in seqs:
+            sq.append(int(gen.integers(0, 32000)))
+        L = prompt + k + 1
+        inputs.append((d(np.concatenate(seqs)), d(np.arange(B + 1) * L), d(np.full(B, L - 1)),
+                       d(np.arange(B + 1)), torch.empty(B, dtype=torch.int64, device=dev)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms = []
+    for k, (tk, ts_, old, qsl, sl) in enumerate(inputs):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        P.vllm_block_manager_schedule(state, num_blocks, tk, ts_, old, qsl, rows, sl, nc, status,
+                                      2 + k, workspace=ws)
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+        assert int(status.item()) == 0
+    return {"workload": f"decode step: {B} running sequences of ~{prompt} tokens, "
+                        f"{num_blocks}-block pool", "bound": "latency",
+            "call_us_median": round(float(np.median(ms)) * 1e3, 1),
+            "note": "HIP events around each call on an idle stream (host argument checks "
+                    "included); kernel time in profiles/block_manager_decode_step_kernel_trace.txt"}
+
+
 def cpu_baseline(case, seconds: float) -> dict:
     """The fp64 oracle, unchanged, on this host: whole decode steps (cache
     write of the batch's new tokens + decode of every sequence) repeated for
@@ -293,6 +348,8 @@ def main():
                     help="decode a prefix-shared workload without reading the shared pages once")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill measurement appended to the decode line")
+    ap.add_argument("--block-manager-only", action="store_true",
+                    help="only time the device block manager on a decode step (one JSON line)")
     ap.add_argument("--chunk-size", type=int, default=0,
                     help="prefill workload: chunked-local attention of this chunk (plan + prefill)")
     ap.add_argument("--graph", action="store_true",
@@ -309,6 +366,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+    if args.block_manager_only:
+        print(json.dumps(bench_block_manager(steps=min(args.steps, 50))), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the hot path here is a single-GPU kernel "
@@ -447,7 +507,7 @@ def main():
         "vs_baseline": None,
         "dtype": case.kv_dtype,
         "data": "synthetic",
-        "config": {"workload": r["workload"], "num_seqs": case.num_seqs,
+        "config": {"workload": case.name, "num_seqs": case.num_seqs,
                    "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": 16,
                    "context_lens": cfg.get("ctx_range") or cfg.get("ctx_list"),
@@ -480,6 +540,8 @@ def main():
         # chunked-local attention (8192-token chunks) on the same batch
         res["chunked_local"] = bench_prefill(make_case(4), steps=min(args.steps, 20), warmup=3,
                                              chunk=args.chunk_size or 8192)
+        # the step before the path: block tables and slots from the device block manager
+        res["block_manager"] = bench_block_manager()
     print(json.dumps(res), flush=True)
 
 

@@ -323,6 +323,97 @@ vllm_status vllm_paged_recycle_pages(const vllm_tensor* context_lens, vllm_tenso
                                      vllm_tensor* freed_offsets, vllm_tensor* freed_pages,
                                      void* hip_stream);
 
+/*
+ * Prefix-caching KV block manager on the device: the step before the path,
+ * which fills block tables and slot mappings ("Building and Deploying
+ * vllm.cpp", Step 3, RadixTree prefix caching: radix matching over runs of
+ * physical blocks, zero-copy hits that bind a new sequence's table to
+ * existing pages, LRU eviction of the oldest leaves returning their blocks
+ * to the pool; the vllm.cpp repository listing, "What's implemented":
+ * hash-based prefix caching in the KV cache manager).
+ *
+ * The manager's whole state lives in one caller-owned device buffer of
+ * vllm_block_manager_state_size(num_blocks) bytes, set up by
+ * vllm_block_manager_init.  Cached prefixes form a trie with one node per
+ * full 16-token block, keyed by (parent block, its 16 token ids), behind a
+ * chain-hash index (Karp-Rabin polynomial hash of the whole prefix modulo
+ * 2^64; cached blocks carry distinct hashes, and a block whose hash is taken
+ * stays uncached).  Every call is stream-ordered and runs on the device;
+ * calls on one state must not overlap.
+ */
+size_t vllm_block_manager_state_size(int32_t num_blocks);   /* 0 if num_blocks is not in [1, 2^24] */
+
+/* Byte offsets inside the state of its regions, for inspection: [0] the
+ * int32 header (free-stack height, cached blocks, index tombstones,
+ * num_blocks, index slots), then free stack (int32, bottom first), ref
+ * (int32), last-access step (uint32), depth (int32), parent (int32), flags
+ * (int32, bit 0 = cached), chain hash (uint64), tokens (int32 x 16), index
+ * slots (int32: -1 empty, -2 tombstone, else a block), two per-call scratch
+ * arrays (int32); [12] the total size.  Returns the number written (<= n). */
+int32_t vllm_block_manager_state_layout(int32_t num_blocks, int64_t* offsets, int32_t n);
+
+/* Empty pool: all blocks free (the first allocations take 0, 1, 2, ...),
+ * nothing cached. */
+vllm_status vllm_block_manager_init(void* state, size_t state_bytes, int32_t num_blocks,
+                                    void* hip_stream);
+
+/* Scratch bytes of a schedule call (chain hashes and candidates per
+ * (request, block)). */
+size_t vllm_block_manager_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq);
+
+/*
+ * Admit or extend a batch of requests, in request order.  Request r holds
+ * old = num_computed[r] tokens in the cache (0: a new request) and adds
+ * q = query_start_loc[r+1] - query_start_loc[r] tokens; its token ids, all
+ * old + q of them, are token_ids[token_start[r] .. token_start[r+1]).
+ *  - A new request reuses the longest cached prefix of whole blocks, at most
+ *    floor((old + q - 1) / 16) blocks so that one token is computed; lookups
+ *    see the index as it stood before the call.  Reused blocks gain a
+ *    reference.
+ *  - Missing blocks are popped from the free stack (request order, block
+ *    order).  When too few are free, unreferenced cached blocks are evicted
+ *    in (last access, deeper first, lower id) order -- only leaves -- and
+ *    pushed in increasing id order first.
+ *  - Blocks that become full are cached, request by request; a request
+ *    stops caching at the first block whose hash is already taken.
+ *  - block_tables[r, ceil(old/16) ..) is written; entries before are read.
+ *  - slot_mapping[query_start_loc[r] + i] = slot of token old + i (block *
+ *    16 + offset), or -1 for tokens served by the cache (the cache write
+ *    skips negative slots); num_cached_tokens[r] = max(old, 16 * reused).
+ *  - Blocks touched (reused or allocated) get last access = now.
+ * status[0] (device) = 0 done, 1 not enough free plus evictable blocks, 2
+ * metadata that do not fit (old < 0, q < 0, a token count that is not
+ * old + q, a row too short, an existing entry outside [0, num_blocks),
+ * offsets outside the arrays); with 1 or 2 nothing changes.
+ *   token_ids [T] I32; token_start, query_start_loc [B + 1] I32;
+ *   num_computed [B] I32; block_tables [B, max_blocks_per_seq] I32;
+ *   slot_mapping [sum q] I64; num_cached_tokens [B] I32; status [1] I32.
+ *   B <= 2048.  workspace: null (allocated on the stream) or at least
+ *   vllm_block_manager_workspace_size(B, max_blocks_per_seq) bytes.
+ */
+vllm_status vllm_block_manager_schedule(void* state, int32_t num_blocks,
+                                        const vllm_tensor* token_ids,
+                                        const vllm_tensor* token_start,
+                                        const vllm_tensor* num_computed,
+                                        const vllm_tensor* query_start_loc,
+                                        vllm_tensor* block_tables, vllm_tensor* slot_mapping,
+                                        vllm_tensor* num_cached_tokens, vllm_tensor* status,
+                                        uint32_t now, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream);
+
+/*
+ * Sequences end: each block of row r's first ceil(num_tokens[r] / 16)
+ * entries loses one reference and gets last access = now; blocks that are
+ * not cached go back on the free stack (request order, block order), cached
+ * ones stay in the index, evictable once unreferenced.  Entries outside
+ * [0, num_blocks) are skipped.  B <= 2048.
+ *   block_tables [B, max_blocks_per_seq] I32; num_tokens [B] I32.
+ */
+vllm_status vllm_block_manager_release(void* state, int32_t num_blocks,
+                                       const vllm_tensor* block_tables,
+                                       const vllm_tensor* num_tokens, uint32_t now,
+                                       void* hip_stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

@@ -16,6 +16,12 @@ from .binding import (  # noqa: F401
     vllm_paged_attn_shared_prefix_workspace_size,
     vllm_paged_attn_workspace_size, vllm_paged_attn_decode_shared_prefix,
     vllm_paged_attn_shared_prefix_workspace_size,
+    vllm_block_manager_init,
+    vllm_block_manager_release,
+    vllm_block_manager_schedule,
+    vllm_block_manager_state_layout,
+    vllm_block_manager_state_size,
+    vllm_block_manager_workspace_size,
     vllm_paged_cache_write,
     vllm_paged_chunked_local_plan,
     vllm_paged_chunked_local_virtual_count,

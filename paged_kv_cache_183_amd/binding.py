@@ -34,7 +34,10 @@ EXPORTED = ["vllm_abi_version", "vllm_last_error", "vllm_paged_cache_write",
             "vllm_paged_attn_decode", "vllm_paged_attn_workspace_size",
             "vllm_paged_attn_decode_shared_prefix", "vllm_paged_attn_shared_prefix_workspace_size",
             "vllm_paged_attn_prefill", "vllm_paged_chunked_local_plan",
-            "vllm_paged_chunked_local_virtual_count", "vllm_paged_recycle_pages"]
+            "vllm_paged_chunked_local_virtual_count", "vllm_paged_recycle_pages",
+            "vllm_block_manager_state_size", "vllm_block_manager_state_layout",
+            "vllm_block_manager_init", "vllm_block_manager_workspace_size",
+            "vllm_block_manager_schedule", "vllm_block_manager_release"]
 
 
 class VllmTensor(ctypes.Structure):
@@ -88,6 +91,23 @@ def _load():
     lib.vllm_paged_recycle_pages.restype = ctypes.c_int
     lib.vllm_paged_recycle_pages.argtypes = [T, T, ctypes.c_int32, ctypes.c_int32, T, T,
                                              ctypes.c_void_p]
+    lib.vllm_block_manager_state_size.restype = ctypes.c_size_t
+    lib.vllm_block_manager_state_size.argtypes = [ctypes.c_int32]
+    lib.vllm_block_manager_state_layout.restype = ctypes.c_int32
+    lib.vllm_block_manager_state_layout.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                                    ctypes.c_int32]
+    lib.vllm_block_manager_init.restype = ctypes.c_int
+    lib.vllm_block_manager_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                            ctypes.c_void_p]
+    lib.vllm_block_manager_workspace_size.restype = ctypes.c_size_t
+    lib.vllm_block_manager_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.vllm_block_manager_schedule.restype = ctypes.c_int
+    lib.vllm_block_manager_schedule.argtypes = ([ctypes.c_void_p, ctypes.c_int32] + [T] * 8 +
+                                                [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t,
+                                                 ctypes.c_void_p])
+    lib.vllm_block_manager_release.restype = ctypes.c_int
+    lib.vllm_block_manager_release.argtypes = [ctypes.c_void_p, ctypes.c_int32, T, T,
+                                               ctypes.c_uint32, ctypes.c_void_p]
     return lib
 
 
@@ -245,3 +265,45 @@ def vllm_paged_recycle_pages(context_lens, block_tables, window, chunk_size, fre
                                         ctypes.c_int32(chunk_size),
                                         *[ctypes.byref(a) for a in outs],
                                         ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_block_manager_state_size(num_blocks) -> int:
+    return int(LIB.vllm_block_manager_state_size(num_blocks))
+
+
+def vllm_block_manager_state_layout(num_blocks) -> list:
+    """Byte offsets of the state's regions (header first) and its size."""
+    buf = (ctypes.c_int64 * 16)()
+    n = LIB.vllm_block_manager_state_layout(num_blocks, buf, 16)
+    return [int(buf[i]) for i in range(n)]
+
+
+def vllm_block_manager_init(state, num_blocks, stream=None) -> None:
+    """state: a device tensor of at least vllm_block_manager_state_size bytes."""
+    _check(LIB.vllm_block_manager_init(ctypes.c_void_p(state.data_ptr()),
+                                       state.numel() * state.element_size(), num_blocks,
+                                       ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_block_manager_workspace_size(num_seqs, max_blocks_per_seq) -> int:
+    return int(LIB.vllm_block_manager_workspace_size(num_seqs, max_blocks_per_seq))
+
+
+def vllm_block_manager_schedule(state, num_blocks, token_ids, token_start, num_computed,
+                                query_start_loc, block_tables, slot_mapping, num_cached_tokens,
+                                status, now, workspace=None, stream=None) -> None:
+    args = [tensor_desc(x) for x in (token_ids, token_start, num_computed, query_start_loc,
+                                     block_tables, slot_mapping, num_cached_tokens, status)]
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(LIB.vllm_block_manager_schedule(ctypes.c_void_p(state.data_ptr()), num_blocks,
+                                           *[ctypes.byref(a) for a in args], ctypes.c_uint32(now),
+                                           ws, wsb, ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_block_manager_release(state, num_blocks, block_tables, num_tokens, now,
+                               stream=None) -> None:
+    args = [tensor_desc(x) for x in (block_tables, num_tokens)]
+    _check(LIB.vllm_block_manager_release(ctypes.c_void_p(state.data_ptr()), num_blocks,
+                                          *[ctypes.byref(a) for a in args], ctypes.c_uint32(now),
+                                          ctypes.c_void_p(_stream(stream))))

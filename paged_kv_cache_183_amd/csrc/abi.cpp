@@ -748,4 +748,151 @@ vllm_status vllm_paged_recycle_pages(const vllm_tensor* context_lens, vllm_tenso
   return ok();
 }
 
+size_t vllm_block_manager_state_size(int32_t num_blocks) {
+  if (num_blocks < 1 || num_blocks > (1 << 24)) return 0;
+  return (size_t)vp::bm_layout(num_blocks).bytes;
+}
+
+int32_t vllm_block_manager_state_layout(int32_t num_blocks, int64_t* offsets, int32_t n) {
+  if (num_blocks < 1 || num_blocks > (1 << 24) || !offsets || n <= 0) return 0;
+  const vp::BmLayout L = vp::bm_layout(num_blocks);
+  int64_t all[vp::kBmRegions + 2];
+  all[0] = 0;
+  for (int i = 0; i < vp::kBmRegions; ++i) all[i + 1] = L.off[i];
+  all[vp::kBmRegions + 1] = L.bytes;
+  const int32_t m = std::min<int32_t>(n, vp::kBmRegions + 2);
+  for (int i = 0; i < m; ++i) offsets[i] = all[i];
+  return m;
+}
+
+namespace {
+vllm_status check_bm_state(void* state, size_t state_bytes, int32_t num_blocks) {
+  if (num_blocks < 1 || num_blocks > (1 << 24))
+    return fail(VLLM_ERR_INVALID_ARG, "num_blocks %d outside [1, 2^24]", (int)num_blocks);
+  if (!state) return fail(VLLM_ERR_INVALID_ARG, "state: null pointer");
+  if (state_bytes < (size_t)vp::bm_layout(num_blocks).bytes)
+    return fail(VLLM_ERR_INVALID_ARG, "state of %zu bytes, %lld needed", state_bytes,
+                (long long)vp::bm_layout(num_blocks).bytes);
+  VP_TRY(check_align(state, "state", 256));
+  return check_device_ptr(state, "state");
+}
+}  // namespace
+
+vllm_status vllm_block_manager_init(void* state, size_t state_bytes, int32_t num_blocks,
+                                    void* hip_stream) {
+  VP_TRY(check_bm_state(state, state_bytes, num_blocks));
+  VP_TRY(hip_status(vp::launch_bm_init(vp::bm_state(state, num_blocks), (hipStream_t)hip_stream),
+                    "block manager init launch"));
+  return ok();
+}
+
+size_t vllm_block_manager_workspace_size(int32_t num_seqs, int32_t max_blocks_per_seq) {
+  if (num_seqs < 0 || num_seqs > vp::kBmMaxSeqs || max_blocks_per_seq < 0) return 0;
+  return vp::bm_workspace_bytes(num_seqs, max_blocks_per_seq);
+}
+
+vllm_status vllm_block_manager_schedule(void* state, int32_t num_blocks,
+                                        const vllm_tensor* token_ids,
+                                        const vllm_tensor* token_start,
+                                        const vllm_tensor* num_computed,
+                                        const vllm_tensor* query_start_loc,
+                                        vllm_tensor* block_tables, vllm_tensor* slot_mapping,
+                                        vllm_tensor* num_cached_tokens, vllm_tensor* status,
+                                        uint32_t now, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream) {
+  VP_TRY(check_tensor(token_ids, "token_ids", 1));
+  VP_TRY(check_tensor(token_start, "token_start", 1));
+  VP_TRY(check_tensor(num_computed, "num_computed", 1));
+  VP_TRY(check_tensor(query_start_loc, "query_start_loc", 1));
+  VP_TRY(check_tensor(block_tables, "block_tables", 2));
+  VP_TRY(check_tensor(slot_mapping, "slot_mapping", 1));
+  VP_TRY(check_tensor(num_cached_tokens, "num_cached_tokens", 1));
+  VP_TRY(check_tensor(status, "status", 1));
+  for (const vllm_tensor* x : {token_ids, token_start, num_computed, query_start_loc,
+                               (const vllm_tensor*)block_tables, (const vllm_tensor*)num_cached_tokens,
+                               (const vllm_tensor*)status})
+    if (x->dtype != VLLM_DTYPE_I32) return fail(VLLM_ERR_UNSUPPORTED, "block manager metadata must be I32");
+  VP_TRY(check_dtype(slot_mapping, "slot_mapping", VLLM_DTYPE_I64));
+  const int64_t B = num_computed->shape[0], mb = block_tables->shape[1];
+  if (token_start->shape[0] != B + 1 || query_start_loc->shape[0] != B + 1 ||
+      block_tables->shape[0] != B || num_cached_tokens->shape[0] != B || status->shape[0] != 1)
+    return fail(VLLM_ERR_INVALID_ARG,
+                "token_start and query_start_loc need %lld entries, block_tables and "
+                "num_cached_tokens %lld rows, status 1 entry", (long long)(B + 1), (long long)B);
+  if (B > vp::kBmMaxSeqs || mb > 65535 || token_ids->shape[0] > INT32_MAX ||
+      slot_mapping->shape[0] > INT32_MAX)
+    return fail(VLLM_ERR_UNSUPPORTED, "batch above %d requests or rows above 65535 blocks",
+                vp::kBmMaxSeqs);
+  VP_TRY(check_bm_state(state, ~(size_t)0, num_blocks));
+  const size_t need = vp::bm_workspace_bytes((int32_t)B, (int32_t)mb);
+  if (workspace && workspace_bytes < need)
+    return fail(VLLM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (workspace) VP_TRY(check_align(workspace, "workspace", 256));
+  VP_TRY(check_data(token_ids, "token_ids", 4));
+  VP_TRY(check_data(token_start, "token_start", 4));
+  VP_TRY(check_data(num_computed, "num_computed", 4));
+  VP_TRY(check_data(query_start_loc, "query_start_loc", 4));
+  VP_TRY(check_data(block_tables, "block_tables", 4));
+  VP_TRY(check_data(slot_mapping, "slot_mapping", 8));
+  VP_TRY(check_data(num_cached_tokens, "num_cached_tokens", 4));
+  VP_TRY(check_data(status, "status", 4));
+  hipStream_t stream = (hipStream_t)hip_stream;
+  void* ws = workspace;
+  if (!ws && need > 0) VP_TRY(hip_status(hipMallocAsync(&ws, need, stream), "workspace hipMallocAsync"));
+  vp::BmScheduleParams p{};
+  p.st = vp::bm_state(state, num_blocks);
+  p.token_ids = static_cast<const int32_t*>(token_ids->data);
+  p.token_start = static_cast<const int32_t*>(token_start->data);
+  p.num_computed = static_cast<const int32_t*>(num_computed->data);
+  p.query_start_loc = static_cast<const int32_t*>(query_start_loc->data);
+  p.block_tables = static_cast<int32_t*>(block_tables->data);
+  p.slot_mapping = static_cast<int64_t*>(slot_mapping->data);
+  p.num_cached = static_cast<int32_t*>(num_cached_tokens->data);
+  p.status = static_cast<int32_t*>(status->data);
+  const int64_t items = B * mb;
+  p.ws_hash = static_cast<uint64_t*>(ws);
+  p.ws_cand = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + (8 * items + 255) / 256 * 256);
+  p.num_token_ids = token_ids->shape[0];
+  p.num_seqs = (int32_t)B;
+  p.mb = (int32_t)mb;
+  p.sum_q = (int32_t)slot_mapping->shape[0];
+  p.now = now;
+  hipError_t e = vp::launch_bm_schedule(p, stream);
+  if (!workspace && ws) {
+    const hipError_t e2 = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = e2;
+  }
+  VP_TRY(hip_status(e, "block manager schedule launch"));
+  return ok();
+}
+
+vllm_status vllm_block_manager_release(void* state, int32_t num_blocks,
+                                       const vllm_tensor* block_tables,
+                                       const vllm_tensor* num_tokens, uint32_t now,
+                                       void* hip_stream) {
+  VP_TRY(check_tensor(block_tables, "block_tables", 2));
+  VP_TRY(check_tensor(num_tokens, "num_tokens", 1));
+  if (block_tables->dtype != VLLM_DTYPE_I32 || num_tokens->dtype != VLLM_DTYPE_I32)
+    return fail(VLLM_ERR_UNSUPPORTED, "block manager metadata must be I32");
+  const int64_t B = num_tokens->shape[0];
+  if (block_tables->shape[0] != B)
+    return fail(VLLM_ERR_INVALID_ARG, "block_tables must have %lld rows", (long long)B);
+  if (B > vp::kBmMaxSeqs || block_tables->shape[1] > 65535)
+    return fail(VLLM_ERR_UNSUPPORTED, "batch above %d requests or rows above 65535 blocks",
+                vp::kBmMaxSeqs);
+  VP_TRY(check_bm_state(state, ~(size_t)0, num_blocks));
+  if (B == 0) return ok();
+  VP_TRY(check_data(block_tables, "block_tables", 4));
+  VP_TRY(check_data(num_tokens, "num_tokens", 4));
+  vp::BmReleaseParams p{};
+  p.st = vp::bm_state(state, num_blocks);
+  p.block_tables = static_cast<const int32_t*>(block_tables->data);
+  p.num_tokens = static_cast<const int32_t*>(num_tokens->data);
+  p.num_seqs = (int32_t)B;
+  p.mb = (int32_t)block_tables->shape[1];
+  p.now = now;
+  VP_TRY(hip_status(vp::launch_bm_release(p, (hipStream_t)hip_stream), "block manager release launch"));
+  return ok();
+}
+
 }  // extern "C"

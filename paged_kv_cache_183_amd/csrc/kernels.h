@@ -152,6 +152,70 @@ struct RecycleParams {
 
 hipError_t launch_recycle_pages(const RecycleParams& p, hipStream_t stream);
 
+// ---- prefix-caching block manager -------------------------------------------
+// State of a pool of N blocks, one device buffer (regions 256-byte aligned, in
+// this order after a 256-byte header of int32: free count, cached count,
+// tombstones, N, table capacity).
+enum BmRegion { kBmFree, kBmRef, kBmTs, kBmDepth, kBmParent, kBmFlags, kBmHash, kBmTokens,
+                kBmTable, kBmMark, kBmOwner, kBmRegions };
+struct BmLayout {
+  int64_t off[kBmRegions];
+  int64_t bytes;
+  int32_t cap;                      // table slots (a power of two >= 2N)
+};
+BmLayout bm_layout(int32_t num_blocks);
+
+struct BmState {
+  int32_t* hdr;
+  int32_t* free_stack;   // [N], top at hdr[0] - 1
+  int32_t* ref;          // [N]
+  uint32_t* ts;          // [N]
+  int32_t* depth;        // [N]
+  int32_t* parent;       // [N]
+  int32_t* flags;        // [N] bit 0: cached
+  uint64_t* chash;       // [N] chain hash of a cached block's whole prefix
+  int32_t* tokens;       // [N, 16]
+  int32_t* table;        // [cap] -1 empty, -2 tombstone, else a cached block
+  int32_t* mark;         // [N] per-call scratch
+  int32_t* owner;        // [N] per-call scratch
+  int32_t num_blocks;
+  int32_t cap;
+};
+BmState bm_state(void* base, int32_t num_blocks);
+
+struct BmScheduleParams {
+  BmState st;
+  const int32_t* token_ids;
+  const int32_t* token_start;    // [B + 1]
+  const int32_t* num_computed;   // [B]
+  const int32_t* query_start_loc;  // [B + 1]
+  int32_t* block_tables;         // [B, mb]
+  int64_t* slot_mapping;         // [sum_q]
+  int32_t* num_cached;           // [B]
+  int32_t* status;               // [1]
+  uint64_t* ws_hash;             // [B * mb] chain hashes
+  int32_t* ws_cand;              // [B * mb] lookup candidates, then claimed slots
+  int64_t num_token_ids;
+  int32_t num_seqs;
+  int32_t mb;
+  int32_t sum_q;
+  uint32_t now;
+};
+constexpr int kBmMaxSeqs = 2048;
+size_t bm_workspace_bytes(int32_t num_seqs, int32_t mb);
+hipError_t launch_bm_init(const BmState& st, hipStream_t stream);
+hipError_t launch_bm_schedule(const BmScheduleParams& p, hipStream_t stream);
+
+struct BmReleaseParams {
+  BmState st;
+  const int32_t* block_tables;   // [B, mb]
+  const int32_t* num_tokens;     // [B]
+  int32_t num_seqs;
+  int32_t mb;
+  uint32_t now;
+};
+hipError_t launch_bm_release(const BmReleaseParams& p, hipStream_t stream);
+
 // Decode work split: at most this many waves, each taking at least
 // kMinChunkPages pages when the chunk size is automatic.
 constexpr int kMaxWorkers = 4096;

@@ -223,3 +223,63 @@ def test_empty_tensors_carry_any_strides():
     d = _recycle_args(B=0)
     d["context_lens"] = e
     _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_recycle_pages, **d)   # past the layout checks
+
+
+def test_block_manager_sizes_and_layout():
+    assert P.vllm_block_manager_state_size(0) == 0
+    assert P.vllm_block_manager_state_size((1 << 24) + 1) == 0
+    lay = P.vllm_block_manager_state_layout(100)
+    assert len(lay) == 13 and lay[0] == 0
+    assert all(b > a for a, b in zip(lay, lay[1:])) and all(x % 256 == 0 for x in lay)
+    assert lay[-1] == P.vllm_block_manager_state_size(100)
+    # tokens region holds 16 int32 per block; the index has >= 2N slots (a power of two)
+    assert lay[9] - lay[8] >= 100 * 16 * 4
+    assert lay[10] - lay[9] >= 256 * 4
+    assert P.vllm_block_manager_workspace_size(3, 10) == (3 * 10 * 8 + 255) // 256 * 256 + 256
+    assert P.vllm_block_manager_workspace_size(4096, 10) == 0
+
+
+def _bm_args(B=2, mb=4, dt=torch.int32):
+    return dict(token_ids=torch.zeros(10, dtype=dt), token_start=torch.zeros(B + 1, dtype=dt),
+                num_computed=torch.zeros(B, dtype=dt), query_start_loc=torch.zeros(B + 1, dtype=dt),
+                block_tables=torch.zeros(B, mb, dtype=dt), slot_mapping=torch.zeros(10, dtype=torch.int64),
+                num_cached_tokens=torch.zeros(B, dtype=dt), status_out=torch.zeros(1, dtype=dt))
+
+
+def _schedule(state, num_blocks, status_out, **kw):
+    return P.vllm_block_manager_schedule(state, num_blocks, status=status_out, **kw)
+
+
+def _aligned_bytes(n, a=256):
+    raw = torch.zeros(n + a, dtype=torch.uint8)
+    off = (-raw.data_ptr()) % a
+    return raw[off:off + n]
+
+
+def test_block_manager_validation():
+    st = _aligned_bytes(P.vllm_block_manager_state_size(8))
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_block_manager_init, _aligned_bytes(4096)[1:], 8)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_block_manager_init, st, 0)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_block_manager_init, st[:100], 8)
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_block_manager_init, st, 8)
+    f = _schedule
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, f, st, 8, **_bm_args(dt=torch.int64), now=1)
+    a = _bm_args()
+    a["slot_mapping"] = a["slot_mapping"].int()
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, f, st, 8, **a, now=1)
+    a = _bm_args()
+    a["token_start"] = a["token_start"][:-1]
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, st, 8, **a, now=1)
+    a = _bm_args()
+    a["status_out"] = torch.zeros(2, dtype=torch.int32)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, st, 8, **a, now=1)
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, f, st, 8, **_bm_args(B=2049), now=1)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, f, st, 0, **_bm_args(), now=1)
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, f, st, 8, **_bm_args(), now=1)
+    g = P.vllm_block_manager_release
+    _expect(Bd.VLLM_ERR_INVALID_ARG, g, st, 8, torch.zeros(3, 4, dtype=torch.int32),
+            torch.zeros(2, dtype=torch.int32), 1)
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, g, st, 8, torch.zeros(2, 4, dtype=torch.int64),
+            torch.zeros(2, dtype=torch.int32), 1)
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, g, st, 8, torch.zeros(2, 4, dtype=torch.int32),
+            torch.zeros(2, dtype=torch.int32), 1)
