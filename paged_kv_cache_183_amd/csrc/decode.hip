@@ -184,27 +184,40 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int s) {
 }
 
 // Exclusive prefix of np(s) over the batch, computed by one workgroup of
-// kNW * 64 threads into pre[0 .. B] (pre[B] = total).
+// kNW * 64 threads into pre[0 .. B] (pre[B] = total): each thread sums a
+// run of sequences, the runs are scanned within each wave with lane
+// shuffles, then across the kNW wave totals.
 __device__ void page_prefix(const DecodeParams& p, int* pre) {
-  __shared__ int s_tot[kNW * 64];
+  __shared__ int s_wave[kNW];
+  __shared__ int s_total;
   const int B = p.num_seqs;
   const int nt = kNW * 64;
   const int per = (B + nt - 1) / nt;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   int sum = 0;
   for (int i = 0; i < per; ++i) {
     const int s = t * per + i;
     if (s < B) sum += seq_range(p, s).np;
   }
-  s_tot[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {       // inclusive Hillis-Steele scan
-    const int v = t >= off ? s_tot[t - off] : 0;
-    __syncthreads();
-    s_tot[t] += v;
-    __syncthreads();
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
   }
-  int run = t > 0 ? s_tot[t - 1] : 0;
+  if (lane == 63) s_wave[w] = incl;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < kNW; ++i) {
+      const int x = s_wave[i];
+      s_wave[i] = run;
+      run += x;
+    }
+    s_total = run;
+  }
+  __syncthreads();
+  int run = s_wave[w] + incl - sum;
   for (int i = 0; i < per; ++i) {
     const int s = t * per + i;
     if (s < B) {
@@ -212,13 +225,9 @@ __device__ void page_prefix(const DecodeParams& p, int* pre) {
       run += seq_range(p, s).np;
     }
   }
-  if (t == nt - 1) pre[B] = s_tot[t];
+  if (t == 0) pre[B] = s_total;
   __syncthreads();
 }
-
-// Waves per SIMD the decode kernel is compiled for (caps its registers).
-template <int G>
-constexpr int kWavesPerSimd = G <= 4 ? 4 : (G <= 6 ? 3 : 2);
 
 template <int D, int G, int KF, int QF, int LPR, int PD>
 __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {

@@ -121,7 +121,7 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int 
 hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
                                 hipStream_t stream);
 // Pages per split of the shared-prefix pass.
-constexpr int kPrefixSplitPages = 16;
+constexpr int kPrefixSplitPages = 32;
 
 struct LocalPlanParams {
   const int32_t* query_start_loc;  // [B + 1]
