@@ -197,7 +197,10 @@ size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * "Building and Deploying vllm.cpp", Step 3).  Those pages are read from
  * sequence 0's table (the other sequences' first shared_pages entries are not
  * read) once per kv-head for the whole batch: every sequence's query is
- * scored against them together on the matrix cores, in splits of 32 pages.
+ * scored against them together on the matrix cores, in splits of 32 pages,
+ * on a second stream that the library owns (default priority, one per
+ * device, created on first use) forked from hip_stream and joined back to it
+ * before the merge, so the call stays ordered on hip_stream.
  * The rest of each sequence is decoded as usual, and the parts are merged with
  * the log-sum-exp rule.  Keys of the shared pages are kept per sequence as in
  * decode: t < n (a sequence shorter than the prefix uses its first n tokens)

@@ -13,6 +13,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -132,6 +134,32 @@ vllm_status check_data(const vllm_tensor* t, const char* name, uintptr_t align) 
 vllm_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return VLLM_OK;
   return fail(VLLM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A second stream per device, with a fork and a join event: the shared-prefix
+// pass (matrix cores) runs on it beside the suffix decode (memory bound) of
+// the same call.  Default priority; created on first use and kept for the
+// life of the process.  The mutex keeps each fork/launch/join sequence whole
+// when several host threads call at once.
+struct AuxStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_aux_mu;
+std::map<int, AuxStream> g_aux;
+
+hipError_t aux_stream(AuxStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  AuxStream& a = g_aux[dev];
+  if (!a.stream) {
+    if ((e = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &a;
+  return hipSuccess;
 }
 
 int fmt_of(int32_t d) {
@@ -487,8 +515,8 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   p.ws_l = reinterpret_cast<float*>(base + dp.l_off);
   p.ws_spare = base + dp.spare_off;
   hipError_t e = hipSuccess;
+  vp::PrefillParams sp{};
   if (shared_pages > 0) {
-    vp::PrefillParams sp{};
     sp.q = q->data;
     sp.k_cache = k_cache->data;
     sp.v_cache = v_cache->data;
@@ -510,7 +538,6 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
     sp.pfx_o = reinterpret_cast<float*>(base + dp.po_off);
     sp.pfx_m = reinterpret_cast<float*>(base + dp.pm_off);
     sp.pfx_l = reinterpret_cast<float*>(base + dp.pl_off);
-    e = vp::launch_shared_prefix(sp, (int)D, kv_fmt, q_fmt, stream);
     p.skip_tokens = shared_pages * 16;
     p.num_splits = dp.num_splits;
     p.pfx_o = sp.pfx_o;
@@ -520,7 +547,23 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
     p.ws_um = reinterpret_cast<float*>(base + dp.um_off);
     p.ws_ul = reinterpret_cast<float*>(base + dp.ul_off);
   }
-  if (e == hipSuccess) e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
+  if (shared_pages == 0) {
+    e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
+  } else {
+    // Fork: the suffix decode goes first on the caller's stream, the prefix
+    // pass on the second stream fills the CUs as decode waves finish; the
+    // merge waits for both.
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    AuxStream* ax = nullptr;
+    e = aux_stream(&ax);
+    if (e == hipSuccess) e = hipEventRecord(ax->fork, stream);
+    if (e == hipSuccess) e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream, /*split=*/true);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ax->stream, ax->fork, 0);
+    if (e == hipSuccess) e = vp::launch_shared_prefix(sp, (int)D, kv_fmt, q_fmt, ax->stream);
+    if (e == hipSuccess) e = hipEventRecord(ax->join, ax->stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ax->join, 0);
+    if (e == hipSuccess) e = vp::launch_decode_merge(p, (int)D, q_fmt, stream);
+  }
   if (owned) {
     hipError_t e2 = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = e2;

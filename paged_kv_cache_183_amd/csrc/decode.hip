@@ -821,7 +821,8 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
   return (int)((w + kNW - 1) / kNW * kNW);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream,
+                         bool split) {
   if (p.num_seqs == 0) return hipSuccess;
   const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, p.head_chunk);
   const void* mk = merge_kernel_for(head_dim, q_fmt, p.head_chunk);
@@ -834,7 +835,16 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_
     if (e != hipSuccess) return e;
   }
   hipError_t e = hipLaunchKernel(k, dim3(p.num_workers / kNW), dim3(kNW * 64), args, 0, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || split) return e;
+  return launch_decode_merge(p, head_dim, q_fmt, stream);
+}
+
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int q_fmt, hipStream_t stream) {
+  if (p.num_seqs == 0) return hipSuccess;
+  const void* mk = merge_kernel_for(head_dim, q_fmt, p.head_chunk);
+  if (!mk) return hipErrorInvalidValue;
+  DecodeParams a = p;
+  void* args[] = {&a};
   const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * (p.group / p.head_chunk);
   const int64_t slices = (p.head_chunk * head_dim + kMergeThreads - 1) / kMergeThreads;
   return hipLaunchKernel(mk, dim3((unsigned)(units * slices)), dim3(kMergeThreads), args, 0, stream);

@@ -77,9 +77,13 @@ struct DecodeParams {
   const float* pfx_l;
 };
 
-// kv_fmt: kF16 / kBF16 / kE4M3 / kE5M2; q_fmt: kF16 / kBF16.
+// kv_fmt: kF16 / kBF16 / kE4M3 / kE5M2; q_fmt: kF16 / kBF16.  Launches the
+// decode kernel, then the merge; with split = true only the decode kernel
+// (launch_decode_merge then follows, once the partials it also reads --
+// from work on another stream -- are ordered before it).
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt,
-                         hipStream_t stream);
+                         hipStream_t stream, bool split = false);
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int q_fmt, hipStream_t stream);
 
 struct PrefillParams {
   const void* q;               // [sumQ, Hq, D]
