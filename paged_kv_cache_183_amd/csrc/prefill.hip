@@ -250,9 +250,9 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   };
   // Loads are unconditional (rows at or past n_valid are replaced by zeros
   // when written to LDS) so that nothing waits on them before the LDS write.
-  auto fetch = [&](RawT (&kr)[2], RawT (&vr)[2], int kb) __attribute__((always_inline)) {
-    const int j0 = kb >> 4;
-    const int64_t pa = (int64_t)page_blk(j0) * blk_stride, pb = (int64_t)page_blk(j0 + 1) * blk_stride;
+  // (the two block ids of a block are read one block ahead of its K/V)
+  auto fetch = [&](RawT (&kr)[2], RawT (&vr)[2], int ida, int idb) __attribute__((always_inline)) {
+    const int64_t pa = (int64_t)ida * blk_stride, pb = (int64_t)idb * blk_stride;
     kr[0] = *reinterpret_cast<const RawT*>(kpool + pa + k_off);
     kr[1] = *reinterpret_cast<const RawT*>(kpool + pb + k_off);
     const uint8_t* vp = vpool + (v_pgB ? pb : pa) + v_off;
@@ -367,14 +367,19 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   // accumulators in place; unrolling by two made the compiler copy them.)
   RawT kr[2], vr[2];
   auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
+  int ida = 0, idb = 0;                        // block ids of the block fetched next
   if (nblk > 0) {
-    fetch(kr, vr, kb_of(0));
+    fetch(kr, vr, page_blk(kb_of(0) >> 4), page_blk((kb_of(0) >> 4) + 1));
     stage(0, kr, vr, kb_of(0));
+    ida = page_blk(kb_of(1) >> 4);
+    idb = page_blk((kb_of(1) >> 4) + 1);
   }
   __syncthreads();
   for (int bi = 0; bi < nblk; ++bi) {
     const int buf = bi & 1;
-    fetch(kr, vr, kb_of(bi + 1));              // (past the end: re-reads the last block)
+    fetch(kr, vr, ida, idb);                   // (past the end: re-reads the last block)
+    ida = page_blk(kb_of(bi + 2) >> 4);
+    idb = page_blk((kb_of(bi + 2) >> 4) + 1);
     __builtin_amdgcn_sched_barrier(0);
     block(buf, kb0 + bi * kBK);
     __builtin_amdgcn_sched_barrier(0);
