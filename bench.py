@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 from workloads import CONFIGS, ELEM_BYTES, make_case, raw_bits  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+EVENT_EVERY = 4          # decode steps per timed sample of the decode call
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 matrix-core peak of MI355X
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + seqs/s"
 PREFILL_METRIC = "chunked-prefill paged attention: TFLOP/s (% bf16 MFMA peak) + tokens/s"
@@ -348,6 +349,8 @@ def main():
                     help="decode a prefix-shared workload without reading the shared pages once")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill measurement appended to the decode line")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="decode step as two calls (cache write, then decode) instead of the fused one")
     ap.add_argument("--block-manager-only", action="store_true",
                     help="only time the device block manager on a decode step (one JSON line)")
     ap.add_argument("--chunk-size", type=int, default=0,
@@ -423,14 +426,25 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    # The step's cache write goes into the decode call (same result bit for
+    # bit: vllm_paged_attn_decode_append) unless asked to run the two calls
+    # separately; the shared-prefix decode has no fused form.
+    fused = not (args.separate_write or shared_pages)
+
     def write(r):
+        if fused:
+            return
         kc, vc = pools[r]
         P.vllm_paged_cache_write(new_k, new_v, new_slots, view(kc), view(vc),
                                  k_scale=case.k_scale, v_scale=case.v_scale)
 
     def decode(r):
         kc, vc = pools[r]
-        if shared_pages:
+        if fused:
+            P.vllm_paged_attn_decode_append(out, q, new_k, new_v, new_slots, view(kc), view(vc), bt,
+                                            ctx, case.scale, case.window, k_scale=case.k_scale,
+                                            v_scale=case.v_scale, partition_size=part, workspace=ws)
+        elif shared_pages:
             P.vllm_paged_attn_decode_shared_prefix(out, q, view(kc), view(vc), bt, ctx,
                                                    shared_pages, case.scale, case.window,
                                                    k_scale=case.k_scale, v_scale=case.v_scale,
@@ -473,27 +487,43 @@ def main():
             run_decode(i % R)
         torch.cuda.synchronize()
 
+    # HIP events around the decode call of every EVENT_EVERY-th step: timing
+    # events cost GPU time themselves (about 6.7 us per step when recorded
+    # on every step of the 8B-class batch), so only a regular sample of the
+    # timed steps carries them.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           if i % EVENT_EVERY == 0 else None for i in range(args.steps)]
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record(stream)
     for i in range(args.steps):
         r = (args.warmup + i) % R
         run_write(r)
-        evs[i][0].record(stream)
+        ev = evs[i]
+        if ev:
+            ev[0].record(stream)
         run_decode(r)
-        evs[i][1].record(stream)
+        if ev:
+            ev[1].record(stream)
+    region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms = [ev[0].elapsed_time(ev[1]) for ev in evs if ev]
     dec_avg = sum(dec_ms) / len(dec_ms)
+    region_ms = region[0].elapsed_time(region[1]) / args.steps   # GPU time per step
 
     step_bytes = by["decode"] + by["write"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # roofline on the bytes the path must move: with the shared prefix read
     # once, its K/V count once
-    achieved = (by["unique_decode"] if shared_pages else by["decode"]) / (dec_avg * 1e-3) / 1e9
+    call_bytes = by["unique_decode"] if shared_pages else by["decode"] + (by["write"] if fused else 0)
+    # a fused step is one decode call: its duration is the events around the
+    # whole timed region over the steps (the sampled per-call events add a
+    # bubble of their own); otherwise the sampled per-call events
+    call_ms = region_ms if fused else dec_avg
+    achieved = call_bytes / (call_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -516,16 +546,24 @@ def main():
                    "shared_prefix_pages": shared_pages,
                    "unique_kv_bytes_per_step": by["unique_kv"],
                    "pool_replicas": R, "seed": args.config,
-                   "launch": "hip_graph_replay" if args.graph else "eager"},
+                   "launch": "hip_graph_replay" if args.graph else "eager",
+                   "step": "cache write fused into the decode" if fused else
+                           "cache write, then decode"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seqs_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
-        "decode_call_ms": {"mean": round(dec_avg, 5),
+        "decode_call_ms": {"roofline_basis": ("events around the timed region / steps" if fused else
+                                              "sampled events around the call"),
+                           "region_per_step": round(region_ms, 5),
+                           "events_every_n_steps": EVENT_EVERY, "samples": len(dec_ms),
+                           "mean": round(dec_avg, 5),
                            "p10": round(float(np.percentile(dec_ms, 10)), 5),
                            "p50": round(float(np.percentile(dec_ms, 50)), 5),
                            "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "roofline": {"bound": "hbm",
                      "kernel": ("decode call (attn_tile_kernel shared-prefix pass + decode_kernel + "
                                 "decode_merge_kernel), unique bytes" if shared_pages else
+                                "decode call with the fused cache write (decode_kernel + "
+                                "decode_merge_kernel)" if fused else
                                 "decode call (decode_kernel + decode_merge_kernel)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -2,8 +2,11 @@
  * vllm_paged.h -- C ABI of the paged KV-cache hot path for AMD Instinct
  * MI355X (gfx950): the cache-write scatter that fills a block-paged KV pool,
  * attention decode over that pool (work split evenly over the GPU's waves,
- * pieces of cut sequences merged with the log-sum-exp rule), FP8-E4M3 pools,
- * and an MFMA chunked-prefill variant.
+ * pieces of cut sequences merged with the log-sum-exp rule), FP8 pools (E4M3
+ * and E5M2, per-tensor or per-kv-head scales), an MFMA chunked-prefill
+ * variant, a decode that reads a batch's shared prefix once, chunked-local
+ * attention and page recycling for local attention, and a device-side
+ * prefix-caching block manager that fills block tables and slot mappings.
  *
  * What is computed follows the pages' problem statement:
  *   - a block-paged KV cache held in FP16 or FP8 pages ("Building and
@@ -26,8 +29,10 @@
  * Conventions for every call below
  *   - All tensor data pointers are DEVICE pointers (hipMalloc / torch CUDA
  *     tensors).  Host pointers are rejected with VLLM_ERR_DEVICE_PTR.
- *   - The caller owns every buffer (inputs, pools, outputs, workspace).  The
- *     library keeps no device memory between calls.
+ *   - The caller owns every buffer (inputs, pools, outputs, workspace, the
+ *     block manager's state).  The library keeps no device memory between
+ *     calls; it keeps one extra stream and two events per device, created on
+ *     first use by the shared-prefix decode.
  *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronize the host.  A VLLM_OK return means the
  *     work was enqueued; device-side faults surface on the stream.
@@ -53,7 +58,10 @@
 extern "C" {
 #endif
 
-#define VLLM_PAGED_ABI_VERSION 2
+/* Version 2 appended k_scales / v_scales to vllm_attn_opts; version 3 added
+ * FP8 pools in vllm_paged_attn_prefill and the local-attention and block
+ * manager entry points (no struct changed). */
+#define VLLM_PAGED_ABI_VERSION 3
 #define VLLM_PAGED_BLOCK_SIZE 16
 
 typedef enum vllm_status {
@@ -177,6 +185,32 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
                                    const vllm_tensor* context_lens, float scale,
                                    int32_t window, const vllm_attn_opts* opts,
                                    void* hip_stream);
+
+/*
+ * Cache write of each sequence's newest token fused into the decode (the two
+ * calls of a decode step in one launch sequence): the same result, bit for
+ * bit, as vllm_paged_cache_write(k_new, v_new, slot_mapping, ...) followed
+ * by vllm_paged_attn_decode(...) with the same pools and options.
+ *   k_new, v_new   [B, Hkv, D]  q's dtype: K/V of token context_lens[s] - 1
+ *   slot_mapping   [B] I64      its slot (page * 16 + row); negative = none.
+ *                  It must be the slot that sequence s's table gives for
+ *                  that token: the wave that reads the sequence's last page
+ *                  writes the token there first (a slot elsewhere is
+ *                  written too, but unordered with the reads of that page).
+ *   other arguments as vllm_paged_attn_decode (k_cache, v_cache are written).
+ * FP8 pools quantize as vllm_paged_cache_write does (opts scales).  When a
+ * work unit holds more than 4 query heads (the fused write would cost the
+ * decode more than a launch), the library runs the cache-write kernel first
+ * instead; the result is the same.
+ */
+vllm_status vllm_paged_attn_decode_append(vllm_tensor* out, const vllm_tensor* q,
+                                          const vllm_tensor* k_new, const vllm_tensor* v_new,
+                                          const vllm_tensor* slot_mapping,
+                                          vllm_tensor* k_cache, vllm_tensor* v_cache,
+                                          const vllm_tensor* block_tables,
+                                          const vllm_tensor* context_lens, float scale,
+                                          int32_t window, const vllm_attn_opts* opts,
+                                          void* hip_stream);
 
 /*
  * Bytes of workspace vllm_paged_attn_decode needs for these sizes (it

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     vllm_block_manager_state_layout,
     vllm_block_manager_state_size,
     vllm_block_manager_workspace_size,
+    vllm_paged_attn_decode_append,
     vllm_paged_cache_write,
     vllm_paged_chunked_local_plan,
     vllm_paged_chunked_local_virtual_count,

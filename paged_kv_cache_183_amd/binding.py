@@ -33,7 +33,7 @@ BLOCK_SIZE = 16
 EXPORTED = ["vllm_abi_version", "vllm_last_error", "vllm_paged_cache_write",
             "vllm_paged_attn_decode", "vllm_paged_attn_workspace_size",
             "vllm_paged_attn_decode_shared_prefix", "vllm_paged_attn_shared_prefix_workspace_size",
-            "vllm_paged_attn_prefill", "vllm_paged_chunked_local_plan",
+            "vllm_paged_attn_prefill", "vllm_paged_attn_decode_append", "vllm_paged_chunked_local_plan",
             "vllm_paged_chunked_local_virtual_count", "vllm_paged_recycle_pages",
             "vllm_block_manager_state_size", "vllm_block_manager_state_layout",
             "vllm_block_manager_init", "vllm_block_manager_workspace_size",
@@ -91,6 +91,10 @@ def _load():
     lib.vllm_paged_recycle_pages.restype = ctypes.c_int
     lib.vllm_paged_recycle_pages.argtypes = [T, T, ctypes.c_int32, ctypes.c_int32, T, T,
                                              ctypes.c_void_p]
+    lib.vllm_paged_attn_decode_append.restype = ctypes.c_int
+    lib.vllm_paged_attn_decode_append.argtypes = [T] * 9 + [ctypes.c_float, ctypes.c_int32,
+                                                             ctypes.POINTER(VllmAttnOpts),
+                                                             ctypes.c_void_p]
     lib.vllm_block_manager_state_size.restype = ctypes.c_size_t
     lib.vllm_block_manager_state_size.argtypes = [ctypes.c_int32]
     lib.vllm_block_manager_state_layout.restype = ctypes.c_int32
@@ -225,6 +229,19 @@ def vllm_paged_attn_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
                                                     ctypes.c_float(scale), ctypes.c_int32(window),
                                                     ctypes.byref(o),
                                                     ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_paged_attn_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                  block_tables, context_lens, scale, window=0, k_scale=0.0,
+                                  v_scale=0.0, partition_size=0, workspace=None,
+                                  stream=None) -> None:
+    """Cache write of each sequence's newest token fused with the decode."""
+    args = [tensor_desc(x) for x in (out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                     block_tables, context_lens)]
+    o = _opts(k_scale, v_scale, partition_size, workspace)
+    _check(LIB.vllm_paged_attn_decode_append(*[ctypes.byref(a) for a in args],
+                                             ctypes.c_float(scale), ctypes.c_int32(window),
+                                             ctypes.byref(o), ctypes.c_void_p(_stream(stream))))
 
 
 def vllm_paged_attn_prefill(out, q, k_cache, v_cache, block_tables, query_start_loc,

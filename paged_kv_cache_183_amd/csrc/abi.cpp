@@ -392,10 +392,17 @@ namespace {
 
 // Decode, optionally with the first shared_pages pages of every sequence
 // handled by the shared-prefix pass (read once per kv-head for the batch).
+// Largest work unit (query heads) that the decode kernel with the fused
+// newest-token write handles; larger ones write first with the cache-write
+// kernel.
+constexpr int kFusedMaxHeads = 4;
+
 vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor* k_cache,
                        const vllm_tensor* v_cache, const vllm_tensor* block_tables,
                        const vllm_tensor* context_lens, int32_t shared_pages, float scale,
-                       int32_t window, const vllm_attn_opts* opts, void* hip_stream) {
+                       int32_t window, const vllm_attn_opts* opts, void* hip_stream,
+                       const vllm_tensor* k_new = nullptr, const vllm_tensor* v_new = nullptr,
+                       const vllm_tensor* slot_mapping = nullptr) {
   VP_TRY(check_tensor(out, "out", 3));
   VP_TRY(check_tensor(q, "q", 3));
   VP_TRY(check_tensor(k_cache, "k_cache", 4));
@@ -422,6 +429,21 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
                 (long long)Hq, (long long)Hkv);
   if (window < 0) return fail(VLLM_ERR_INVALID_ARG, "window must be >= 0 (got %d)", (int)window);
   if (!std::isfinite(scale)) return fail(VLLM_ERR_INVALID_ARG, "scale must be finite");
+  const bool append = k_new != nullptr;
+  if (append) {                            // the newest token of each sequence, fused
+    VP_TRY(check_tensor(k_new, "k_new", 3));
+    VP_TRY(check_tensor(v_new, "v_new", 3));
+    VP_TRY(check_tensor(slot_mapping, "slot_mapping", 1));
+    for (const vllm_tensor* x : {k_new, v_new})
+      if (x->shape[0] != B || x->shape[1] != Hkv || x->shape[2] != D)
+        return fail(VLLM_ERR_INVALID_ARG, "k_new / v_new must be [%lld, %lld, %lld]", (long long)B,
+                    (long long)Hkv, (long long)D);
+    if (slot_mapping->shape[0] != B)
+      return fail(VLLM_ERR_INVALID_ARG, "slot_mapping must have %lld entries", (long long)B);
+    VP_TRY(check_dtype(k_new, "k_new", q->dtype));
+    VP_TRY(check_dtype(v_new, "v_new", q->dtype));
+    VP_TRY(check_dtype(slot_mapping, "slot_mapping", VLLM_DTYPE_I64));
+  }
   if (q->dtype != VLLM_DTYPE_F16 && q->dtype != VLLM_DTYPE_BF16)
     return fail(VLLM_ERR_UNSUPPORTED, "q: dtype %s, expected F16 or BF16", dtype_name(q->dtype));
   VP_TRY(check_dtype(out, "out", q->dtype));
@@ -463,6 +485,11 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   VP_TRY(check_data(block_tables, "block_tables", 4));
   VP_TRY(check_data(context_lens, "context_lens", 4));
   if (fp8) VP_TRY(check_scales(opts));
+  if (append) {
+    VP_TRY(check_data(k_new, "k_new", 16));
+    VP_TRY(check_data(v_new, "v_new", 16));
+    VP_TRY(check_data(slot_mapping, "slot_mapping", 8));
+  }
 
   hipStream_t stream = (hipStream_t)hip_stream;
   const int kv_fmt = fmt_of(k_cache->dtype), q_fmt = fmt_of(q->dtype);
@@ -483,11 +510,18 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   p.window = window;
   p.chunk_pages = dp.chunk_pages;
   p.max_chunks = (int32_t)dp.max_chunks;
+  // The fused write costs the decode kernel a few registers: with units of
+  // more than kFusedMaxHeads query heads that slows it more than a separate
+  // cache-write launch costs, so those take the write kernel first (the
+  // same result either way).
+  const bool fused = append && dp.head_chunk <= kFusedMaxHeads;
+  const bool write_first = append && !fused;
   p.num_workers = dp.chunk_pages > 0
                       ? (int32_t)std::min<int64_t>(dp.max_chunks,
                                                    vp::decode_workers(dp.pages_bound, (int)D, kv_fmt,
-                                                                      q_fmt, dp.head_chunk))
-                      : vp::decode_workers(dp.pages_bound, (int)D, kv_fmt, q_fmt, dp.head_chunk);
+                                                                      q_fmt, dp.head_chunk, fused))
+                      : vp::decode_workers(dp.pages_bound, (int)D, kv_fmt, q_fmt, dp.head_chunk,
+                                           fused);
   p.num_workers = std::max<int32_t>(vp::kDecodeWaves,
                                     (p.num_workers + vp::kDecodeWaves - 1) / vp::kDecodeWaves *
                                         vp::kDecodeWaves);
@@ -496,6 +530,14 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   p.out_scale = vs;
   p.k_scales = (fp8 && opts) ? opts->k_scales : nullptr;
   p.v_scales = (fp8 && opts) ? opts->v_scales : nullptr;
+  if (fused) {
+    p.k_new = k_new->data;
+    p.v_new = v_new->data;
+    p.new_slots = static_cast<const int64_t*>(slot_mapping->data);
+    p.num_slots = NB * VLLM_PAGED_BLOCK_SIZE;
+    p.k_scale = ks;
+    p.v_scale = vs;
+  }
 
   void* ws = nullptr;
   bool owned = false;
@@ -547,7 +589,29 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
     p.ws_um = reinterpret_cast<float*>(base + dp.um_off);
     p.ws_ul = reinterpret_cast<float*>(base + dp.ul_off);
   }
-  if (shared_pages == 0) {
+  if (e == hipSuccess && write_first) {
+    vp::CacheWriteParams w{};
+    w.k = k_new->data;
+    w.v = v_new->data;
+    w.slot_mapping = static_cast<const int64_t*>(slot_mapping->data);
+    w.k_cache = k_cache->data;
+    w.v_cache = v_cache->data;
+    w.num_slots = NB * VLLM_PAGED_BLOCK_SIZE;
+    w.src_tok_stride = Hkv * D;
+    w.num_items = (uint32_t)(B * Hkv * (D / 8));
+    w.items_per_token = (uint32_t)(Hkv * (D / 8));
+    w.items_per_head = (uint32_t)(D / 8);
+    w.num_kv_heads = (int32_t)Hkv;
+    w.head_dim = (int32_t)D;
+    w.k_scale = ks;
+    w.v_scale = vs;
+    w.k_scales = p.k_scales;
+    w.v_scales = p.v_scales;
+    e = vp::launch_cache_write(w, q_fmt, kv_fmt, stream);
+  }
+  if (e != hipSuccess) {
+    // (nothing more is launched)
+  } else if (shared_pages == 0) {
     e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
   } else {
     // Fork: the suffix decode goes first on the caller's stream, the prefix
@@ -583,6 +647,20 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
                                    const vllm_attn_opts* opts, void* hip_stream) {
   return run_decode(out, q, k_cache, v_cache, block_tables, context_lens, 0, scale, window, opts,
                     hip_stream);
+}
+
+vllm_status vllm_paged_attn_decode_append(vllm_tensor* out, const vllm_tensor* q,
+                                          const vllm_tensor* k_new, const vllm_tensor* v_new,
+                                          const vllm_tensor* slot_mapping,
+                                          vllm_tensor* k_cache, vllm_tensor* v_cache,
+                                          const vllm_tensor* block_tables,
+                                          const vllm_tensor* context_lens, float scale,
+                                          int32_t window, const vllm_attn_opts* opts,
+                                          void* hip_stream) {
+  if (!k_new || !v_new || !slot_mapping)
+    return fail(VLLM_ERR_INVALID_ARG, "k_new, v_new and slot_mapping are required");
+  return run_decode(out, q, k_cache, v_cache, block_tables, context_lens, 0, scale, window, opts,
+                    hip_stream, k_new, v_new, slot_mapping);
 }
 
 vllm_status vllm_paged_attn_decode_shared_prefix(vllm_tensor* out, const vllm_tensor* q,

@@ -229,7 +229,47 @@ __device__ void page_prefix(const DecodeParams& p, int* pre) {
   __syncthreads();
 }
 
-template <int D, int G, int KF, int QF, int LPR, int PD>
+// Fused cache write: the new token of sequence s, kv-head hk, written to its
+// slot exactly as the cache-write kernel writes it (bit copy for 16-bit
+// pools; for FP8 pools one correctly rounded fp32 division by the scale, then
+// the saturating nearest-even encoder).  Lanes 0..D/8-1 write K chunks, the
+// next D/8 lanes V chunks.  The stores complete before the wave goes on, so
+// its own reads of that page see them.
+template <int D, int KF, int QF>
+__device__ __forceinline__ void append_row(const DecodeParams& p, int s, int hk, int lane) {
+  constexpr int CH = D / 8;
+  const int64_t slot = p.new_slots[s];
+  if (slot >= 0 && slot < p.num_slots && lane < 2 * CH) {
+    const bool is_v = lane >= CH;
+    const int c = is_v ? lane - CH : lane;
+    const int64_t src = ((int64_t)s * p.num_kv_heads + hk) * D + c * 8;
+    const int64_t dst = (((slot >> 4) * p.num_kv_heads + hk) * 16 + (slot & 15)) * D + c * 8;
+    const uint4 x = *reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(is_v ? p.v_new : p.k_new) + src);
+    void* pool = is_v ? const_cast<void*>(p.v_cache) : const_cast<void*>(p.k_cache);
+    if constexpr (!is_fp8(KF)) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(pool) + dst) = x;
+    } else {
+      const float sc = is_v ? (p.v_scales ? p.v_scales[hk] : p.v_scale)
+                            : (p.k_scales ? p.k_scales[hk] : p.k_scale);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      uint32_t o[2] = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a, b;
+        x2_to_f32<QF>(w[i], a, b);
+        const uint32_t ca = fp8_from_f32<KF>(a / sc), cb = fp8_from_f32<KF>(b / sc);
+        o[i >> 1] |= (ca | (cb << 8)) << ((i & 1) * 16);
+      }
+      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(pool) + dst) = make_uint2(o[0], o[1]);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the stores are done
+}
+
+// AP: with the fused cache write of each sequence's newest token (a variant
+// of its own, so that the plain decode keeps its registers).
+template <int D, int G, int KF, int QF, int LPR, int PD, bool AP>
 __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
   constexpr int CH = D / 8;
   static_assert(LPR >= 4 && LPR <= CH, "lanes per K row");
@@ -324,6 +364,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
       const float oscale = p.v_scales ? p.v_scales[hk] : p.out_scale;
 
       // ---- one segment: pages [i0, i1) of unit (s, y) ----
+      if constexpr (AP) {
+        if (i1 == sr.np) append_row<D, KF, QF>(p, s, hk, lane);
+      }
       uint4 qv[G][CPL];
       {
         const uint16_t* qp =
@@ -723,40 +766,41 @@ template <int D, int G>
 constexpr int kPd = 2;
 
 template <int D, int G, int KF, int QF>
-static const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&decode_kernel<D, G, KF, QF, kLpr<D, G>, kPd<D, G>>);
+static const void* kernel_ptr(bool ap) {
+  return ap ? reinterpret_cast<const void*>(&decode_kernel<D, G, KF, QF, kLpr<D, G>, kPd<D, G>, true>)
+            : reinterpret_cast<const void*>(&decode_kernel<D, G, KF, QF, kLpr<D, G>, kPd<D, G>, false>);
 }
 
 template <int D, int KF, int QF>
-static const void* pick(int gc) {
+static const void* pick(int gc, bool ap) {
   switch (gc) {
-    case 1: return kernel_ptr<D, 1, KF, QF>();
-    case 2: return kernel_ptr<D, 2, KF, QF>();
-    case 3: return kernel_ptr<D, 3, KF, QF>();
-    case 4: return kernel_ptr<D, 4, KF, QF>();
-    case 5: return kernel_ptr<D, 5, KF, QF>();
-    case 6: return kernel_ptr<D, 6, KF, QF>();
-    case 7: return kernel_ptr<D, 7, KF, QF>();
-    case 8: return kernel_ptr<D, 8, KF, QF>();
+    case 1: return kernel_ptr<D, 1, KF, QF>(ap);
+    case 2: return kernel_ptr<D, 2, KF, QF>(ap);
+    case 3: return kernel_ptr<D, 3, KF, QF>(ap);
+    case 4: return kernel_ptr<D, 4, KF, QF>(ap);
+    case 5: return kernel_ptr<D, 5, KF, QF>(ap);
+    case 6: return kernel_ptr<D, 6, KF, QF>(ap);
+    case 7: return kernel_ptr<D, 7, KF, QF>(ap);
+    case 8: return kernel_ptr<D, 8, KF, QF>(ap);
     default: return nullptr;
   }
 }
 
-static const void* decode_kernel_for(int D, int kv_fmt, int q_fmt, int gc) {
+static const void* decode_kernel_for(int D, int kv_fmt, int q_fmt, int gc, bool ap) {
   if (D == 128) {
-    if (kv_fmt == kF16 && q_fmt == kF16) return pick<128, kF16, kF16>(gc);
-    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<128, kBF16, kBF16>(gc);
-    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<128, kE4M3, kF16>(gc);
-    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<128, kE4M3, kBF16>(gc);
-    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<128, kE5M2, kF16>(gc);
-    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<128, kE5M2, kBF16>(gc);
+    if (kv_fmt == kF16 && q_fmt == kF16) return pick<128, kF16, kF16>(gc, ap);
+    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<128, kBF16, kBF16>(gc, ap);
+    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<128, kE4M3, kF16>(gc, ap);
+    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<128, kE4M3, kBF16>(gc, ap);
+    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<128, kE5M2, kF16>(gc, ap);
+    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<128, kE5M2, kBF16>(gc, ap);
   } else if (D == 64) {
-    if (kv_fmt == kF16 && q_fmt == kF16) return pick<64, kF16, kF16>(gc);
-    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<64, kBF16, kBF16>(gc);
-    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<64, kE4M3, kF16>(gc);
-    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<64, kE4M3, kBF16>(gc);
-    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<64, kE5M2, kF16>(gc);
-    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<64, kE5M2, kBF16>(gc);
+    if (kv_fmt == kF16 && q_fmt == kF16) return pick<64, kF16, kF16>(gc, ap);
+    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<64, kBF16, kBF16>(gc, ap);
+    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<64, kE4M3, kF16>(gc, ap);
+    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<64, kE4M3, kBF16>(gc, ap);
+    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<64, kE5M2, kF16>(gc, ap);
+    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<64, kE5M2, kBF16>(gc, ap);
   }
   return nullptr;
 }
@@ -782,7 +826,8 @@ static const void* merge_kernel_for(int D, int q_fmt, int gc) {
   return nullptr;
 }
 
-int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk) {
+int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk,
+                   bool append) {
   static int cus = -1;
   if (cus < 0) {
     int dev = 0;
@@ -795,13 +840,13 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
     cus = v;
   }
   // workgroups resident per CU, queried once per kernel variant
-  static constexpr int kVariants = 2 * 4 * 2 * 8;
+  static constexpr int kVariants = 2 * 2 * 4 * 16;     // (append, D = 128, kv format, q format, G)
   static int occ_cache[kVariants] = {0};
   int per_cu = 4;
-  const int vi = ((head_dim == 128) * 4 + kv_fmt) * 16 + q_fmt * 8 + (head_chunk - 1);
+  const int vi = (((int)append * 2 + (head_dim == 128)) * 4 + kv_fmt) * 16 + q_fmt * 8 + (head_chunk - 1);
   if (vi >= 0 && vi < kVariants && occ_cache[vi] > 0) {
     per_cu = occ_cache[vi];
-  } else if (const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, head_chunk)) {
+  } else if (const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, head_chunk, append)) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, kNW * 64, 0) == hipSuccess && occ > 0) {
       per_cu = occ;
@@ -824,7 +869,7 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream,
                          bool split) {
   if (p.num_seqs == 0) return hipSuccess;
-  const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, p.head_chunk);
+  const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, p.head_chunk, p.new_slots != nullptr);
   const void* mk = merge_kernel_for(head_dim, q_fmt, p.head_chunk);
   if (!k || !mk) return hipErrorInvalidValue;
   DecodeParams a = p;

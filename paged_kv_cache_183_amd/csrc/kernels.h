@@ -75,6 +75,14 @@ struct DecodeParams {
   const float* pfx_o;
   const float* pfx_m;
   const float* pfx_l;
+  // Fused cache write of each sequence's newest token (null: none): k_new /
+  // v_new [B, Hkv, D] in q's format, written to new_slots[s] as the cache
+  // write would, by the wave that reads the unit's last page, before it reads it.
+  const void* k_new;
+  const void* v_new;
+  const int64_t* new_slots;
+  int64_t num_slots;
+  float k_scale, v_scale;      // FP8 pools: the per-tensor scales of the write
 };
 
 // kv_fmt: kF16 / kBF16 / kE4M3 / kE5M2; q_fmt: kF16 / kBF16.  Launches the
@@ -240,6 +248,7 @@ inline int decode_head_chunk(int g) {
 }
 
 // Workers (waves) the decode grid uses for an upper bound of the page count.
-int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk);
+int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk,
+                   bool append = false);
 
 }  // namespace vp
