@@ -42,6 +42,7 @@
 //    stays in L2) so that the compiler can keep the buffers in flight across
 //    iterations.
 #include <cstdlib>
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -638,31 +639,40 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Log-sum-exp merge of the pieces of units cut by chunk boundaries.  The
-// G x D outputs of a unit are split into slices of kMergeThreads, one
-// workgroup per (unit, slice) and one output per thread; the unit's record
-// (first slot, piece count) comes from the decode kernel.  All loads of a
-// round are unconditional and independent (padding pieces past the count
-// re-read the last piece and get weight 0), so a round of up to 64 pieces has
-// all its loads in flight at once.
-constexpr int kMergeThreads = 256;
+// Log-sum-exp merge of the pieces of units cut by chunk boundaries (and, with
+// a shared prefix, of every unit with its prefix splits).  One workgroup per
+// unit, one thread per 4 consecutive outputs of its G x D block; the unit's
+// record (first slot, piece count) comes from the decode kernel.  Pieces are
+// read in rounds of kMergeBatch (units of more pieces: twice that) straight
+// into registers, every load of a round independent (padding pieces past the
+// count re-read the last piece and get weight 0), so a round costs one
+// memory latency:
+// M = max m, w = l 2^(m - M), out = sum w o / sum w.
+constexpr int kMergeBatch = 8;
 
-template <int D, int G>
-constexpr int kMergeSlices = (G * D + kMergeThreads - 1) / kMergeThreads;
-
-template <int D, int G, int NB>
-__device__ __forceinline__ void merge_rounds(const DecodeParams& p, int64_t unit, int64_t sl0,
-                                             int nsuf, int npieces, int64_t prow, int e,
-                                             float (&s_m)[64][G], float (&s_l)[64][G], float& M,
-                                             float& den, float& acc) {
-  const int t = threadIdx.x;
+template <int D, int G, int QF>
+__global__ __launch_bounds__(G * D / 4) void decode_merge_kernel(DecodeParams p) {
+  const int ngc = p.group / G;
+  const int NY = p.num_kv_heads * ngc;
+  const int64_t u = blockIdx.x;
+  const int nsuf = p.ws_unit[u * 2 + 1];
+  const int npieces = nsuf + p.num_splits;
+  if (npieces == 0) return;                   // finished inside one chunk, or empty
+  const int64_t sl0 = p.ws_unit[u * 2];
+  const int s = (int)(u / NY);
+  const int y = (int)(u - (int64_t)s * NY);
+  const int hk = y / ngc;
+  const int h0 = hk * p.group + (y - hk * ngc) * G;
+  const int64_t prow = (int64_t)s * p.num_q_heads + h0;    // row of head h0 in the prefix partials
   const int64_t fk = sl0 >> 1;
   const int64_t split_rows = (int64_t)p.num_seqs * p.num_q_heads;
+  const int e = threadIdx.x * 4;
+  const int h = e / D;
   // Piece k < nsuf: a piece of the decode (the first sits in the slot its
   // wave recorded, or in the unit's own slot when that is -1; the later ones
   // open the following chunks, slot 0 of each); piece nsuf + i: split i of
-  // the shared-prefix partials.  Returns the row index of head 0 of the unit
-  // in the piece's (o, m, l) arrays.
+  // the shared-prefix partials.  Gives the row of head 0 of the unit in the
+  // piece's (o, m, l) arrays.
   auto ml_row = [&](int k, const float*& op, const float*& mp, const float*& lp)
       __attribute__((always_inline)) {
     if (k < nsuf) {
@@ -670,7 +680,7 @@ __device__ __forceinline__ void merge_rounds(const DecodeParams& p, int64_t unit
         op = p.ws_uo;
         mp = p.ws_um;
         lp = p.ws_ul;
-        return unit * G;
+        return u * G;
       }
       op = p.ws_o;
       mp = p.ws_m;
@@ -682,73 +692,51 @@ __device__ __forceinline__ void merge_rounds(const DecodeParams& p, int64_t unit
     lp = p.pfx_l;
     return (int64_t)(k - nsuf) * split_rows + prow;
   };
-  const int h = e / D;
-  for (int k0 = 0; k0 < npieces; k0 += NB) {
-    const int last = npieces - 1 - k0;          // last valid index of this round
-    for (int i = t; i < NB * G; i += kMergeThreads) {
-      const int k = i / G, hh = i - k * G;
-      const float *op, *mp, *lp;
-      const int64_t j = ml_row(k0 + min(k, last), op, mp, lp) + hh;
-      const float m = mp[j], l = lp[j];
-      s_m[k][hh] = k <= last ? m : -INFINITY;
-      s_l[k][hh] = k <= last ? l : 0.0f;
-    }
-    float o[NB];
+  float M = -INFINITY, den = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto rounds = [&](auto nb) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb)::value;
+    for (int k0 = 0; k0 < npieces; k0 += NB) {
+      float mk[NB], lk[NB];
+      float4 ok[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const float *op, *mp, *lp;
-      const int64_t r0 = ml_row(k0 + min(k, last), op, mp, lp);
-      o[k] = op[r0 * D + e];
-    }
-    __syncthreads();
-    float Mn = M;
+      for (int k = 0; k < NB; ++k) {
+        const float *op, *mp, *lp;
+        const int64_t r = ml_row(min(k0 + k, npieces - 1), op, mp, lp) + h;
+        mk[k] = mp[r];
+        lk[k] = lp[r];
+        ok[k] = *reinterpret_cast<const float4*>(op + r * D + (e - h * D));
+      }
+      float Mn = M;
 #pragma unroll
-    for (int k = 0; k < NB; ++k) Mn = fmaxf(Mn, s_m[k][h]);
-    const float a = (M == -INFINITY) ? 0.0f : fast_exp2(M - Mn);
-    den *= a;
-    acc *= a;
-    M = Mn;
-    const float Mu = (M == -INFINITY) ? 0.0f : M;   // (every piece so far empty)
+      for (int k = 0; k < NB; ++k)
+        if (k0 + k < npieces) Mn = fmaxf(Mn, mk[k]);
+      const float a = (M == -INFINITY) ? 0.0f : fast_exp2(M - Mn);
+      den *= a;
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const float w = s_l[k][h] * fast_exp2(s_m[k][h] - Mu);  // 0 for padding / empty pieces
-      den += w;
-      acc = fmaf(w, o[k], acc);
+      for (int j = 0; j < 4; ++j) acc[j] *= a;
+      M = Mn;
+      const float Mu = (M == -INFINITY) ? 0.0f : M;   // (every piece so far empty)
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float w = (k0 + k < npieces) ? lk[k] * fast_exp2(mk[k] - Mu) : 0.0f;  // 0: padding, empty
+        den += w;
+        acc[0] = fmaf(w, ok[k].x, acc[0]);
+        acc[1] = fmaf(w, ok[k].y, acc[1]);
+        acc[2] = fmaf(w, ok[k].z, acc[2]);
+        acc[3] = fmaf(w, ok[k].w, acc[3]);
+      }
     }
-    __syncthreads();
-  }
-}
-
-template <int D, int G, int QF>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
-  constexpr int S = kMergeSlices<D, G>;
-  __shared__ float s_m[64][G], s_l[64][G];
-  const int ngc = p.group / G;
-  const int NY = p.num_kv_heads * ngc;
-  const int u = blockIdx.x / S;
-  const int e_raw = (blockIdx.x - u * S) * kMergeThreads + threadIdx.x;
-  const int e = min(e_raw, G * D - 1);
-  const int nsuf = p.ws_unit[(int64_t)u * 2 + 1];
-  const int npieces = nsuf + p.num_splits;
-  if (npieces == 0) return;                   // finished inside one chunk, or empty
-  const int64_t sl0 = p.ws_unit[(int64_t)u * 2];
-  const int s = u / NY;
-  const int y = u - s * NY;
-  const int hk = y / ngc;
-  const int h0 = hk * p.group + (y - hk * ngc) * G;
-  const int64_t prow = (int64_t)s * p.num_q_heads + h0;    // row of head h0 in the prefix partials
-  float M = -INFINITY, den = 0.0f, acc = 0.0f;
-  if (npieces <= 16)
-    merge_rounds<D, G, 16>(p, u, sl0, nsuf, npieces, prow, e, s_m, s_l, M, den, acc);
-  else if (npieces <= 32)
-    merge_rounds<D, G, 32>(p, u, sl0, nsuf, npieces, prow, e, s_m, s_l, M, den, acc);
-  else
-    merge_rounds<D, G, 64>(p, u, sl0, nsuf, npieces, prow, e, s_m, s_l, M, den, acc);
-  if (e_raw < G * D) {
-    uint16_t* out = static_cast<uint16_t*>(p.out) + prow * D;
-    const float oscale = p.v_scales ? p.v_scales[hk] : p.out_scale;
-    out[e] = f32_to_16<QF>(den > 0.0f ? acc / den * oscale : 0.0f);
-  }
+  };
+  // (npieces is uniform over the workgroup)
+  if (npieces <= kMergeBatch) rounds(std::integral_constant<int, kMergeBatch>{});
+  else rounds(std::integral_constant<int, 2 * kMergeBatch>{});
+  const float oscale = p.v_scales ? p.v_scales[hk] : p.out_scale;
+  const float f = den > 0.0f ? oscale / den : 0.0f;
+  uint16_t* out = static_cast<uint16_t*>(p.out) + prow * D + e;
+  const uint32_t lo = (uint32_t)f32_to_16<QF>(acc[0] * f) | ((uint32_t)f32_to_16<QF>(acc[1] * f) << 16);
+  const uint32_t hi = (uint32_t)f32_to_16<QF>(acc[2] * f) | ((uint32_t)f32_to_16<QF>(acc[3] * f) << 16);
+  *reinterpret_cast<uint2*>(out) = make_uint2(lo, hi);
 }
 
 // Page prefix for batches too large for the LDS scan of decode_kernel.
@@ -891,8 +879,7 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int q_fmt, h
   DecodeParams a = p;
   void* args[] = {&a};
   const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * (p.group / p.head_chunk);
-  const int64_t slices = (p.head_chunk * head_dim + kMergeThreads - 1) / kMergeThreads;
-  return hipLaunchKernel(mk, dim3((unsigned)(units * slices)), dim3(kMergeThreads), args, 0, stream);
+  return hipLaunchKernel(mk, dim3((unsigned)units), dim3(p.head_chunk * head_dim / 4), args, 0, stream);
 }
 
 }  // namespace vp
