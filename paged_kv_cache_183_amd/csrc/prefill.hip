@@ -199,6 +199,18 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
     q_off = ((int64_t)s * p.num_q_heads + hk * g + head) * D;
   }
 
+  // Q operand: lane (row, hf) holds d = 64 hf + 8 t + i for k-step t.  The
+  // loads are in flight during the reduction below and waited for after it:
+  // once that wait has been seen, the block loop need not wait for them (the
+  // memory counter cannot tell them from the next block's loads, so an
+  // in-loop wait for Q would wait for those every block).
+  uint4 qr[8];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + q_off + 64 * hf;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qr[t] = *reinterpret_cast<const uint4*>(qp + 8 * t);
+  }
+
   // Over the workgroup's rows: the largest lower and the smallest and largest
   // upper bounds.  A block inside every row's range needs no per-key mask;
   // keys at or past every row's range are staged as zeros.
@@ -219,14 +231,8 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   const int n_valid = min(key_end, __builtin_amdgcn_readfirstlane(s_red[2]));
   const int kb0 = (key_begin / kBK) * kBK;
   const int nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
+  __builtin_amdgcn_s_waitcnt(0);               // (the Q loads)
 
-  // Q operand: lane (row, hf) holds d = 64 hf + 8 t + i for k-step t.
-  uint4 qr[8];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + q_off + 64 * hf;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qr[t] = *reinterpret_cast<const uint4*>(qp + 8 * t);
-  }
 
   const int32_t* bt = p.block_tables + (int64_t)seq_tbl * p.bt_stride;
   const uint8_t* kpool = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
@@ -251,8 +257,12 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   // Loads are unconditional (rows at or past n_valid are replaced by zeros
   // when written to LDS) so that nothing waits on them before the LDS write.
   // (the two block ids of a block are read one block ahead of its K/V)
+  // (the ids are uniform over the workgroup: taken into scalar registers
+  // here, a block after their loads were issued, so that the address
+  // arithmetic runs on the scalar unit without waiting on the loads)
   auto fetch = [&](RawT (&kr)[2], RawT (&vr)[2], int ida, int idb) __attribute__((always_inline)) {
-    const int64_t pa = (int64_t)ida * blk_stride, pb = (int64_t)idb * blk_stride;
+    const int64_t pa = (int64_t)__builtin_amdgcn_readfirstlane(ida) * blk_stride;
+    const int64_t pb = (int64_t)__builtin_amdgcn_readfirstlane(idb) * blk_stride;
     kr[0] = *reinterpret_cast<const RawT*>(kpool + pa + k_off);
     kr[1] = *reinterpret_cast<const RawT*>(kpool + pb + k_off);
     const uint8_t* vp = vpool + (v_pgB ? pb : pa) + v_off;
