@@ -574,9 +574,9 @@ def main():
     }
     if not args.no_prefill:
         # The matrix-core variant of the path, on the chunked-prefill workload.
-        res["prefill"] = bench_prefill(make_case(4), steps=min(args.steps, 20), warmup=3)
+        res["prefill"] = bench_prefill(make_case(4), steps=min(args.steps, 50), warmup=10)
         # chunked-local attention (8192-token chunks) on the same batch
-        res["chunked_local"] = bench_prefill(make_case(4), steps=min(args.steps, 20), warmup=3,
+        res["chunked_local"] = bench_prefill(make_case(4), steps=min(args.steps, 50), warmup=10,
                                              chunk=args.chunk_size or 8192)
         # the step before the path: block tables and slots from the device block manager
         res["block_manager"] = bench_block_manager()
