@@ -166,9 +166,10 @@ struct SeqRange {
   int n, lo, lo_page, np;   // np = pages of the kept range (0 if n <= 0)
 };
 
-__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int s) {
+// (ctx: the sequence's context length as stored in context_lens)
+__device__ __forceinline__ SeqRange seq_range_of(const DecodeParams& p, int ctx) {
   SeqRange r;
-  r.n = min(p.context_lens[s], p.bt_stride * 16);
+  r.n = min(ctx, p.bt_stride * 16);
   if (r.n <= 0) {
     r.n = 0; r.lo = 0; r.lo_page = 0; r.np = 0;
     return r;
@@ -184,11 +185,17 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int s) {
   return r;
 }
 
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int s) {
+  return seq_range_of(p, p.context_lens[s]);
+}
+
 // Exclusive prefix of np(s) over the batch, computed by one workgroup of
 // kNW * 64 threads into pre[0 .. B] (pre[B] = total): each thread sums a
 // run of sequences, the runs are scanned within each wave with lane
 // shuffles, then across the kNW wave totals.
-__device__ void page_prefix(const DecodeParams& p, int* pre) {
+// ctx (null: not kept): also receives each sequence's context length, so
+// that the waves take it from LDS instead of reading it again.
+__device__ void page_prefix(const DecodeParams& p, int* pre, int* ctx = nullptr) {
   __shared__ int s_wave[kNW];
   __shared__ int s_total;
   const int B = p.num_seqs;
@@ -198,7 +205,11 @@ __device__ void page_prefix(const DecodeParams& p, int* pre) {
   int sum = 0;
   for (int i = 0; i < per; ++i) {
     const int s = t * per + i;
-    if (s < B) sum += seq_range(p, s).np;
+    if (s < B) {
+      const int c = p.context_lens[s];
+      if (ctx) ctx[s] = c;
+      sum += seq_range_of(p, c).np;
+    }
   }
   int incl = sum;
 #pragma unroll
@@ -223,7 +234,7 @@ __device__ void page_prefix(const DecodeParams& p, int* pre) {
     const int s = t * per + i;
     if (s < B) {
       pre[s] = run;
-      run += seq_range(p, s).np;
+      run += seq_range_of(p, ctx ? ctx[s] : p.context_lens[s]).np;
     }
   }
   if (t == 0) pre[B] = s_total;
@@ -287,6 +298,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
   constexpr int64_t kPageBytes = 16 * ROWB;
 
   __shared__ int s_pre[kScanMax + 1];
+  __shared__ int s_ctx[kScanMax];      // context lengths (batches of up to kScanMax)
   __shared__ uint32_t s_p[kNW][16][GW];
 
   const int lane = threadIdx.x & 63;
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
   // stores it for the merge), else precomputed in the workspace.
   const int* pre;
   if (B <= kScanMax) {
-    page_prefix(p, s_pre);
+    page_prefix(p, s_pre, s_ctx);
     pre = s_pre;
   } else {
     pre = p.ws_prefix;
@@ -347,7 +359,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
     while (g < g_end) {
       // (values read from LDS are wave-uniform: keep them in scalar registers)
       while ((int64_t)NY * __builtin_amdgcn_readfirstlane(pre[s + 1]) <= g) ++s;   // skip empty seqs
-      const SeqRange sr = seq_range(p, s);
+      const SeqRange sr = seq_range_of(
+          p, B <= kScanMax ? __builtin_amdgcn_readfirstlane(s_ctx[s]) : p.context_lens[s]);
       const int64_t off = g - (int64_t)NY * __builtin_amdgcn_readfirstlane(pre[s]);
       const int y = (int)(off / sr.np);
       const int i0 = (int)(off - (int64_t)y * sr.np);
