@@ -97,6 +97,17 @@ def test_decode_parity_reduced(idx):
     check_decode(case, out, kp, vp)
 
 
+@pytest.mark.parametrize("partition", [0, 32])
+def test_decode_batch_beyond_lds_prefix(partition):
+    """More sequences (2,100) than the decode kernel keeps its page prefix
+    and context lengths for in LDS (2,048): the prefix then comes from its
+    own kernel and the lengths from memory."""
+    case = make_case(1, B=2100, ctx_range=(1, 60), Hq=4, Hkv=2)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    check_decode(case, gpu_decode(case, kc, vc, partition=partition), kp, vp)
+
+
 @pytest.mark.parametrize("idx,seqs", [(1, None), (2, [0, 5, 11, 15]), (3, [0, 1, 63, 127])])
 def test_decode_parity_full_size(idx, seqs):
     """Full-size workloads in the launch configuration the benchmark times;
