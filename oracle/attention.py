@@ -206,12 +206,31 @@ def _prefill_one(args):
     for c0 in range(0, rows.size, 128):
         r = rows[c0:c0 + 128]
         for kv in range(Hkv):
-            qg = qs[r, kv * g:(kv + 1) * g, :]                    # [r, g, D]
-            z = scale * np.einsum("rgd,td->rgt", qg, K[:, kv, :])  # [r, g, n]
-            z = np.where(mask[r][:, None, :], z, -np.inf)
+            # the (row, head) pairs of this kv-head as the rows of one product
+            qg = qs[r, kv * g:(kv + 1) * g, :].reshape(r.size * g, D)
+            z = scale * (qg @ K[:, kv, :].T)                      # [r * g, n]
+            z = np.where(np.repeat(mask[r], g, axis=0), z, -np.inf)
             p = softmax_rows(z)
-            out[c0:c0 + r.size, kv * g:(kv + 1) * g] = np.einsum("rgt,td->rgd", p, V[:, kv, :])
+            out[c0:c0 + r.size, kv * g:(kv + 1) * g] = (p @ V[:, kv, :]).reshape(r.size, g, D)
     return out
+
+
+def _prefill_job_args(s, q, q_fmt, k_pool, v_pool, kv_fmt, block_tables, query_start_loc,
+                      context_lens, scale, window, k_scale, v_scale, rows):
+    a, b = int(query_start_loc[s]), int(query_start_loc[s + 1])
+    n = int(context_lens[s])
+    K = reassemble(k_pool, kv_fmt, k_scale, block_tables[s], n)
+    V = reassemble(v_pool, kv_fmt, v_scale, block_tables[s], n)
+    return (q_bits_to_f64(q[a:b], q_fmt), K, V, float(scale), int(window),
+            None if rows is None else rows[s])
+
+
+# Inputs of the current multi-process prefill, inherited by forked workers.
+_FORK_PREFILL = None
+
+
+def _prefill_seq_job(s):
+    return _prefill_one(_prefill_job_args(s, *_FORK_PREFILL))
 
 
 def prefill(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
@@ -221,22 +240,30 @@ def prefill(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool: np.ndarray,
             rows: Optional[dict] = None, workers: int = 1) -> np.ndarray:
     """Chunked-prefill attention.  q: raw bits [sumQ, Hq, D].  Returns float64
     [sumQ, Hq, D]; with ``rows`` = {seq: [row indices within the chunk]} only
-    those rows are computed and returned in a dict {seq: [len, Hq, D]}."""
+    those rows are computed and returned in a dict {seq: [len, Hq, D]}.
+
+    ``workers`` > 1 splits whole sequences over forked processes (which read
+    the inputs they inherit); each sequence is computed identically, so the
+    result does not depend on the worker count."""
+    global _FORK_PREFILL
     B = len(context_lens)
     seqs = list(range(B)) if rows is None else sorted(rows)
-    jobs = []
-    for s in seqs:
-        a, b = int(query_start_loc[s]), int(query_start_loc[s + 1])
-        n = int(context_lens[s])
-        K = reassemble(k_pool, kv_fmt, k_scale, block_tables[s], n)
-        V = reassemble(v_pool, kv_fmt, v_scale, block_tables[s], n)
-        jobs.append((q_bits_to_f64(q[a:b], q_fmt), K, V, float(scale), int(window),
-                     None if rows is None else rows[s]))
-    if workers > 1:
-        with ProcessPoolExecutor(max_workers=workers) as ex:
-            res = list(ex.map(_prefill_one, jobs))
+    args = (q, q_fmt, k_pool, v_pool, kv_fmt, block_tables, query_start_loc, context_lens,
+            scale, window, k_scale, v_scale, rows)
+    if workers > 1 and len(seqs) > 1:
+        _FORK_PREFILL = args
+        try:
+            ctx = multiprocessing.get_context("fork")
+            with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+                # longest sequences first: the pool's last jobs are short ones
+                order = sorted(seqs, key=lambda j: -int(query_start_loc[j + 1] - query_start_loc[j])
+                               * int(context_lens[j]))
+                done = dict(zip(order, ex.map(_prefill_seq_job, order)))
+            res = [done[j] for j in seqs]
+        finally:
+            _FORK_PREFILL = None
     else:
-        res = [_prefill_one(j) for j in jobs]
+        res = [_prefill_one(_prefill_job_args(j, *args)) for j in seqs]
     if rows is not None:
         return dict(zip(seqs, res))
     return np.concatenate(res, axis=0) if res else np.zeros(q.shape, np.float64)
@@ -278,10 +305,10 @@ def prefill_chunked_local(q: np.ndarray, q_fmt: str, k_pool: np.ndarray, v_pool:
         g = Hq // Hkv
         mask = chunked_local_mask(n, Q, chunk)
         for kv in range(Hkv):
-            qg = qs[:, kv * g:(kv + 1) * g, :]
-            z = scale * np.einsum("rgd,td->rgt", qg, K[:, kv, :])
-            z = np.where(mask[:, None, :], z, -np.inf)
-            out[a:b, kv * g:(kv + 1) * g] = np.einsum("rgt,td->rgd", softmax_rows(z), V[:, kv, :])
+            qg = qs[:, kv * g:(kv + 1) * g, :].reshape(Q * g, D)
+            z = scale * (qg @ K[:, kv, :].T)                      # [Q * g, n]
+            z = np.where(np.repeat(mask, g, axis=0), z, -np.inf)
+            out[a:b, kv * g:(kv + 1) * g] = (softmax_rows(z) @ V[:, kv, :]).reshape(Q, g, D)
     return out
 
 

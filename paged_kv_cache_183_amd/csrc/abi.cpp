@@ -238,11 +238,14 @@ vllm_status plan_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t m
   if (x.pages_bound >= ((int64_t)1 << 31))
     return fail(VLLM_ERR_UNSUPPORTED, "batch too large: %lld pages of work", (long long)x.pages_bound);
   x.chunk_pages = chunk_tokens / 16;
-  if (x.chunk_pages > 0)
+  if (x.chunk_pages > 0) {
+    // fixed chunks: ceil(T / C) <= ceil(pages_bound / C) whatever the grid
     x.max_chunks = (x.pages_bound + x.chunk_pages - 1) / x.chunk_pages;
-  else
-    x.max_chunks = std::min<int64_t>(vp::kMaxWorkers,
-                                     (x.pages_bound + vp::kMinChunkPages - 1) / vp::kMinChunkPages);
+  } else {
+    // automatic split: one chunk per wave, ceil(T / ceil(T / W)) <= W chunks,
+    // so the slots cover the largest wave count the launch can pick
+    x.max_chunks = vp::decode_workers_bound(x.pages_bound);
+  }
   if (x.max_chunks < 1) x.max_chunks = 1;
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   const size_t pieces = (size_t)x.max_chunks * 2 * (size_t)x.head_chunk;
@@ -525,6 +528,11 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   p.num_workers = std::max<int32_t>(vp::kDecodeWaves,
                                     (p.num_workers + vp::kDecodeWaves - 1) / vp::kDecodeWaves *
                                         vp::kDecodeWaves);
+  // The automatic split makes one chunk per wave: the workspace holds the
+  // pieces of at most max_chunks of them.
+  if (dp.chunk_pages == 0 && p.num_workers > dp.max_chunks)
+    return fail(VLLM_ERR_HIP, "internal: %d decode waves for %lld workspace chunks",
+                (int)p.num_workers, (long long)dp.max_chunks);
   p.score_base = scale * 1.4426950408889634f;
   p.score_scale = p.score_base * ks;
   p.out_scale = vs;

@@ -41,6 +41,7 @@
 //    the end of the stretch they read a spare page of the workspace, which
 //    stays in L2) so that the compiler can keep the buffers in flight across
 //    iterations.
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 #include <utility>
@@ -276,7 +277,9 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int s, int hk,
       *reinterpret_cast<uint2*>(static_cast<uint8_t*>(pool) + dst) = make_uint2(o[0], o[1]);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the stores are done
+  // the stores are done before any lane of the wave reads the page back:
+  // release for the writing lanes, acquire for the reading ones
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
 }
 
 // AP: with the fused cache write of each sequence's newest token (a variant
@@ -827,31 +830,42 @@ static const void* merge_kernel_for(int D, int q_fmt, int gc) {
   return nullptr;
 }
 
+// Per-device caches of the CU count and of each kernel variant's resident
+// workgroups per CU: filled on first use, read without locks (a racing first
+// use computes the same value twice).
+constexpr int kMaxDevices = 64;
+constexpr int kVariants = 2 * 2 * 4 * 16;     // (append, D = 128, kv format, q format, G)
+static std::atomic<int> g_cus[kMaxDevices];
+static std::atomic<int> g_occ[kMaxDevices][kVariants];
+
 int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk,
                    bool append) {
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0;
-    int v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
-      (void)hipGetLastError();
-      v = 256;
-    }
-    cus = v;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    dev = 0;
   }
-  // workgroups resident per CU, queried once per kernel variant
-  static constexpr int kVariants = 2 * 2 * 4 * 16;     // (append, D = 128, kv format, q format, G)
-  static int occ_cache[kVariants] = {0};
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  int cus = cached ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    if (cached) g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
   int per_cu = 4;
   const int vi = (((int)append * 2 + (head_dim == 128)) * 4 + kv_fmt) * 16 + q_fmt * 8 + (head_chunk - 1);
-  if (vi >= 0 && vi < kVariants && occ_cache[vi] > 0) {
-    per_cu = occ_cache[vi];
+  const bool vcached = cached && vi >= 0 && vi < kVariants;
+  const int occ_seen = vcached ? g_occ[dev][vi].load(std::memory_order_relaxed) : 0;
+  if (occ_seen > 0) {
+    per_cu = occ_seen;
   } else if (const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, head_chunk, append)) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, kNW * 64, 0) == hipSuccess && occ > 0) {
       per_cu = occ;
-      if (vi >= 0 && vi < kVariants) occ_cache[vi] = occ;
+      if (vcached) g_occ[dev][vi].store(occ, std::memory_order_relaxed);
     } else {
       (void)hipGetLastError();
     }
@@ -860,11 +874,8 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
     const int v = atoi(e);
     if (v > 0) per_cu = v;
   }
-  int64_t w = (int64_t)cus * per_cu * kNW;
-  const int64_t by_pages = (pages_bound + kMinChunkPages - 1) / kMinChunkPages;
-  w = min(w, max((int64_t)kNW, by_pages));
-  w = min(w, (int64_t)kMaxWorkers);
-  return (int)((w + kNW - 1) / kNW * kNW);
+  const int64_t w = (int64_t)cus * per_cu * kNW;
+  return (int)min(decode_workers_bound(pages_bound), (w + kNW - 1) / kNW * kNW);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream,

@@ -247,7 +247,18 @@ inline int decode_head_chunk(int g) {
   return 1;
 }
 
-// Workers (waves) the decode grid uses for an upper bound of the page count.
+// Largest wave count decode_workers returns for an upper bound of the page
+// count: at least one workgroup, at most kMaxWorkers, about kMinChunkPages
+// pages per wave, a whole number of workgroups.
+constexpr int64_t decode_workers_bound(int64_t pages_bound) {
+  int64_t w = (pages_bound + kMinChunkPages - 1) / kMinChunkPages;
+  w = w < kDecodeWaves ? kDecodeWaves : w;
+  w = w > kMaxWorkers ? kMaxWorkers : w;
+  return (w + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+}
+
+// Workers (waves) the decode grid uses for an upper bound of the page count
+// (never more than decode_workers_bound(pages_bound)).
 int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk,
                    bool append = false);
 

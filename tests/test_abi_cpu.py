@@ -98,27 +98,59 @@ def test_decode_validation():
             **{**d, "partition_size": 512, "workspace": torch.zeros(8, dtype=torch.uint8)})
 
 
+def _ws_layout(B, Hq, Hkv, D, chunks):
+    """Bytes of a decode workspace holding ``chunks`` chunks: piece records
+    (2 ints per unit) + page prefix (B + 3 ints) + 2 pieces per chunk of
+    G x (D + 2) floats + one spare page, each region rounded up to 256 bytes."""
+    g = Hq // Hkv
+    gc = g if g <= 8 else max(c for c in range(1, 9) if g % c == 0)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    pieces = chunks * 2 * gc
+    units = B * Hkv * (g // gc)
+    return (up(units * 8) + up((B + 3) * 4) + up(pieces * D * 4) + 2 * up(pieces * 4)
+            + up(16 * D * 2))
+
+
+def _pages_bound(B, Hq, Hkv, mb):
+    g = Hq // Hkv
+    gc = g if g <= 8 else max(c for c in range(1, 9) if g % c == 0)
+    return B * Hkv * (g // gc) * mb
+
+
 def test_workspace_size():
-    # piece records (2 ints per unit) + page prefix (B + 3 ints) + 2 pieces
-    # per chunk of G x (D + 2) floats + one spare page, each region rounded
-    # up to 256 bytes
     def expect(B, Hq, Hkv, D, mb, part):
-        g = Hq // Hkv
-        gc = g if g <= 8 else max(c for c in range(1, 9) if g % c == 0)
-        bound = B * Hkv * (g // gc) * mb
-        chunks = -(-bound // (part // 16)) if part else min(4096, -(-bound // 4))
-        chunks = max(chunks, 1)
-        up = lambda v: (v + 255) // 256 * 256
-        pieces = chunks * 2 * gc
-        units = B * Hkv * (g // gc)
-        return (up(units * 8) + up((B + 3) * 4) + up(pieces * D * 4) + 2 * up(pieces * 4)
-                + up(16 * D * 2))
+        bound = _pages_bound(B, Hq, Hkv, mb)
+        if part:
+            chunks = -(-bound // (part // 16))
+        else:          # one chunk per wave: up to the launch's largest wave count
+            chunks = min(4096, -(-max(4, -(-bound // 4)) // 4) * 4)
+        return _ws_layout(B, Hq, Hkv, D, max(chunks, 1))
     for args in [(4, 4, 2, 64, 3, 0), (32, 32, 8, 128, 256, 0), (16, 40, 8, 128, 2048, 0),
-                 (4, 4, 2, 64, 3, 16), (32, 32, 8, 128, 256, 512), (3, 16, 1, 128, 10, 0)]:
+                 (4, 4, 2, 64, 3, 16), (32, 32, 8, 128, 256, 512), (3, 16, 1, 128, 10, 0),
+                 (1, 4, 2, 128, 10, 0), (1, 8, 1, 64, 3, 0)]:
         assert P.vllm_paged_attn_workspace_size(*args) == expect(*args), args
     assert P.vllm_paged_attn_workspace_size(4, 3, 2, 64, 3, 0) == 0     # Hq % Hkv -> 0
     assert P.vllm_paged_attn_workspace_size(4, 4, 2, 64, 3, 24) == 0    # invalid partition -> 0
     assert P.vllm_paged_attn_workspace_size(4, 4, 2, 96, 3, 0) == 0     # unsupported D -> 0
+
+
+def test_workspace_holds_every_split_the_launch_can_make():
+    """Full tables (T = the page bound) and every wave count W the automatic
+    split may launch (a multiple of 4 workgroup waves, up to one wave per 4
+    pages and at most 4096): the kernel cuts T pages into ceil(T / ceil(T / W))
+    chunks and writes 2 pieces per chunk, all of which must fit in the
+    workspace the library asks for.  Small shapes are where a wave count
+    rounded up to whole workgroups can exceed the page count / 4."""
+    for B in (1, 2, 3):
+        for Hq, Hkv in ((1, 1), (4, 2), (8, 1), (40, 8), (16, 1)):
+            for D in (64, 128):
+                for mb in (1, 2, 3, 5, 10, 17, 64):
+                    ws = P.vllm_paged_attn_workspace_size(B, Hq, Hkv, D, mb, 0)
+                    T = _pages_bound(B, Hq, Hkv, mb)
+                    wmax = min(4096, -(-max(4, -(-T // 4)) // 4) * 4)
+                    for W in range(4, wmax + 1, 4):
+                        chunks = -(-T // -(-T // W))
+                        assert _ws_layout(B, Hq, Hkv, D, chunks) <= ws, (B, Hq, Hkv, D, mb, W)
 
 
 def _prefill_args(sumq=5, B=2, Hq=4, Hkv=2, D=128, dt=torch.bfloat16, kvdt=None, mb=3):

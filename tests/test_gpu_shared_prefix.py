@@ -2,8 +2,8 @@
 fp64 oracle's decode (the same definition: the shared pages are part of every
 sequence's context through its block table).
 
-Bars: element by element within the stated tolerances (or one output ulp
-where that is larger); properties the arithmetic order makes exact are
+Bars: element by element within the stated tolerances plus half an ulp of
+the output format; properties the arithmetic order makes exact are
 checked bit for bit."""
 import numpy as np
 import pytest
@@ -133,16 +133,19 @@ def test_workspace_caller_and_internal_identical():
     assert torch.equal(a, b)
 
 
+@pytest.mark.fullsize("decode3")
 def test_full_size_prefix_shared_fp8():
     """The full prefix-shared workload (128 sequences, 256 shared pages, FP8)
-    in the launch configuration of the benchmark; sampled sequences."""
+    in the launch configuration of the benchmark: every output element
+    against the oracle's decode reference (computed by the background oracle
+    process from the same seeded inputs)."""
+    import _fullsize
     case = make_case(3)
     kc, vc = gpu_fill(case)
     out = to_f64(shared_decode(case, kc, vc, 256))
-    kp, vp = oracle_pools(case)
-    seqs = [0, 1, 63, 127]
-    assert_close(case, out[seqs], oracle(case, kp, vp, seqs=seqs))
-    assert np.all(np.isfinite(out))
+    ref = _fullsize.result("decode3")
+    assert ref.shape == out.shape
+    assert_close(case, out, ref)
 
 
 def test_many_whole_units_in_one_chunk():

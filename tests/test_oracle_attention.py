@@ -281,6 +281,21 @@ def test_prefill_vs_brute_force(over):
         assert np.max(np.abs(out[qsl[s]:qsl[s + 1]] - np.array(ref))) < 1e-12
 
 
+def test_prefill_worker_count_invariance():
+    """Forked workers (longest sequences first) give the single process's
+    result bit for bit, for all rows and for a row selection."""
+    case = make_case(4, B=5, qlen_range=(1, 140), cached_range=(0, 300), Hq=8, Hkv=2, D=64,
+                     window=50)
+    kp, vp = oracle_pools(case)
+    assert np.array_equal(oracle_prefill(case, kp, vp, workers=1),
+                          oracle_prefill(case, kp, vp, workers=3))
+    qsl = case.query_start_loc.numpy()
+    rows = {s: [0, int(qsl[s + 1] - qsl[s]) - 1] for s in (0, 2, 4) if qsl[s + 1] > qsl[s]}
+    a = oracle_prefill(case, kp, vp, rows=rows, workers=1)
+    b = oracle_prefill(case, kp, vp, rows=rows, workers=2)
+    assert a.keys() == b.keys() and all(np.array_equal(a[s], b[s]) for s in a)
+
+
 def test_prefill_single_token_equals_decode():
     case = make_case(4, B=4, qlen_range=(1, 1), cached_range=(5, 70), Hq=8, Hkv=2, D=64, window=20)
     kp, vp = oracle_pools(case)
