@@ -60,8 +60,9 @@ extern "C" {
 
 /* Version 2 appended k_scales / v_scales to vllm_attn_opts; version 3 added
  * FP8 pools in vllm_paged_attn_prefill and the local-attention and block
- * manager entry points (no struct changed). */
-#define VLLM_PAGED_ABI_VERSION 3
+ * manager entry points; version 4 added vllm_paged_attn_decode_noalloc (no
+ * struct changed). */
+#define VLLM_PAGED_ABI_VERSION 4
 #define VLLM_PAGED_BLOCK_SIZE 16
 
 typedef enum vllm_status {
@@ -222,6 +223,32 @@ size_t vllm_paged_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
                                       int32_t max_blocks_per_seq,
                                       int32_t partition_size);
+
+/*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  The same computation and result, bit for bit, as
+ * vllm_paged_attn_decode with the same arguments; instead of a caller's
+ * workspace or a stream-ordered allocation it uses a scratch array of
+ * VLLM_PAGED_NOALLOC_SCRATCH_BYTES bytes that the library's code object
+ * holds on each GPU it runs on until the process ends (its address is looked
+ * up once per device, on the first call there).
+ *   arguments  as vllm_paged_attn_decode; opts->workspace must be NULL.
+ * Errors: VLLM_ERR_WORKSPACE when the sizes need more scratch than that
+ * (compare vllm_paged_attn_workspace_size with the limit: e.g. 32 sequences
+ * of up to 4096 tokens at Hq = 32, Hkv = 8, D = 128 need about 16 MiB).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; the kernels rewrite whatever they read, so nothing needs clearing,
+ * but calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.
+ */
+#define VLLM_PAGED_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+vllm_status vllm_paged_attn_decode_noalloc(vllm_tensor* out, const vllm_tensor* q,
+                                           const vllm_tensor* k_cache, const vllm_tensor* v_cache,
+                                           const vllm_tensor* block_tables,
+                                           const vllm_tensor* context_lens, float scale,
+                                           int32_t window, const vllm_attn_opts* opts,
+                                           void* hip_stream);
 
 /*
  * Decode with a prefix shared by the whole batch read once ("cascade"): the

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     vllm_abi_version,
     vllm_last_error,
     vllm_paged_attn_decode,
+    vllm_paged_attn_decode_noalloc,
     vllm_paged_attn_decode_shared_prefix,
     vllm_paged_attn_prefill,
     vllm_paged_attn_shared_prefix_workspace_size,

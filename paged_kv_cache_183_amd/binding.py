@@ -32,6 +32,7 @@ BLOCK_SIZE = 16
 
 EXPORTED = ["vllm_abi_version", "vllm_last_error", "vllm_paged_cache_write",
             "vllm_paged_attn_decode", "vllm_paged_attn_workspace_size",
+            "vllm_paged_attn_decode_noalloc",
             "vllm_paged_attn_decode_shared_prefix", "vllm_paged_attn_shared_prefix_workspace_size",
             "vllm_paged_attn_prefill", "vllm_paged_attn_decode_append", "vllm_paged_chunked_local_plan",
             "vllm_paged_chunked_local_virtual_count", "vllm_paged_recycle_pages",
@@ -73,6 +74,9 @@ def _load():
     lib.vllm_paged_attn_decode.restype = ctypes.c_int
     lib.vllm_paged_attn_decode.argtypes = [T, T, T, T, T, T, ctypes.c_float, ctypes.c_int32, O,
                                            ctypes.c_void_p]
+    lib.vllm_paged_attn_decode_noalloc.restype = ctypes.c_int
+    lib.vllm_paged_attn_decode_noalloc.argtypes = [T, T, T, T, T, T, ctypes.c_float,
+                                                   ctypes.c_int32, O, ctypes.c_void_p]
     lib.vllm_paged_attn_workspace_size.restype = ctypes.c_size_t
     lib.vllm_paged_attn_workspace_size.argtypes = [ctypes.c_int32] * 6
     lib.vllm_paged_attn_decode_shared_prefix.restype = ctypes.c_int
@@ -207,6 +211,22 @@ def vllm_paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _check(LIB.vllm_paged_attn_decode(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
                                       ctypes.c_int32(window), ctypes.byref(o),
                                       ctypes.c_void_p(_stream(stream))))
+
+
+# Scratch bytes of vllm_paged_attn_decode_noalloc (VLLM_PAGED_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def vllm_paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   window=0, k_scale=0.0, v_scale=0.0, partition_size=0,
+                                   stream=None) -> None:
+    """Decode attention into ``out`` [B, Hq, D] on the library's own scratch
+    (no allocation, no workspace argument)."""
+    args = [tensor_desc(x) for x in (out, q, k_cache, v_cache, block_tables, context_lens)]
+    o = _opts(k_scale, v_scale, partition_size)
+    _check(LIB.vllm_paged_attn_decode_noalloc(*[ctypes.byref(a) for a in args],
+                                              ctypes.c_float(scale), ctypes.c_int32(window),
+                                              ctypes.byref(o), ctypes.c_void_p(_stream(stream))))
 
 
 def vllm_paged_attn_shared_prefix_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,

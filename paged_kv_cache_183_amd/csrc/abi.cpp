@@ -393,6 +393,44 @@ size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
 
 namespace {
 
+// Scratch of the allocation-free decode (vllm_paged_attn_decode_noalloc): a
+// file-scope device array in the library's code object, so each GPU the
+// library runs on holds its own copy for the life of the process and no call
+// allocates.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, looked up once per device (with the
+// device current) on the entry point's first call there, and only that
+// address is ever passed to a kernel.  The decode kernels rewrite every part
+// of their workspace they read, so the array needs no clearing between calls;
+// calls that overlap on one GPU share it and race.
+constexpr size_t kScratchBytes = VLLM_PAGED_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+vllm_status scratch_address(void** out) {
+  int dev = 0;
+  VP_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(VLLM_ERR_UNSUPPORTED, "device %d: the allocation-free decode supports devices "
+                "0..%d", dev, kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(VLLM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VLLM_OK;
+}
+
 // Decode, optionally with the first shared_pages pages of every sequence
 // handled by the shared-prefix pass (read once per kv-head for the batch).
 // Largest work unit (query heads) that the decode kernel with the fused
@@ -405,7 +443,7 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
                        const vllm_tensor* context_lens, int32_t shared_pages, float scale,
                        int32_t window, const vllm_attn_opts* opts, void* hip_stream,
                        const vllm_tensor* k_new = nullptr, const vllm_tensor* v_new = nullptr,
-                       const vllm_tensor* slot_mapping = nullptr) {
+                       const vllm_tensor* slot_mapping = nullptr, bool noalloc = false) {
   VP_TRY(check_tensor(out, "out", 3));
   VP_TRY(check_tensor(q, "q", 3));
   VP_TRY(check_tensor(k_cache, "k_cache", 4));
@@ -478,6 +516,16 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   if (shared_pages > 0 && !(scale > 0.0f))
     return fail(VLLM_ERR_INVALID_ARG, "shared prefix: scale must be positive");
   VP_TRY(plan_decode(B, Hq, Hkv, D, max_blocks, chunk_tokens, shared_pages, &dp));
+  if (noalloc) {
+    if (opts && opts->workspace)
+      return fail(VLLM_ERR_INVALID_ARG,
+                  "the allocation-free decode uses the library's scratch: opts.workspace must be NULL");
+    if (dp.bytes > kScratchBytes)
+      return fail(VLLM_ERR_WORKSPACE,
+                  "decode needs %zu bytes of scratch; the allocation-free decode has %zu "
+                  "(a smaller batch, a larger partition_size, or vllm_paged_attn_decode with a "
+                  "workspace)", dp.bytes, kScratchBytes);
+  }
   if (B == 0) return ok();
   if (opts && opts->workspace && opts->workspace_bytes < dp.bytes)
     return fail(VLLM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", opts->workspace_bytes, dp.bytes);
@@ -549,7 +597,9 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
 
   void* ws = nullptr;
   bool owned = false;
-  if (opts && opts->workspace) {
+  if (noalloc) {
+    VP_TRY(scratch_address(&ws));        // after every argument check
+  } else if (opts && opts->workspace) {
     ws = opts->workspace;
     VP_TRY(check_align(ws, "workspace", 256));
     VP_TRY(check_device_ptr(ws, "workspace"));
@@ -669,6 +719,16 @@ vllm_status vllm_paged_attn_decode_append(vllm_tensor* out, const vllm_tensor* q
     return fail(VLLM_ERR_INVALID_ARG, "k_new, v_new and slot_mapping are required");
   return run_decode(out, q, k_cache, v_cache, block_tables, context_lens, 0, scale, window, opts,
                     hip_stream, k_new, v_new, slot_mapping);
+}
+
+vllm_status vllm_paged_attn_decode_noalloc(vllm_tensor* out, const vllm_tensor* q,
+                                           const vllm_tensor* k_cache, const vllm_tensor* v_cache,
+                                           const vllm_tensor* block_tables,
+                                           const vllm_tensor* context_lens, float scale,
+                                           int32_t window, const vllm_attn_opts* opts,
+                                           void* hip_stream) {
+  return run_decode(out, q, k_cache, v_cache, block_tables, context_lens, 0, scale, window, opts,
+                    hip_stream, nullptr, nullptr, nullptr, /*noalloc=*/true);
 }
 
 vllm_status vllm_paged_attn_decode_shared_prefix(vllm_tensor* out, const vllm_tensor* q,

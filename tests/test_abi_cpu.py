@@ -98,6 +98,33 @@ def test_decode_validation():
             **{**d, "partition_size": 512, "workspace": torch.zeros(8, dtype=torch.uint8)})
 
 
+def test_noalloc_decode_validation():
+    """The allocation-free decode checks everything on the host before it
+    looks up its scratch: a caller workspace is refused, sizes beyond the
+    scratch are refused, host pointers are refused."""
+    m = re.search(r"#define\s+VLLM_PAGED_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert Bd.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    a = _decode_args()
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_attn_decode_noalloc, **a)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_decode_noalloc, **{**a, "window": -1})
+    # 16 sequences of 2048 pages at Hq = 40, Hkv = 8, with 16-token chunks:
+    # far more scratch than the array holds
+    big = _decode_args(B=16, Hq=40, Hkv=8, D=128, mb=2048)
+    assert P.vllm_paged_attn_workspace_size(16, 40, 8, 128, 2048, 16) > Bd.NOALLOC_SCRATCH_BYTES
+    _expect(Bd.VLLM_ERR_WORKSPACE, P.vllm_paged_attn_decode_noalloc, **big, partition_size=16)
+    # a caller workspace is not accepted (the binding never passes one: call the C ABI directly)
+    args = [Bd.tensor_desc(a[k]) for k in ("out", "q", "k_cache", "v_cache", "block_tables",
+                                           "context_lens")]
+    o = Bd._opts()
+    o.workspace = 256
+    o.workspace_bytes = 1 << 20
+    st = Bd.LIB.vllm_paged_attn_decode_noalloc(*[ctypes.byref(x) for x in args],
+                                               ctypes.c_float(0.125), ctypes.c_int32(0),
+                                               ctypes.byref(o), ctypes.c_void_p(0))
+    assert st == Bd.VLLM_ERR_INVALID_ARG and "workspace" in P.vllm_last_error()
+
+
 def _ws_layout(B, Hq, Hkv, D, chunks):
     """Bytes of a decode workspace holding ``chunks`` chunks: piece records
     (2 ints per unit) + page prefix (B + 3 ints) + 2 pieces per chunk of
