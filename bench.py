@@ -25,13 +25,9 @@ import os
 import sys
 import time
 
-# The CPU oracle's workers each run one sequence at a time; keep numpy's BLAS
-# single-threaded in them (set before numpy is imported).
-os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
-os.environ.setdefault("MKL_NUM_THREADS", "1")
-
 import numpy as np  # noqa: E402
 import torch  # noqa: E402
+from threadpoolctl import threadpool_limits  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -120,11 +116,21 @@ def prefill_work(case, chunk: int = 0) -> dict:
 def cpu_baseline_prefill(case, seconds: float, chunk: int = 0) -> dict:
     """The fp64 oracle, unchanged, on the last query rows of sequences of
     the chunked-prefill batch, for about ``seconds`` (chunk > 0: its
-    chunked-local attention, one sequence at a time)."""
+    chunked-local attention, one sequence at a time, with every BLAS thread
+    of the host's share)."""
+    if chunk:
+        with threadpool_limits(limits=host_cores()["used"], user_api="blas"):
+            return _cpu_baseline_prefill(case, seconds, chunk)
+    with threadpool_limits(limits=1, user_api="blas"):     # one per forked worker
+        return _cpu_baseline_prefill(case, seconds, chunk)
+
+
+def _cpu_baseline_prefill(case, seconds: float, chunk: int = 0) -> dict:
     import numpy as np
     from oracle import attention as A
     from oracle import scatter as S
-    cores = min(16, len(os.sched_getaffinity(0)))
+    hc = host_cores()
+    cores = hc["used"]
     pool0 = raw_bits(case.sentinel_pool())
     slots = case.fill_slots.numpy()
     kp = S.cache_write_fast(pool0, raw_bits(case.fill_k), slots, case.kv_src_dtype, case.kv_dtype)
@@ -169,7 +175,7 @@ def cpu_baseline_prefill(case, seconds: float, chunk: int = 0) -> dict:
     dt = time.time() - t0
     what = f"chunked-local attention ({chunk}-token chunks) of " if chunk else ""
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": 1 if chunk else cores, "kind": "oracle",
+            "cores": cores, "cores_visible": hc["visible"], "kind": "oracle",
             "sample": f"{what}the last {per} query rows (all heads) of sequences 0..{done[-1]} of "
                       f"the chunked-prefill batch ({len(done)} of {case.num_seqs}), {dt:.1f} s"}
 
@@ -296,13 +302,31 @@ def bench_block_manager(steps: int = 20, num_seqs: int = 256, prompt: int = 1024
                     "included); kernel time in profiles/block_manager_decode_step_kernel_trace.txt"}
 
 
+# Worker processes of the CPU oracle: the host's CPU share for one GPU (the
+# visible core count can be larger than what the host gives one GPU's jobs).
+CPU_SHARE = 16
+
+
+def host_cores() -> dict:
+    vis = len(os.sched_getaffinity(0))
+    return {"visible": vis, "used": max(1, min(CPU_SHARE, vis))}
+
+
 def cpu_baseline(case, seconds: float) -> dict:
     """The fp64 oracle, unchanged, on this host: whole decode steps (cache
     write of the batch's new tokens + decode of every sequence) repeated for
-    about ``seconds``."""
+    about ``seconds`` (at least one step)."""
+    # one BLAS thread in each of the forked workers (the host may default
+    # BLAS to every core, which the workers would then oversubscribe)
+    with threadpool_limits(limits=1, user_api="blas"):
+        return _cpu_baseline(case, seconds)
+
+
+def _cpu_baseline(case, seconds: float) -> dict:
     from oracle import attention as A
     from oracle import scatter as S
-    cores = min(16, len(os.sched_getaffinity(0)))
+    hc = host_cores()
+    cores = hc["used"]
     t0 = time.time()
     pool0 = raw_bits(case.sentinel_pool())
     slots = case.fill_slots.numpy()
@@ -329,10 +353,292 @@ def cpu_baseline(case, seconds: float) -> dict:
     dt = (time.time() - t0) / steps
     by = decode_bytes(case)
     return {"value": round((by["decode"] + by["write"]) / dt / 1e9, 4), "unit": "GB/s",
-            "cores": cores, "kind": "oracle",
+            "cores": cores, "cores_visible": hc["visible"], "kind": "oracle",
+            "seqs_per_s": round(case.num_seqs / dt, 3),
             "sample": f"{steps} whole decode step(s) of the benchmark batch "
                       f"({case.num_seqs} seqs, cache write + fp64 decode), {dt:.2f} s each; "
-                      f"seqs/s {case.num_seqs / dt:.2f}; pool build {setup:.1f} s untimed"}
+                      f"pool build {setup:.1f} s untimed"}
+
+
+def _events(n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def bench_scatter(P, case, view, fill_k, fill_v, fill_slots, kc, vc, iters: int = 10) -> dict:
+    """The cache write of a whole pool fill (every token of the batch), timed
+    with HIP events around each call; bytes = the rows read plus the rows
+    written plus the slots."""
+    stream = torch.cuda.current_stream()
+    T = int(fill_slots.numel())
+    for _ in range(2):
+        P.vllm_paged_cache_write(fill_k, fill_v, fill_slots, view(kc), view(vc),
+                                 k_scale=case.k_scale, v_scale=case.v_scale)
+    torch.cuda.synchronize()
+    evs = _events(iters)
+    for a, b in evs:
+        a.record(stream)
+        P.vllm_paged_cache_write(fill_k, fill_v, fill_slots, view(kc), view(vc),
+                                 k_scale=case.k_scale, v_scale=case.v_scale)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    mean = sum(ms) / len(ms)
+    row = case.num_kv_heads * case.head_dim
+    nbytes = T * row * 2 * (fill_k.element_size() + ELEM_BYTES[case.kv_dtype]) + T * 8
+    gbs = nbytes / (mean * 1e-3) / 1e9
+    return {"workload": case.name + "_pool_fill", "tokens": T, "bytes_per_call": nbytes,
+            "ms_per_call": round(mean, 5), "p10_ms": round(float(np.percentile(ms, 10)), 5),
+            "p90_ms": round(float(np.percentile(ms, 90)), 5), "GB_per_s": round(gbs, 2),
+            "roofline": {"bound": "hbm", "kernel": "cache_write_kernel", "achieved": round(gbs, 2),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBPS, 4)}}
+
+
+def read_ceiling(P, kv_bytes: int, page_bytes: int, iters: int = 20) -> dict:
+    """The bandwidth of a plain read of kv_bytes in random page_bytes pages
+    (vllm_paged_read_pages: the decode's load shape with no arithmetic), over
+    buffer copies rotated so that no call finds its pages in the 256 MB
+    last-level cache; HIP events around each call."""
+    dev = torch.device("cuda", 0)
+    pages = max(1, kv_bytes // page_bytes)
+    nbytes = pages * page_bytes
+    R = max(2, math.ceil(3 * 256e6 / nbytes) + 1)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    g = torch.Generator().manual_seed(17)
+    ids = torch.randperm(pages, generator=g).to(torch.int32).to(dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    best = None
+    for waves in (cus * 8, cus * 16):       # 2 and 4 waves per SIMD: the faster one counts
+        sink = torch.empty(waves, dtype=torch.int32, device=dev)
+        for i in range(2 * R):
+            P.vllm_paged_read_pages(bufs[i % R], ids, page_bytes, sink)
+        torch.cuda.synchronize()
+        evs = _events(iters)
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            P.vllm_paged_read_pages(bufs[i % R], ids, page_bytes, sink)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in evs]
+        mean = sum(ms) / len(ms)
+        if best is None or mean < best[1]:
+            best = (waves, mean)
+    del bufs
+    torch.cuda.empty_cache()
+    waves, mean = best
+    return {"kernel": "read_pages_kernel", "page_bytes": page_bytes, "bytes_per_call": nbytes,
+            "waves": waves, "ms_per_call": round(mean, 5),
+            "GB_per_s": round(nbytes / (mean * 1e-3) / 1e9, 2),
+            "frac_of_peak": round(nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def bench_decode(idx: int, case, args, steps: int, warmup: int, cpu=None,
+                 shared_prefix: bool = True, separate_write: bool = False,
+                 partition: int = 0, graph: bool = False) -> dict:
+    """Time decode steps of workload ``idx`` on the GPU: each step writes the
+    batch's new tokens into the pool and decodes the batch (one fused call
+    unless separate_write, or the shared-prefix decode of a prefix-shared
+    batch).  Returns the measurement as a dict (throughput, roofline, the
+    scatter of the pool fill, the read ceiling of the same bytes)."""
+    import paged_kv_cache_183_amd as P
+    cfg = CONFIGS[idx]
+    shared_tokens = int(cfg.get("shared_tokens", 0)) if shared_prefix else 0
+    by = decode_bytes(case, shared_tokens)
+    dev = torch.device("cuda", 0)
+    view = (lambda t: t) if case.kv_dtype == "e4m3" else \
+        (lambda t: t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16))
+
+    fill_k, fill_v = case.fill_k.to(dev), case.fill_v.to(dev)
+    fill_slots = case.fill_slots.to(dev)
+    kc0, vc0 = case.sentinel_pool().to(dev), case.sentinel_pool().to(dev)
+    P.vllm_paged_cache_write(fill_k, fill_v, fill_slots, view(kc0), view(vc0),
+                             k_scale=case.k_scale, v_scale=case.v_scale)
+    scatter = bench_scatter(P, case, view, fill_k, fill_v, fill_slots, kc0, vc0)
+    pool_bytes = 2 * kc0.numel() * kc0.element_size()
+    R = args.replicas or max(2, math.ceil(3 * 256e6 / pool_bytes) + 1)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    rows = case.step_rows.to(dev)
+    new_k, new_v = fill_k[rows].contiguous(), fill_v[rows].contiguous()
+    new_slots = fill_slots[rows].contiguous()
+    del fill_k, fill_v, fill_slots
+    q = case.q.to(dev)
+    out = torch.empty_like(q)
+    bt, ctx = case.block_tables.to(dev), case.context_lens.to(dev)
+    part = partition or case.partition
+    shared_pages = shared_tokens // 16
+    if shared_pages:
+        ws_bytes = P.vllm_paged_attn_shared_prefix_workspace_size(
+            case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+            case.block_tables.shape[1], shared_pages, part)
+    else:
+        ws_bytes = P.vllm_paged_attn_workspace_size(case.num_seqs, case.num_q_heads,
+                                                    case.num_kv_heads, case.head_dim,
+                                                    case.block_tables.shape[1], part)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    # The step's cache write goes into the decode call (same result bit for
+    # bit: vllm_paged_attn_decode_append) unless asked to run the two calls
+    # separately; the shared-prefix decode has no fused form.
+    fused = not (separate_write or shared_pages)
+
+    def write(r):
+        if fused:
+            return
+        kc, vc = pools[r]
+        P.vllm_paged_cache_write(new_k, new_v, new_slots, view(kc), view(vc),
+                                 k_scale=case.k_scale, v_scale=case.v_scale)
+
+    def decode(r):
+        kc, vc = pools[r]
+        if fused:
+            P.vllm_paged_attn_decode_append(out, q, new_k, new_v, new_slots, view(kc), view(vc), bt,
+                                            ctx, case.scale, case.window, k_scale=case.k_scale,
+                                            v_scale=case.v_scale, partition_size=part, workspace=ws)
+        elif shared_pages:
+            P.vllm_paged_attn_decode_shared_prefix(out, q, view(kc), view(vc), bt, ctx,
+                                                   shared_pages, case.scale, case.window,
+                                                   k_scale=case.k_scale, v_scale=case.v_scale,
+                                                   partition_size=part, workspace=ws)
+        else:
+            P.vllm_paged_attn_decode(out, q, view(kc), view(vc), bt, ctx, case.scale, case.window,
+                                     k_scale=case.k_scale, v_scale=case.v_scale,
+                                     partition_size=part, workspace=ws)
+
+    for i in range(max(warmup, R)):          # eager warm-up (also checks every replica)
+        write(i % R)
+        decode(i % R)
+    torch.cuda.synchronize()
+
+    if not graph:
+        run_write = write
+        run_decode = decode
+    else:
+        # One graph per replica for the cache write and one for the decode (a
+        # decode step of a serving engine is replayed from a captured graph;
+        # this removes the Python launch cost from the timed region).
+        gw, gd = [], []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(R):
+                g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g1, stream=side, capture_error_mode="relaxed"):
+                    write(r)
+                with torch.cuda.graph(g2, stream=side, capture_error_mode="relaxed"):
+                    decode(r)
+                gw.append(g1)
+                gd.append(g2)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        run_write = lambda r: gw[r].replay()    # noqa: E731
+        run_decode = lambda r: gd[r].replay()   # noqa: E731
+        for i in range(warmup):
+            run_write(i % R)
+            run_decode(i % R)
+        torch.cuda.synchronize()
+
+    # HIP events around the decode call of every EVENT_EVERY-th step: timing
+    # events cost GPU time themselves (about 6.7 us per step when recorded
+    # on every step of the 8B-class batch), so only a regular sample of the
+    # timed steps carries them.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           if i % EVENT_EVERY == 0 else None for i in range(steps)]
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    region[0].record(stream)
+    for i in range(steps):
+        r = (warmup + i) % R
+        run_write(r)
+        ev = evs[i]
+        if ev:
+            ev[0].record(stream)
+        run_decode(r)
+        if ev:
+            ev[1].record(stream)
+    region[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    dec_ms = [ev[0].elapsed_time(ev[1]) for ev in evs if ev]
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    region_ms = region[0].elapsed_time(region[1]) / steps   # GPU time per step
+    del pools, ws
+    torch.cuda.empty_cache()
+
+    step_bytes = by["decode"] + by["write"]
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # roofline on the bytes the path must move: with the shared prefix read
+    # once, its K/V count once
+    call_bytes = by["unique_decode"] if shared_pages else by["decode"] + (by["write"] if fused else 0)
+    # a fused step is one decode call: its duration is the events around the
+    # whole timed region over the steps (the sampled per-call events add a
+    # bubble of their own); otherwise the sampled per-call events
+    call_ms = region_ms if fused else dec_avg
+    achieved = call_bytes / (call_ms * 1e-3) / 1e9
+    # the read ceiling of the bytes the call must read, in the pool's page size
+    page_bytes = 16 * case.head_dim * ELEM_BYTES[case.kv_dtype]
+    ceiling = read_ceiling(P, by["unique_kv"] if shared_pages else by["kv"], page_bytes)
+    return {
+        "workload": case.name,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "dtype": case.kv_dtype,
+        "config": {"workload": case.name, "num_seqs": case.num_seqs,
+                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": 16,
+                   "context_lens": cfg.get("ctx_range") or cfg.get("ctx_list") or
+                   [int(case.context_lens.min()), int(case.context_lens.max())],
+                   "kept_tokens": by["kept_tokens"], "kv_bytes_per_step": by["kv"],
+                   "bytes_per_step": step_bytes, "partition_tokens": part or "auto",
+                   "shared_prefix_pages": shared_pages,
+                   "unique_kv_bytes_per_step": by["unique_kv"],
+                   "pool_replicas": R, "seed": idx,
+                   "launch": "hip_graph_replay" if graph else "eager",
+                   "step": "cache write fused into the decode" if fused else
+                           "cache write, then decode"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "seqs_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
+        "decode_call_ms": {"roofline_basis": ("events around the timed region / steps" if fused else
+                                              "sampled events around the call"),
+                           "region_per_step": round(region_ms, 5),
+                           "events_every_n_steps": EVENT_EVERY, "samples": len(dec_ms),
+                           "mean": round(dec_avg, 5),
+                           "p10": round(float(np.percentile(dec_ms, 10)), 5),
+                           "p50": round(float(np.percentile(dec_ms, 50)), 5),
+                           "p90": round(float(np.percentile(dec_ms, 90)), 5)},
+        "roofline": {"bound": "hbm",
+                     "kernel": ("decode call (attn_tile_kernel shared-prefix pass + decode_kernel + "
+                                "decode_merge_kernel), unique bytes" if shared_pages else
+                                "decode call with the fused cache write (decode_kernel + "
+                                "decode_merge_kernel)" if fused else
+                                "decode call (decode_kernel + decode_merge_kernel)"),
+                     "bytes_per_call": call_bytes, "ms_per_call": round(call_ms, 5),
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "read_ceiling": ceiling["GB_per_s"],
+                     "frac_of_read_ceiling": round(achieved / ceiling["GB_per_s"], 4),
+                     "traffic": (measured_traffic(case.name + "_shared_prefix",
+                                                  ("decode.hip", "prefill.hip", "common.h"))
+                                 if shared_pages else measured_traffic(case.name))},
+        "meets_70pct_of_peak": bool(achieved >= 0.7 * HBM_PEAK_GBPS),
+        "read_ceiling": ceiling,
+        "scatter": scatter,
+        "cpu_baseline": cpu,
+    }
+
+
+# Decode workloads measured beside the main one in the default line: the
+# long-context split-K (fp16) and the prefix-shared FP8 batch (shared-prefix
+# decode), both under the same 70%-of-peak bar as the 8B-class one.
+EXTRA_DECODE = (2, 3)
 
 
 def main():
@@ -349,6 +655,8 @@ def main():
                     help="decode a prefix-shared workload without reading the shared pages once")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill measurement appended to the decode line")
+    ap.add_argument("--no-extra-decode", action="store_true",
+                    help="skip the long-context and prefix-shared decode objects of the default line")
     ap.add_argument("--separate-write", action="store_true",
                     help="decode step as two calls (cache write, then decode) instead of the fused one")
     ap.add_argument("--block-manager-only", action="store_true",
@@ -382,199 +690,51 @@ def main():
         main_prefill(args)
         return
 
+    extra = [] if (args.no_extra_decode or args.config != 1) else list(EXTRA_DECODE)
+    with_prefill = not args.no_prefill
+    # CPU baselines first: they fork worker processes, which must happen
+    # before this process initialises the GPU.  The main workload's sample is
+    # about --cpu-seconds long, the others' about a third of it.
     case = make_case(args.config)
-    shared_tokens = 0 if args.no_shared_prefix else int(cfg.get("shared_tokens", 0))
-    by = decode_bytes(case, shared_tokens)
-    # CPU baseline first: it forks worker processes, which must happen
-    # before this process initialises the GPU.
     cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
+    cpu_extra = {}
+    for idx in extra:
+        cpu_extra[idx] = None if args.no_cpu_baseline else \
+            cpu_baseline(make_case(idx), args.cpu_seconds / 3)
+    cpu_prefill = None if (args.no_cpu_baseline or not with_prefill) else \
+        cpu_baseline_prefill(make_case(4), args.cpu_seconds * 2 / 3)
 
-    import paged_kv_cache_183_amd as P
-    from paged_kv_cache_183_amd.binding import tensor_desc  # noqa: F401  (library loaded)
-
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    view = (lambda t: t) if case.kv_dtype == "e4m3" else \
-        (lambda t: t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16))
-
-    fill_k, fill_v = case.fill_k.to(dev), case.fill_v.to(dev)
-    fill_slots = case.fill_slots.to(dev)
-    kc0, vc0 = case.sentinel_pool().to(dev), case.sentinel_pool().to(dev)
-    P.vllm_paged_cache_write(fill_k, fill_v, fill_slots, view(kc0), view(vc0),
-                             k_scale=case.k_scale, v_scale=case.v_scale)
-    pool_bytes = 2 * kc0.numel() * kc0.element_size()
-    R = args.replicas or max(2, math.ceil(3 * 256e6 / pool_bytes) + 1)
-    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
-    rows = case.step_rows.to(dev)
-    new_k, new_v = fill_k[rows].contiguous(), fill_v[rows].contiguous()
-    new_slots = fill_slots[rows].contiguous()
-    del fill_k, fill_v
-    q = case.q.to(dev)
-    out = torch.empty_like(q)
-    bt, ctx = case.block_tables.to(dev), case.context_lens.to(dev)
-    part = args.partition or case.partition
-    shared_pages = shared_tokens // 16
-    if shared_pages:
-        ws_bytes = P.vllm_paged_attn_shared_prefix_workspace_size(
-            case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
-            case.block_tables.shape[1], shared_pages, part)
-    else:
-        ws_bytes = P.vllm_paged_attn_workspace_size(case.num_seqs, case.num_q_heads,
-                                                    case.num_kv_heads, case.head_dim,
-                                                    case.block_tables.shape[1], part)
-    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-
-    # The step's cache write goes into the decode call (same result bit for
-    # bit: vllm_paged_attn_decode_append) unless asked to run the two calls
-    # separately; the shared-prefix decode has no fused form.
-    fused = not (args.separate_write or shared_pages)
-
-    def write(r):
-        if fused:
-            return
-        kc, vc = pools[r]
-        P.vllm_paged_cache_write(new_k, new_v, new_slots, view(kc), view(vc),
-                                 k_scale=case.k_scale, v_scale=case.v_scale)
-
-    def decode(r):
-        kc, vc = pools[r]
-        if fused:
-            P.vllm_paged_attn_decode_append(out, q, new_k, new_v, new_slots, view(kc), view(vc), bt,
-                                            ctx, case.scale, case.window, k_scale=case.k_scale,
-                                            v_scale=case.v_scale, partition_size=part, workspace=ws)
-        elif shared_pages:
-            P.vllm_paged_attn_decode_shared_prefix(out, q, view(kc), view(vc), bt, ctx,
-                                                   shared_pages, case.scale, case.window,
-                                                   k_scale=case.k_scale, v_scale=case.v_scale,
-                                                   partition_size=part, workspace=ws)
-        else:
-            P.vllm_paged_attn_decode(out, q, view(kc), view(vc), bt, ctx, case.scale, case.window,
-                                     k_scale=case.k_scale, v_scale=case.v_scale,
-                                     partition_size=part, workspace=ws)
-
-    for i in range(max(args.warmup, R)):          # eager warm-up (also checks every replica)
-        write(i % R)
-        decode(i % R)
-    torch.cuda.synchronize()
-
-    if not args.graph:
-        run_write = write
-        run_decode = decode
-    else:
-        # One graph per replica for the cache write and one for the decode (a
-        # decode step of a serving engine is replayed from a captured graph;
-        # this removes the Python launch cost from the timed region).
-        gw, gd = [], []
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for r in range(R):
-                g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g1, stream=side, capture_error_mode="relaxed"):
-                    write(r)
-                with torch.cuda.graph(g2, stream=side, capture_error_mode="relaxed"):
-                    decode(r)
-                gw.append(g1)
-                gd.append(g2)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        run_write = lambda r: gw[r].replay()
-        run_decode = lambda r: gd[r].replay()
-        for i in range(args.warmup):
-            run_write(i % R)
-            run_decode(i % R)
-        torch.cuda.synchronize()
-
-    # HIP events around the decode call of every EVENT_EVERY-th step: timing
-    # events cost GPU time themselves (about 6.7 us per step when recorded
-    # on every step of the 8B-class batch), so only a regular sample of the
-    # timed steps carries them.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           if i % EVENT_EVERY == 0 else None for i in range(args.steps)]
-    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    region[0].record(stream)
-    for i in range(args.steps):
-        r = (args.warmup + i) % R
-        run_write(r)
-        ev = evs[i]
-        if ev:
-            ev[0].record(stream)
-        run_decode(r)
-        if ev:
-            ev[1].record(stream)
-    region[1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    dec_ms = [ev[0].elapsed_time(ev[1]) for ev in evs if ev]
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    region_ms = region[0].elapsed_time(region[1]) / args.steps   # GPU time per step
-
-    step_bytes = by["decode"] + by["write"]
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # roofline on the bytes the path must move: with the shared prefix read
-    # once, its K/V count once
-    call_bytes = by["unique_decode"] if shared_pages else by["decode"] + (by["write"] if fused else 0)
-    # a fused step is one decode call: its duration is the events around the
-    # whole timed region over the steps (the sampled per-call events add a
-    # bubble of their own); otherwise the sampled per-call events
-    call_ms = region_ms if fused else dec_avg
-    achieved = call_bytes / (call_ms * 1e-3) / 1e9
+    torch.cuda.set_device(0)
+    main_res = bench_decode(args.config, case, args, args.steps, args.warmup, cpu,
+                            shared_prefix=not args.no_shared_prefix,
+                            separate_write=args.separate_write, partition=args.partition,
+                            graph=args.graph)
+    del case
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": main_res["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.kv_dtype,
+        "dtype": main_res["dtype"],
         "data": "synthetic",
-        "config": {"workload": case.name, "num_seqs": case.num_seqs,
-                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
-                   "head_dim": case.head_dim, "block_size": 16,
-                   "context_lens": cfg.get("ctx_range") or cfg.get("ctx_list"),
-                   "kept_tokens": by["kept_tokens"], "kv_bytes_per_step": by["kv"],
-                   "bytes_per_step": step_bytes, "partition_tokens": part or "auto",
-                   "shared_prefix_pages": shared_pages,
-                   "unique_kv_bytes_per_step": by["unique_kv"],
-                   "pool_replicas": R, "seed": args.config,
-                   "launch": "hip_graph_replay" if args.graph else "eager",
-                   "step": "cache write fused into the decode" if fused else
-                           "cache write, then decode"},
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "seqs_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
-        "decode_call_ms": {"roofline_basis": ("events around the timed region / steps" if fused else
-                                              "sampled events around the call"),
-                           "region_per_step": round(region_ms, 5),
-                           "events_every_n_steps": EVENT_EVERY, "samples": len(dec_ms),
-                           "mean": round(dec_avg, 5),
-                           "p10": round(float(np.percentile(dec_ms, 10)), 5),
-                           "p50": round(float(np.percentile(dec_ms, 50)), 5),
-                           "p90": round(float(np.percentile(dec_ms, 90)), 5)},
-        "roofline": {"bound": "hbm",
-                     "kernel": ("decode call (attn_tile_kernel shared-prefix pass + decode_kernel + "
-                                "decode_merge_kernel), unique bytes" if shared_pages else
-                                "decode call with the fused cache write (decode_kernel + "
-                                "decode_merge_kernel)" if fused else
-                                "decode call (decode_kernel + decode_merge_kernel)"),
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": (measured_traffic(case.name + "_shared_prefix",
-                                                  ("decode.hip", "prefill.hip", "common.h"))
-                                 if shared_pages else measured_traffic(case.name))},
-        "cpu_baseline": cpu,
     }
-    if not args.no_prefill:
+    for k in ("config", "pct_hbm_peak", "seqs_per_s", "decode_call_ms", "roofline",
+              "meets_70pct_of_peak", "read_ceiling", "scatter", "cpu_baseline"):
+        res[k] = main_res[k]
+    for idx in extra:
+        sub = bench_decode(idx, make_case(idx), args, min(args.steps, 100), min(args.warmup, 10),
+                           cpu_extra[idx])
+        res[sub["workload"]] = sub
+    if with_prefill:
         # The matrix-core variant of the path, on the chunked-prefill workload.
         res["prefill"] = bench_prefill(make_case(4), steps=min(args.steps, 50), warmup=10)
+        res["prefill"]["cpu_baseline"] = cpu_prefill
         # chunked-local attention (8192-token chunks) on the same batch
         res["chunked_local"] = bench_prefill(make_case(4), steps=min(args.steps, 50), warmup=10,
                                              chunk=args.chunk_size or 8192)

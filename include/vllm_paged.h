@@ -388,6 +388,24 @@ vllm_status vllm_paged_recycle_pages(const vllm_tensor* context_lens, vllm_tenso
                                      void* hip_stream);
 
 /*
+ * Measurement aid: a plain read of a list of pages, the practical ceiling of
+ * the decode's memory access pattern on this GPU.  Page page_ids[j] (bytes
+ * page_bytes * id .. of `buffer`; ids outside the buffer read page 0) is
+ * read once for every j, with 16-byte non-temporal loads, 64 lanes per page
+ * and 16 KiB in flight per wave, the list cut into one equal contiguous
+ * chunk per wave; nothing is computed but an XOR of the bytes each wave read,
+ * stored to sink[wave].  Timing it over the pages of a decode's K and V, in a
+ * random order, gives the bandwidth the decode could reach if it did nothing
+ * but read.
+ *   buffer     any dtype, rank 1 to 4, contiguous, at least one page
+ *   page_ids   [P] I32
+ *   page_bytes 1024, 2048 or 4096
+ *   sink       [W] I32 written: W waves (a multiple of 4, at most 2^20)
+ */
+vllm_status vllm_paged_read_pages(const vllm_tensor* buffer, const vllm_tensor* page_ids,
+                                  int32_t page_bytes, vllm_tensor* sink, void* hip_stream);
+
+/*
  * Prefix-caching KV block manager on the device: the step before the path,
  * which fills block tables and slot mappings ("Building and Deploying
  * vllm.cpp", Step 3, RadixTree prefix caching: radix matching over runs of

@@ -26,5 +26,6 @@ from .binding import (  # noqa: F401
     vllm_paged_cache_write,
     vllm_paged_chunked_local_plan,
     vllm_paged_chunked_local_virtual_count,
+    vllm_paged_read_pages,
     vllm_paged_recycle_pages,
 )

@@ -32,7 +32,7 @@ BLOCK_SIZE = 16
 
 EXPORTED = ["vllm_abi_version", "vllm_last_error", "vllm_paged_cache_write",
             "vllm_paged_attn_decode", "vllm_paged_attn_workspace_size",
-            "vllm_paged_attn_decode_noalloc",
+            "vllm_paged_attn_decode_noalloc", "vllm_paged_read_pages",
             "vllm_paged_attn_decode_shared_prefix", "vllm_paged_attn_shared_prefix_workspace_size",
             "vllm_paged_attn_prefill", "vllm_paged_attn_decode_append", "vllm_paged_chunked_local_plan",
             "vllm_paged_chunked_local_virtual_count", "vllm_paged_recycle_pages",
@@ -99,6 +99,8 @@ def _load():
     lib.vllm_paged_attn_decode_append.argtypes = [T] * 9 + [ctypes.c_float, ctypes.c_int32,
                                                              ctypes.POINTER(VllmAttnOpts),
                                                              ctypes.c_void_p]
+    lib.vllm_paged_read_pages.restype = ctypes.c_int
+    lib.vllm_paged_read_pages.argtypes = [T, T, ctypes.c_int32, T, ctypes.c_void_p]
     lib.vllm_block_manager_state_size.restype = ctypes.c_size_t
     lib.vllm_block_manager_state_size.argtypes = [ctypes.c_int32]
     lib.vllm_block_manager_state_layout.restype = ctypes.c_int32
@@ -344,3 +346,13 @@ def vllm_block_manager_release(state, num_blocks, block_tables, num_tokens, now,
     _check(LIB.vllm_block_manager_release(ctypes.c_void_p(state.data_ptr()), num_blocks,
                                           *[ctypes.byref(a) for a in args], ctypes.c_uint32(now),
                                           ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_paged_read_pages(buffer, page_ids, page_bytes, sink, stream=None) -> None:
+    """Read pages ``page_ids`` (int32) of ``buffer`` once; one XOR per wave
+    into ``sink`` (int32, one entry per wave)."""
+    args = [tensor_desc(x) for x in (buffer, page_ids)]
+    s = tensor_desc(sink)
+    _check(LIB.vllm_paged_read_pages(ctypes.byref(args[0]), ctypes.byref(args[1]),
+                                     ctypes.c_int32(page_bytes), ctypes.byref(s),
+                                     ctypes.c_void_p(_stream(stream))))

@@ -937,6 +937,39 @@ vllm_status vllm_paged_recycle_pages(const vllm_tensor* context_lens, vllm_tenso
   return ok();
 }
 
+vllm_status vllm_paged_read_pages(const vllm_tensor* buffer, const vllm_tensor* page_ids,
+                                  int32_t page_bytes, vllm_tensor* sink, void* hip_stream) {
+  if (!buffer) return fail(VLLM_ERR_INVALID_ARG, "buffer: null tensor descriptor");
+  if (buffer->ndim < 1 || buffer->ndim > 4)
+    return fail(VLLM_ERR_INVALID_ARG, "buffer: rank 1 to 4");
+  VP_TRY(check_tensor(buffer, "buffer", buffer->ndim));
+  VP_TRY(check_tensor(page_ids, "page_ids", 1));
+  VP_TRY(check_tensor(sink, "sink", 1));
+  VP_TRY(check_dtype(page_ids, "page_ids", VLLM_DTYPE_I32));
+  VP_TRY(check_dtype(sink, "sink", VLLM_DTYPE_I32));
+  if (page_bytes != 1024 && page_bytes != 2048 && page_bytes != 4096)
+    return fail(VLLM_ERR_UNSUPPORTED, "page_bytes %d: supported 1024, 2048, 4096", (int)page_bytes);
+  const int64_t W = sink->shape[0];
+  if (W < 4 || W % 4 != 0 || W > (1 << 20))
+    return fail(VLLM_ERR_INVALID_ARG, "sink: a multiple of 4 entries (one per wave), 4 .. 2^20");
+  const int64_t nbytes = numel(buffer) * elem_bytes(buffer->dtype);
+  if (nbytes < page_bytes) return fail(VLLM_ERR_INVALID_ARG, "buffer smaller than one page");
+  if (page_ids->shape[0] == 0) return ok();
+  VP_TRY(check_data(buffer, "buffer", 16));
+  VP_TRY(check_data(page_ids, "page_ids", 4));
+  VP_TRY(check_data(sink, "sink", 4));
+  vp::ReadPagesParams p{};
+  p.base = static_cast<const uint8_t*>(buffer->data);
+  p.page_ids = static_cast<const int32_t*>(page_ids->data);
+  p.sink = static_cast<uint32_t*>(sink->data);
+  p.num_pages = page_ids->shape[0];
+  p.num_base_pages = nbytes / page_bytes;
+  p.page_bytes = page_bytes;
+  p.num_waves = (int32_t)W;
+  VP_TRY(hip_status(vp::launch_read_pages(p, (hipStream_t)hip_stream), "read_pages launch"));
+  return ok();
+}
+
 size_t vllm_block_manager_state_size(int32_t num_blocks) {
   if (num_blocks < 1 || num_blocks > (1 << 24)) return 0;
   return (size_t)vp::bm_layout(num_blocks).bytes;

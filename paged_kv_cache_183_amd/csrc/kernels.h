@@ -164,6 +164,18 @@ struct RecycleParams {
 
 hipError_t launch_recycle_pages(const RecycleParams& p, hipStream_t stream);
 
+// Plain random-page read (the ceiling of the decode's access pattern).
+struct ReadPagesParams {
+  const uint8_t* base;         // pages of page_bytes bytes
+  const int32_t* page_ids;     // [num_pages] pages to read (outside the buffer: page 0)
+  uint32_t* sink;              // [num_waves] XOR of the bytes each wave read
+  int64_t num_pages;
+  int64_t num_base_pages;      // pages in the buffer
+  int32_t page_bytes;          // 1024, 2048 or 4096
+  int32_t num_waves;           // a multiple of 4
+};
+hipError_t launch_read_pages(const ReadPagesParams& p, hipStream_t stream);
+
 // ---- prefix-caching block manager -------------------------------------------
 // State of a pool of N blocks, one device buffer (regions 256-byte aligned, in
 // this order after a 256-byte header of int32: free count, cached count,

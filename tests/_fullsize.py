@@ -84,10 +84,14 @@ def compute(job: str):
 
 def _child(outdir: str, jobs: list) -> int:
     import numpy as np
+    from threadpoolctl import threadpool_limits
     for job in jobs:
         t0 = time.time()
         try:
-            ref = compute(job)
+            # one BLAS thread in each forked worker (the host may default BLAS
+            # to every core, which the workers would then oversubscribe)
+            with threadpool_limits(limits=1, user_api="blas"):
+                ref = compute(job)
         except Exception as e:                       # reported to the waiting test
             with open(os.path.join(outdir, job + ".err"), "w") as f:
                 f.write(f"{type(e).__name__}: {e}\n")
@@ -110,8 +114,6 @@ def start(jobs) -> None:
         return
     outdir = tempfile.mkdtemp(prefix="vllm_paged_oracle_")
     env = dict(os.environ)
-    env.setdefault("OPENBLAS_NUM_THREADS", "1")     # one BLAS thread per forked worker
-    env.setdefault("OMP_NUM_THREADS", "1")
     log = open(os.path.join(outdir, "child.log"), "w")
     _STATE["proc"] = subprocess.Popen([sys.executable, os.path.abspath(__file__), outdir, *jobs],
                                       stdout=log, stderr=subprocess.STDOUT, env=env, cwd=ROOT)

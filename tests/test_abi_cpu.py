@@ -125,6 +125,18 @@ def test_noalloc_decode_validation():
     assert st == Bd.VLLM_ERR_INVALID_ARG and "workspace" in P.vllm_last_error()
 
 
+def test_read_pages_validation():
+    buf = torch.zeros(8192, dtype=torch.uint8)
+    ids = torch.zeros(3, dtype=torch.int32)
+    sink = torch.zeros(8, dtype=torch.int32)
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_read_pages, buf, ids, 3000, sink)
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_read_pages, buf, ids, 4096, sink[:6])
+    _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_read_pages, buf[:1000], ids, 1024, sink)
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_read_pages, buf, ids.long(), 1024, sink)
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_read_pages, buf, ids, 4096, sink)
+    P.vllm_paged_read_pages(buf, ids[:0], 4096, sink, stream=0)      # no pages: no-op
+
+
 def _ws_layout(B, Hq, Hkv, D, chunks):
     """Bytes of a decode workspace holding ``chunks`` chunks: piece records
     (2 ints per unit) + page prefix (B + 3 ints) + 2 pieces per chunk of
