@@ -158,7 +158,12 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
 /*
  * Paged attention decode: one query token per sequence, at position n - 1
  * where n = context_lens[s] counts every cached token including the query's
- * own (its K/V are written by vllm_paged_cache_write first).
+ * own (its K/V are written by vllm_paged_cache_write first).  This is the
+ * paged attention over the block-paged KV cache of the model forward (vllm.cpp
+ * repository listing, "What's implemented (CPU, behaviorally tested)", model
+ * forward), over 16-token FP16/FP8 pages reached through per-sequence block
+ * tables that may share physical pages ("Building and Deploying vllm.cpp",
+ * Step 3), with the sliding window of the listing's local-attention entry.
  *   out[s, h, :] = sum_t softmax_t(scale * <q[s, h, :], K_s[t, h / g, :]>) V_s[t, h / g, :]
  * over t in [max(0, n - window), n) (window = 0: all n tokens), where token t
  * of sequence s is row t % 16 of physical page block_tables[s, t / 16] and
@@ -175,6 +180,14 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
  *   scale        softmax scale applied to q.k (e.g. 1/sqrt(D))
  *   window       sliding window in tokens, 0 = off, must be >= 0
  *   opts         nullable; fp8 scales, split-K partition size, workspace
+ * Work split: by default the kept pages of the whole batch are cut into one
+ * equal chunk per wave the GPU holds at once.  A nonzero partition_size fixes
+ * the chunk at that many tokens instead, but the chunks still tile the
+ * batch's page stream (sequence by sequence, kv-head by kv-head), not each
+ * sequence from its token 0.  So a chunk boundary inside a sequence falls
+ * where the pages before it put it, and the log-sum-exp merge combines pieces
+ * of that sequence cut there.  Either way the result is the same softmax;
+ * only the rounding order differs.
  * Supported: D in {64, 128}; Hq % Hkv == 0 (any g >= 1); at most 131072
  * work units B * Hkv * (g / head chunk), where the head chunk is g for
  * g <= 8, else the largest divisor of g not above 8; the work bound
@@ -293,7 +306,14 @@ size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
                                                     int32_t partition_size);
 
 /*
- * Chunked-prefill attention on matrix cores: sequence s has Q_s =
+ * Chunked-prefill attention on matrix cores, for the multi-token query
+ * chunks that a token-budget scheduler with chunked prefill produces (vllm.cpp
+ * repository listing, "What's implemented (CPU, behaviorally tested)", engine
+ * core: the unified token-budget scheduler with chunked prefill; its CUDA path
+ * runs a vendored FlashAttention-2 prefill, listed under the optimized paths
+ * of the same listing).  Prefix hits skip the prefill of the cached part
+ * ("Building and Deploying vllm.cpp", Step 3), so a chunk attends to cached
+ * pages plus its own.  Sequence s has Q_s =
  * query_start_loc[s+1] - query_start_loc[s] query tokens (rows
  * query_start_loc[s] .. query_start_loc[s+1]-1 of q) at positions
  * n - Q_s .. n - 1, where n = context_lens[s] includes them (their K/V are

@@ -588,49 +588,6 @@ __global__ __launch_bounds__(kBT) void bm_release_kernel(BmReleaseParams p) {
   if (t == 0) S.hdr[0] = min(N, s_free + s_pre[B]);
 }
 
-BmLayout bm_layout(int32_t num_blocks) {
-  BmLayout L{};
-  const int64_t N = num_blocks;
-  int64_t cap = 64;
-  while (cap < 2 * N) cap <<= 1;
-  L.cap = (int32_t)cap;
-  const int64_t sizes[kBmRegions] = {4 * N, 4 * N, 4 * N, 4 * N, 4 * N, 4 * N, 8 * N, 4 * kBlk * N,
-                                     4 * cap, 4 * N, 4 * N};
-  int64_t off = 256;                         // header
-  for (int i = 0; i < kBmRegions; ++i) {
-    L.off[i] = off;
-    off += (sizes[i] + 255) / 256 * 256;
-  }
-  L.bytes = off;
-  return L;
-}
-
-BmState bm_state(void* base, int32_t num_blocks) {
-  const BmLayout L = bm_layout(num_blocks);
-  uint8_t* p = static_cast<uint8_t*>(base);
-  BmState S;
-  S.hdr = reinterpret_cast<int32_t*>(p);
-  S.free_stack = reinterpret_cast<int32_t*>(p + L.off[kBmFree]);
-  S.ref = reinterpret_cast<int32_t*>(p + L.off[kBmRef]);
-  S.ts = reinterpret_cast<uint32_t*>(p + L.off[kBmTs]);
-  S.depth = reinterpret_cast<int32_t*>(p + L.off[kBmDepth]);
-  S.parent = reinterpret_cast<int32_t*>(p + L.off[kBmParent]);
-  S.flags = reinterpret_cast<int32_t*>(p + L.off[kBmFlags]);
-  S.chash = reinterpret_cast<uint64_t*>(p + L.off[kBmHash]);
-  S.tokens = reinterpret_cast<int32_t*>(p + L.off[kBmTokens]);
-  S.table = reinterpret_cast<int32_t*>(p + L.off[kBmTable]);
-  S.mark = reinterpret_cast<int32_t*>(p + L.off[kBmMark]);
-  S.owner = reinterpret_cast<int32_t*>(p + L.off[kBmOwner]);
-  S.num_blocks = num_blocks;
-  S.cap = L.cap;
-  return S;
-}
-
-size_t bm_workspace_bytes(int32_t num_seqs, int32_t mb) {
-  const int64_t items = (int64_t)num_seqs * mb;
-  return (size_t)((8 * items + 255) / 256 * 256 + (4 * items + 255) / 256 * 256);
-}
-
 hipError_t launch_bm_init(const BmState& st, hipStream_t stream) {
   const int64_t work = std::max<int64_t>((int64_t)st.num_blocks * kBlk, st.cap);
   const int grid = (int)std::min<int64_t>(1024, (work + kBT - 1) / kBT);
