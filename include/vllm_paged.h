@@ -284,7 +284,7 @@ vllm_status vllm_paged_attn_decode_noalloc(vllm_tensor* out, const vllm_tensor* 
  *   scale         > 0 when shared_pages > 0
  *   other arguments as vllm_paged_attn_decode; the workspace must hold
  *   vllm_paged_attn_shared_prefix_workspace_size bytes.
- * Supported: as vllm_paged_attn_decode, with D = 128 when shared_pages > 0.
+ * Supported: as vllm_paged_attn_decode.
  */
 vllm_status vllm_paged_attn_decode_shared_prefix(vllm_tensor* out, const vllm_tensor* q,
                                                  const vllm_tensor* k_cache,
@@ -297,7 +297,7 @@ vllm_status vllm_paged_attn_decode_shared_prefix(vllm_tensor* out, const vllm_te
 /*
  * Bytes of workspace vllm_paged_attn_decode_shared_prefix needs for these
  * sizes (sizes and partition_size only).  Returns 0 for invalid arguments
- * (including head_dim other than 128, or shared_pages outside
+ * (including head_dim other than 64 or 128, or shared_pages outside
  * [0, max_blocks_per_seq]).
  */
 size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -335,7 +335,7 @@ size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
  *   max_query_len    an upper bound of max_s Q_s (rows of longer chunks past
  *                    it are not computed)
  *   scale        softmax scale applied to q.k, finite and > 0
- * Supported: D = 128; g = Hq / Hkv <= 128.  sumQ = 0 is a no-op.  Values of
+ * Supported: D in {64, 128}; g = Hq / Hkv <= 128.  sumQ = 0 is a no-op.  Values of
  * query_start_loc are clamped to [0, sumQ], so no value leads outside q/out.
  */
 vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,

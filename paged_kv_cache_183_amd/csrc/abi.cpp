@@ -377,7 +377,7 @@ size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
                                                     int32_t max_blocks_per_seq, int32_t shared_pages,
                                                     int32_t partition_size) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-      head_dim != 128 || max_blocks_per_seq < 0 || shared_pages < 0 ||
+      (head_dim != 64 && head_dim != 128) || max_blocks_per_seq < 0 || shared_pages < 0 ||
       shared_pages > max_blocks_per_seq)
     return 0;
   int32_t chunk_tokens = 0;
@@ -511,8 +511,6 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   if (shared_pages < 0 || shared_pages > max_blocks)
     return fail(VLLM_ERR_INVALID_ARG, "shared_pages %d outside [0, max_blocks_per_seq = %lld]",
                 (int)shared_pages, (long long)max_blocks);
-  if (shared_pages > 0 && D != 128)
-    return fail(VLLM_ERR_UNSUPPORTED, "shared prefix: head_dim %lld, supported 128", (long long)D);
   if (shared_pages > 0 && !(scale > 0.0f))
     return fail(VLLM_ERR_INVALID_ARG, "shared prefix: scale must be positive");
   VP_TRY(plan_decode(B, Hq, Hkv, D, max_blocks, chunk_tokens, shared_pages, &dp));
@@ -796,7 +794,8 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
     VP_TRY(scale_of(opts ? opts->v_scale : 0.0f, "v_scale", &vs));
   }
   VP_TRY(check_dtype(context_lens, "context_lens", VLLM_DTYPE_I32));
-  if (D != 128) return fail(VLLM_ERR_UNSUPPORTED, "prefill head_dim %lld: supported 128", (long long)D);
+  if (D != 64 && D != 128)
+    return fail(VLLM_ERR_UNSUPPORTED, "prefill head_dim %lld: supported 64, 128", (long long)D);
   if (Hq / Hkv > 128) return fail(VLLM_ERR_UNSUPPORTED, "prefill: group size above 128");
   if (NB > INT32_MAX || block_tables->shape[1] > INT32_MAX / 16 || B > 65535 || Hq > 65535 ||
       sumQ > INT32_MAX)

@@ -116,8 +116,10 @@ __device__ __forceinline__ uint4 to_q16(const typename Raw<KF>::T& x) {
 // prefix, (max, sum, normalized output) partials per row and split.
 template <int D, int QF, int KF, bool PFX>
 __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
-  static_assert(D == 128, "head_dim 128");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr int CH = D / 8;                    // 8-element chunks per K/V row
+  constexpr int KS = D / 16;                   // k-steps of S^T = K Q^T (16 values of d each)
+  constexpr int KPT = CH / 8;                  // K chunks a thread stages per block (2 or 1)
   constexpr int EB = is_fp8(KF) ? 1 : 2;       // bytes per pool element
   constexpr int KROW = D * 2 + 16;             // bytes per LDS K row
   constexpr int VROWW = kBK / 2 + 2;           // dwords per LDS V^T row (18)
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   constexpr int VBUF = D * VROWW * 4;          // bytes per V^T buffer
   constexpr int64_t kPageBytes = 16 * D * EB;
   using RawT = typename Raw<KF>::T;
-  static_assert(kPW * 64 == 16 * CH, "staging map: one thread per (row-of-page, chunk)");
+  static_assert(kPW * 64 * KPT == 32 * CH, "staging map: K chunks of a block over the threads");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][KBUF];
   __shared__ __attribute__((aligned(16))) uint32_t s_v[2][VBUF / 4];
   __shared__ int s_red[3];
@@ -199,16 +201,16 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
     q_off = ((int64_t)s * p.num_q_heads + hk * g + head) * D;
   }
 
-  // Q operand: lane (row, hf) holds d = 64 hf + 8 t + i for k-step t.  The
+  // Q operand: lane (row, hf) holds d = D/2 hf + 8 t + i for k-step t.  The
   // loads are in flight during the reduction below and waited for after it:
   // once that wait has been seen, the block loop need not wait for them (the
   // memory counter cannot tell them from the next block's loads, so an
   // in-loop wait for Q would wait for those every block).
-  uint4 qr[8];
+  uint4 qr[KS];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + q_off + 64 * hf;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + q_off + (D / 2) * hf;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) qr[t] = *reinterpret_cast<const uint4*>(qp + 8 * t);
+    for (int t = 0; t < KS; ++t) qr[t] = *reinterpret_cast<const uint4*>(qp + 8 * t);
   }
 
   // Over the workgroup's rows: the largest lower and the smallest and largest
@@ -240,13 +242,17 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
 
   // Staging maps (256 threads, one block = pages A and B of 16 rows):
-  //  K: thread i loads row i / 16, chunk i % 16 of both pages;
+  //  K: thread i stages chunk i % CH of block row i / CH and, for D = 128,
+  //     of the same row of page B as well (block row + 16);
   //  V: thread i loads rows 2 kp and 2 kp + 1 (kp = i % 16: key pair of the
   //     block, page kp / 8) at chunk i / 16, and writes the 8 dwords
-  //     (V[2kp][d], V[2kp+1][d]) of V^T: 64 lanes hit 64 distinct banks.
-  const int k_r = threadIdx.x / CH, k_c = threadIdx.x % CH;
-  const int v_kp = threadIdx.x % 16, v_c = threadIdx.x / 16;
-  const int k_off = k_r * (D * EB) + k_c * 8 * EB;
+  //     (V[2kp][d], V[2kp+1][d]) of V^T: 64 lanes hit 64 distinct banks
+  //     (D = 64: 16 x 8 items, the first 128 threads).
+  const int k_r = threadIdx.x / CH, k_c = threadIdx.x % CH;     // k_r: block row (D = 64) or page row
+  const int v_kp = threadIdx.x % 16, v_c = (threadIdx.x / 16) % CH;
+  const bool v_on = threadIdx.x < 16 * CH;
+  const int k_off = (k_r & 15) * (D * EB) + k_c * 8 * EB;
+  const bool k_pgB = k_r >= 16;                // (D = 64) the row is in page B
   const int v_off = 2 * (v_kp & 7) * (D * EB) + v_c * 8 * EB;
   const bool v_pgB = v_kp >= 8;
   auto page_blk = [&](int j) __attribute__((always_inline)) {
@@ -260,11 +266,15 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   // (the ids are uniform over the workgroup: taken into scalar registers
   // here, a block after their loads were issued, so that the address
   // arithmetic runs on the scalar unit without waiting on the loads)
-  auto fetch = [&](RawT (&kr)[2], RawT (&vr)[2], int ida, int idb) __attribute__((always_inline)) {
+  auto fetch = [&](RawT (&kr)[KPT], RawT (&vr)[2], int ida, int idb) __attribute__((always_inline)) {
     const int64_t pa = (int64_t)__builtin_amdgcn_readfirstlane(ida) * blk_stride;
     const int64_t pb = (int64_t)__builtin_amdgcn_readfirstlane(idb) * blk_stride;
-    kr[0] = *reinterpret_cast<const RawT*>(kpool + pa + k_off);
-    kr[1] = *reinterpret_cast<const RawT*>(kpool + pb + k_off);
+    if constexpr (KPT == 2) {
+      kr[0] = *reinterpret_cast<const RawT*>(kpool + pa + k_off);
+      kr[1] = *reinterpret_cast<const RawT*>(kpool + pb + k_off);
+    } else {
+      kr[0] = *reinterpret_cast<const RawT*>(kpool + (k_pgB ? pb : pa) + k_off);
+    }
     const uint8_t* vp = vpool + (v_pgB ? pb : pa) + v_off;
     vr[0] = *reinterpret_cast<const RawT*>(vp);
     vr[1] = *reinterpret_cast<const RawT*>(vp + D * EB);
@@ -273,18 +283,22 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
     const uint32_t m = keep ? 0xFFFFFFFFu : 0u;    // value-level select (no pointer select)
     return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
   };
-  auto stage = [&](int buf, const RawT (&kr)[2], const RawT (&vr)[2], int kb)
+  auto stage = [&](int buf, const RawT (&kr)[KPT], const RawT (&vr)[2], int kb)
       __attribute__((always_inline)) {
-    uint4 k0 = to_q16<KF, QF>(kr[0]), k1 = to_q16<KF, QF>(kr[1]);
+    const bool crossing = kb + kBK > n_valid;  // block crossing n_valid: zero the rows past it
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int r = k_r + 16 * j;              // block row
+      uint4 kx = to_q16<KF, QF>(kr[j]);
+      if (crossing) kx = masked(kx, kb + r < n_valid);
+      *reinterpret_cast<uint4*>(&s_k[buf][r * KROW + k_c * 16]) = kx;
+    }
+    if (!v_on) return;
     uint4 va = to_q16<KF, QF>(vr[0]), vc = to_q16<KF, QF>(vr[1]);
-    if (kb + kBK > n_valid) {                  // block crossing n_valid: zero the rows past it
-      k0 = masked(k0, kb + k_r < n_valid);
-      k1 = masked(k1, kb + 16 + k_r < n_valid);
+    if (crossing) {
       va = masked(va, kb + 2 * v_kp < n_valid);
       vc = masked(vc, kb + 2 * v_kp + 1 < n_valid);
     }
-    *reinterpret_cast<uint4*>(&s_k[buf][k_r * KROW + k_c * 16]) = k0;
-    *reinterpret_cast<uint4*>(&s_k[buf][(16 + k_r) * KROW + k_c * 16]) = k1;
     const uint32_t a[4] = {va.x, va.y, va.z, va.w};
     const uint32_t bb[4] = {vc.x, vc.y, vc.z, vc.w};
     uint32_t* vt = &s_v[buf][(v_c * 8) * VROWW + v_kp];
@@ -304,18 +318,18 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   const float c = p.k_scales ? p.score_base * p.k_scales[hk] : p.score_scale;
 
   // One block: S^T, online softmax, O^T update.  buf holds the block's K and
-  // V^T.  Lane reads: K rows col (16 bytes at d = 64 hf + 8 t), V^T rows
+  // V^T.  Lane reads: K rows col (16 bytes at d = D/2 hf + 8 t), V^T rows
   // d = 32 m + col (8 bytes at key pairs 8 kap + 2 hf and + 4).
-  const uint8_t* k_rd = &s_k[0][col * KROW + 128 * hf];
+  const uint8_t* k_rd = &s_k[0][col * KROW + D * hf];
   const uint32_t* v_rd = &s_v[0][col * VROWW + 2 * hf];
   auto block = [&](int buf, int kb) __attribute__((always_inline)) {
     // ---- S^T = K Q^T ----
-    uint4 ka[8];
+    uint4 ka[KS];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) ka[t] = *reinterpret_cast<const uint4*>(k_rd + buf * KBUF + 16 * t);
+    for (int t = 0; t < KS; ++t) ka[t] = *reinterpret_cast<const uint4*>(k_rd + buf * KBUF + 16 * t);
     f32x16_t sacc = f32x16_t{};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) sacc = mfma32<QF>(ka[t], qr[t], sacc);
+    for (int t = 0; t < KS; ++t) sacc = mfma32<QF>(ka[t], qr[t], sacc);
 
     // ---- online softmax (row = col; this lane holds keys 8j + 4hf + i) ----
     // Scores stay unscaled up to the exponent (scale > 0: max(c s) = c max(s)),
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
   // Block bi + 1 is fetched into registers while block bi is computed, then
   // written to the other LDS buffer.  (A single-block loop body keeps the
   // accumulators in place; unrolling by two made the compiler copy them.)
-  RawT kr[2], vr[2];
+  RawT kr[KPT], vr[2];
   auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
   int ida = 0, idb = 0;                        // block ids of the block fetched next
   if (nblk > 0) {
@@ -437,15 +451,21 @@ __global__ __launch_bounds__(kPW * 64) void attn_tile_kernel(PrefillParams p) {
 }
 
 template <int QF, int KF, bool PFX>
-static hipError_t launch_tiles(const PrefillParams& x, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_tile_kernel<128, QF, KF, PFX>), dim3((unsigned)grid), dim3(kPW * 64), 0,
-                     stream, x);
+static hipError_t launch_tiles(const PrefillParams& x, int head_dim, int64_t grid, hipStream_t stream) {
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_tile_kernel<128, QF, KF, PFX>), dim3((unsigned)grid), dim3(kPW * 64), 0,
+                       stream, x);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((attn_tile_kernel<64, QF, KF, PFX>), dim3((unsigned)grid), dim3(kPW * 64), 0,
+                       stream, x);
+  else
+    return hipErrorNotSupported;
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
                           hipStream_t stream) {
-  if (head_dim != 128) return hipErrorNotSupported;
+  if (head_dim != 128 && head_dim != 64) return hipErrorNotSupported;
   const int tq = kRows / p.group;
   if (tq < 1) return hipErrorNotSupported;
   PrefillParams x = p;
@@ -455,19 +475,19 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int 
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (kv_fmt == kE4M3)
-    return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, false>(x, grid, stream)
-                          : launch_tiles<kF16, kE4M3, false>(x, grid, stream);
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, false>(x, head_dim, grid, stream)
+                          : launch_tiles<kF16, kE4M3, false>(x, head_dim, grid, stream);
   if (kv_fmt == kE5M2)
-    return q_fmt == kBF16 ? launch_tiles<kBF16, kE5M2, false>(x, grid, stream)
-                          : launch_tiles<kF16, kE5M2, false>(x, grid, stream);
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE5M2, false>(x, head_dim, grid, stream)
+                          : launch_tiles<kF16, kE5M2, false>(x, head_dim, grid, stream);
   if (kv_fmt != q_fmt) return hipErrorNotSupported;
-  return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, false>(x, grid, stream)
-                        : launch_tiles<kF16, kF16, false>(x, grid, stream);
+  return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, false>(x, head_dim, grid, stream)
+                        : launch_tiles<kF16, kF16, false>(x, head_dim, grid, stream);
 }
 
 hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
                                 hipStream_t stream) {
-  if (head_dim != 128) return hipErrorNotSupported;
+  if (head_dim != 128 && head_dim != 64) return hipErrorNotSupported;
   PrefillParams x = p;
   x.num_tiles = (int)(((int64_t)p.num_seqs * p.group + kRows - 1) / kRows);
   const int64_t pairs = (int64_t)p.num_kv_heads * p.num_splits;
@@ -475,14 +495,14 @@ hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (kv_fmt == kE4M3)
-    return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, true>(x, grid, stream)
-                          : launch_tiles<kF16, kE4M3, true>(x, grid, stream);
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, true>(x, head_dim, grid, stream)
+                          : launch_tiles<kF16, kE4M3, true>(x, head_dim, grid, stream);
   if (kv_fmt == kE5M2)
-    return q_fmt == kBF16 ? launch_tiles<kBF16, kE5M2, true>(x, grid, stream)
-                          : launch_tiles<kF16, kE5M2, true>(x, grid, stream);
+    return q_fmt == kBF16 ? launch_tiles<kBF16, kE5M2, true>(x, head_dim, grid, stream)
+                          : launch_tiles<kF16, kE5M2, true>(x, head_dim, grid, stream);
   if (kv_fmt != q_fmt) return hipErrorNotSupported;
-  return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, true>(x, grid, stream)
-                        : launch_tiles<kF16, kF16, true>(x, grid, stream);
+  return q_fmt == kBF16 ? launch_tiles<kBF16, kBF16, true>(x, head_dim, grid, stream)
+                        : launch_tiles<kF16, kF16, true>(x, head_dim, grid, stream);
 }
 
 }  // namespace vp

@@ -210,7 +210,8 @@ def test_prefill_validation():
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "scale": 0.0})
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **{**a, "scale": -0.1})
     _expect(Bd.VLLM_ERR_INVALID_ARG, P.vllm_paged_attn_prefill, **_prefill_args(Hq=3, Hkv=2))
-    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(D=64))
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(D=96))
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_attn_prefill, **_prefill_args(D=64))
     _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(kvdt=torch.int32))
     _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_prefill, **_prefill_args(kvdt=torch.float16))
     e4 = _prefill_args(kvdt=torch.uint8)                   # E4M3 pools: scales must be > 0

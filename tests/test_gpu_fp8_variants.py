@@ -137,12 +137,14 @@ def test_e5m2_every_finite_code():
 @pytest.mark.parametrize("kv", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("qd", ["bf16", "f16"])
 @pytest.mark.parametrize("per_head", [False, True])
-def test_fp8_prefill(kv, qd, per_head):
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_prefill(kv, qd, per_head, d):
     """Chunked prefill over FP8 pools (per-tensor and per-kv-head scales)."""
     ks = (0.05, 0.2, 0.03, 0.5, 0.08, 0.1, 0.02, 0.3) if per_head else 0.05
     vs = (0.5, 0.05, 0.09, 0.02, 0.3, 0.07, 0.2, 0.04) if per_head else 0.07
-    case = make_case(4, seed=800 + per_head, B=4, qlen_range=(1, 300), cached_range=(0, 600),
-                     kv=kv, q=qd, kv_src=qd, k_scale=ks, v_scale=vs, window=0 if per_head else 200)
+    case = make_case(4, seed=800 + per_head + d, B=4, qlen_range=(1, 300), cached_range=(0, 600),
+                     kv=kv, q=qd, kv_src=qd, k_scale=ks, v_scale=vs, window=0 if per_head else 200,
+                     D=d)
     kc, vc = gpu_fill(case)
     kp, vp = oracle_pools(case)
     q = case.q.to(DEV)

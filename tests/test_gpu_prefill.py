@@ -61,6 +61,30 @@ def test_prefill_heads_dtypes(hq, hkv, qd):
     check_all_rows(case, run_prefill(case, kc, vc), kp, vp)
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (4, 1), (10, 2), (64, 8), (32, 8)])
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+def test_prefill_head_dim_64(hq, hkv, qd):
+    """head_dim 64: ragged chunks over ragged caches, windows on odd groups."""
+    case = make_case(4, seed=400 + hq, B=4, qlen_range=(1, 200), cached_range=(0, 400),
+                     Hq=hq, Hkv=hkv, D=64, kv=qd, q=qd, window=100 if hq % 2 else 0,
+                     scale=0.125)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    check_all_rows(case, run_prefill(case, kc, vc), kp, vp)
+
+
+def test_prefill_head_dim_64_single_token_chunks_match_decode():
+    """Q = 1 at head_dim 64: prefill and decode agree with the oracle."""
+    case = make_case(4, B=6, qlen_range=(1, 1), cached_range=(0, 700), window=0, D=64,
+                     scale=0.125)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    ref = A.decode(raw_bits(case.q), case.q_dtype, kp, vp, case.kv_dtype,
+                   case.block_tables.numpy(), case.context_lens.numpy(), case.scale, 0)
+    assert_close(case, to_f64(run_prefill(case, kc, vc)), ref, " prefill")
+    assert_close(case, to_f64(gpu_decode(case, kc, vc)), ref, " decode")
+
+
 @pytest.mark.fullsize("prefill4")
 def test_prefill_full_size_every_row():
     """The full chunked-prefill workload (64 sequences, 16,411 query rows,

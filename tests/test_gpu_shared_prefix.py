@@ -103,6 +103,21 @@ def test_shared_prefix_head_groups(hq, hkv):
     assert_close(case, to_f64(shared_decode(case, kc, vc, 16, partition=64)), oracle(case, kp, vp))
 
 
+@pytest.mark.parametrize("kvq", [("e4m3", "f16"), ("bf16", "bf16"), ("f16", "f16")])
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2), (32, 8)])
+def test_shared_prefix_head_dim_64(kvq, hq, hkv):
+    kv, qd = kvq
+    over = dict(kv=kv, q=qd, kv_src=qd if kv == "e4m3" else kv, D=64, Hq=hq, Hkv=hkv, scale=0.125)
+    if kv != "e4m3":
+        over.update(k_scale=1.0, v_scale=1.0)
+    case = shared_case(60 + hq, B=5, shared_tokens=16 * 20, suffix_range=(0, 400), **over)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    for sp, part in ((20, 0), (7, 64), (1, 0)):
+        assert_close(case, to_f64(shared_decode(case, kc, vc, sp, partition=part)),
+                     oracle(case, kp, vp), f" shared pages {sp}")
+
+
 def test_zero_shared_pages_is_plain_decode():
     case = shared_case(45)
     kc, vc = gpu_fill(case)
