@@ -466,7 +466,7 @@ def bench_decode(idx: int, case, args, steps: int, warmup: int, cpu=None,
     q = case.q.to(dev)
     out = torch.empty_like(q)
     bt, ctx = case.block_tables.to(dev), case.context_lens.to(dev)
-    part = partition or case.partition
+    part = 0 if partition < 0 else (partition or case.partition)
     shared_pages = shared_tokens // 16
     if shared_pages:
         ws_bytes = P.vllm_paged_attn_shared_prefix_workspace_size(
@@ -647,7 +647,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload index (default: 8B-class decode)")
-    ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="split-K partition tokens (0 = the workload's own, -1 = the automatic split)")
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies rotated over steps (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -728,8 +729,23 @@ def main():
               "meets_70pct_of_peak", "read_ceiling", "scatter", "cpu_baseline"):
         res[k] = main_res[k]
     for idx in extra:
-        sub = bench_decode(idx, make_case(idx), args, min(args.steps, 100), min(args.warmup, 10),
-                           cpu_extra[idx])
+        xcase = make_case(idx)
+        if xcase.partition:
+            # The workload names a fixed split-K partition.  Its object reports
+            # the library's default split (one equal chunk of the batch's page
+            # stream per resident wave, merged by the same log-sum-exp rule),
+            # with the fixed partition timed beside it.
+            sub = bench_decode(idx, xcase, args, min(args.steps, 100), min(args.warmup, 10),
+                               cpu_extra[idx], partition=-1)
+            fixed = bench_decode(idx, xcase, args, min(args.steps, 100), min(args.warmup, 10))
+            sub["split"] = "automatic (library default)"
+            sub[f"partition_{xcase.partition}"] = {
+                k: fixed[k] for k in ("value", "ms_per_step", "pct_hbm_peak", "seqs_per_s",
+                                      "decode_call_ms", "roofline", "meets_70pct_of_peak")}
+        else:
+            sub = bench_decode(idx, xcase, args, min(args.steps, 100), min(args.warmup, 10),
+                               cpu_extra[idx])
+        del xcase
         res[sub["workload"]] = sub
     if with_prefill:
         # The matrix-core variant of the path, on the chunked-prefill workload.

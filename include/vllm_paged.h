@@ -212,10 +212,7 @@ vllm_status vllm_paged_attn_decode(vllm_tensor* out, const vllm_tensor* q,
  *                  writes the token there first (a slot elsewhere is
  *                  written too, but unordered with the reads of that page).
  *   other arguments as vllm_paged_attn_decode (k_cache, v_cache are written).
- * FP8 pools quantize as vllm_paged_cache_write does (opts scales).  When a
- * work unit holds more than 4 query heads (the fused write would cost the
- * decode more than a launch), the library runs the cache-write kernel first
- * instead; the result is the same.
+ * FP8 pools quantize as vllm_paged_cache_write does (opts scales).
  */
 vllm_status vllm_paged_attn_decode_append(vllm_tensor* out, const vllm_tensor* q,
                                           const vllm_tensor* k_new, const vllm_tensor* v_new,

@@ -432,11 +432,9 @@ vllm_status scratch_address(void** out) {
 }
 
 // Decode, optionally with the first shared_pages pages of every sequence
-// handled by the shared-prefix pass (read once per kv-head for the batch).
-// Largest work unit (query heads) that the decode kernel with the fused
-// newest-token write handles; larger ones write first with the cache-write
-// kernel.
-constexpr int kFusedMaxHeads = 4;
+// handled by the shared-prefix pass (read once per kv-head for the batch),
+// and optionally with the cache write of each sequence's newest token fused
+// into the decode kernel (k_new, v_new, slot_mapping).
 
 vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor* k_cache,
                        const vllm_tensor* v_cache, const vllm_tensor* block_tables,
@@ -559,12 +557,7 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   p.window = window;
   p.chunk_pages = dp.chunk_pages;
   p.max_chunks = (int32_t)dp.max_chunks;
-  // The fused write costs the decode kernel a few registers: with units of
-  // more than kFusedMaxHeads query heads that slows it more than a separate
-  // cache-write launch costs, so those take the write kernel first (the
-  // same result either way).
-  const bool fused = append && dp.head_chunk <= kFusedMaxHeads;
-  const bool write_first = append && !fused;
+  const bool fused = append;
   p.num_workers = dp.chunk_pages > 0
                       ? (int32_t)std::min<int64_t>(dp.max_chunks,
                                                    vp::decode_workers(dp.pages_bound, (int)D, kv_fmt,
@@ -644,26 +637,6 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
     p.ws_uo = reinterpret_cast<float*>(base + dp.uo_off);
     p.ws_um = reinterpret_cast<float*>(base + dp.um_off);
     p.ws_ul = reinterpret_cast<float*>(base + dp.ul_off);
-  }
-  if (e == hipSuccess && write_first) {
-    vp::CacheWriteParams w{};
-    w.k = k_new->data;
-    w.v = v_new->data;
-    w.slot_mapping = static_cast<const int64_t*>(slot_mapping->data);
-    w.k_cache = k_cache->data;
-    w.v_cache = v_cache->data;
-    w.num_slots = NB * VLLM_PAGED_BLOCK_SIZE;
-    w.src_tok_stride = Hkv * D;
-    w.num_items = (uint32_t)(B * Hkv * (D / 8));
-    w.items_per_token = (uint32_t)(Hkv * (D / 8));
-    w.items_per_head = (uint32_t)(D / 8);
-    w.num_kv_heads = (int32_t)Hkv;
-    w.head_dim = (int32_t)D;
-    w.k_scale = ks;
-    w.v_scale = vs;
-    w.k_scales = p.k_scales;
-    w.v_scales = p.v_scales;
-    e = vp::launch_cache_write(w, q_fmt, kv_fmt, stream);
   }
   if (e != hipSuccess) {
     // (nothing more is launched)

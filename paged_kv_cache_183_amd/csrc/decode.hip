@@ -251,6 +251,10 @@ __device__ void page_prefix(const DecodeParams& p, int* pre, int* ctx = nullptr)
 template <int D, int KF, int QF>
 __device__ __forceinline__ void append_row(const DecodeParams& p, int s, int hk, int lane) {
   constexpr int CH = D / 8;
+  // (an opaque copy of the lane index: nothing lane-dependent of this write
+  // is hoisted out of the segment loop, where it would hold registers
+  // through the whole page stream)
+  asm volatile("" : "+v"(lane));
   const int64_t slot = p.new_slots[s];
   if (slot >= 0 && slot < p.num_slots && lane < 2 * CH) {
     const bool is_v = lane >= CH;

@@ -124,22 +124,25 @@ def test_decode_parity_full_size_8b():
 @pytest.mark.parametrize("idx,job", [pytest.param(2, "decode2", marks=pytest.mark.fullsize("decode2")),
                                      pytest.param(3, "decode3", marks=pytest.mark.fullsize("decode3"))])
 def test_decode_parity_full_size(idx, job):
-    """Full-size long-context split-K (partition 512, all 16 sequences) and
-    prefix-shared FP8 (plain decode, all 128 sequences) workloads in the
-    launch configuration the benchmark times: the scatter of the whole fill
-    bit-exact, then every output element against the oracle's reference
-    (computed by the background oracle process from the same seeded inputs)."""
+    """Full-size long-context split-K (all 16 sequences; the automatic split
+    and the fixed 512-token partition) and prefix-shared FP8 (plain decode,
+    all 128 sequences) workloads in the launch configurations the benchmark
+    times: the scatter of the whole fill bit-exact, then every output element
+    against the oracle's reference (computed by the background oracle process
+    from the same seeded inputs)."""
     import _fullsize
     case = make_case(idx)
     kc, vc = gpu_fill(case)
     kp, vp = oracle_pools(case)
     assert np.array_equal(bits(kc), kp) and np.array_equal(bits(vc), vp)
     del kp, vp
-    out = gpu_decode(case, kc, vc, partition=case.partition)
+    parts = sorted({0, case.partition})
+    outs = [gpu_decode(case, kc, vc, partition=part) for part in parts]
     torch.cuda.synchronize()
     ref = _fullsize.result(job)
-    assert ref.shape == tuple(out.shape)
-    assert_close(case, to_f64(out), ref)
+    for part, out in zip(parts, outs):
+        assert ref.shape == tuple(out.shape)
+        assert_close(case, to_f64(out), ref, f" partition {part}")
 
 
 def test_single_key_is_exact():
