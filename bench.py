@@ -142,6 +142,20 @@ def _cpu_baseline_prefill(case, seconds: float, chunk: int = 0) -> dict:
     done, flops = [], 0
     Hq, D, W = case.num_q_heads, case.head_dim, case.window
     n = case.context_lens.numpy()
+    if not chunk:
+        # whole passes over every query row of the batch (at least one)
+        passes = 0
+        while passes == 0 or time.time() - t0 < seconds:
+            A.prefill(qb, case.q_dtype, kp, vp, case.kv_dtype, case.block_tables.numpy(), qsl,
+                      n, case.scale, W, workers=cores)
+            passes += 1
+        dt = time.time() - t0
+        flops = prefill_work(case)["flops"] * passes
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+                "cores_visible": hc["visible"], "kind": "oracle",
+                "tokens_per_s": round(int(qsl[-1]) * passes / dt, 1),
+                "sample": f"{passes} whole pass(es) of the chunked-prefill batch ({case.num_seqs} "
+                          f"seqs, {int(qsl[-1])} query rows, all heads), {dt / passes:.1f} s each"}
     s = 0
     per = 64                                   # query rows per sequence in the sample
     while s < case.num_seqs and (time.time() - t0 < seconds or not done):
