@@ -129,31 +129,6 @@ __device__ __forceinline__ uint32_t fp8x2_to_q16(uint32_t w) {
     return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
 }
 
-// ---- cross-lane sums within 16-lane rows (DPP) ---------------------------------
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), CTRL, 0xF, 0xF, false));
-}
-
-constexpr int kRowMirror = 0x140;      // lane i <- lane 15 - i within a row of 16
-constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7 - i within each 8
-constexpr int kQuad3210 = 0x1B;        // quad_perm [3,2,1,0]
-constexpr int kQuad1032 = 0xB1;        // quad_perm [1,0,3,2]
-
-// Sum over aligned groups of W lanes (W = 4, 8 or 16); every lane of the group
-// receives the total.  Each step pairs the two halves of a group, so after
-// log2(W) steps every lane holds the full group sum.
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(W == 4 || W == 8 || W == 16, "group width");
-  if constexpr (W == 16) x += dpp_f<kRowMirror>(x);
-  if constexpr (W >= 8) x += dpp_f<kRowHalfMirror>(x);
-  x += dpp_f<kQuad3210>(x);
-  x += dpp_f<kQuad1032>(x);
-  return x;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace vp

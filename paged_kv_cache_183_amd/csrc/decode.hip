@@ -18,29 +18,38 @@
 // merges them with the log-sum-exp rule.  The per-sequence page prefix is
 // computed by every workgroup with a block-wide scan.
 //
-// Inside a wave, per 16-token page of one kv-head (CH = D/8 chunks of 8
-// elements per token row):
-//  * K role: LPR lanes share a token row; load instruction k gives lane
-//    (rho, c) chunk (k % CPL) * LPR + c of row (k / CPL) * RPI + rho, so the
-//    LPR lanes of a row read LPR adjacent chunks.  Packed dot2 (fp16 or bf16
-//    pairs; FP8 codes are first converted exactly to q's format) gives
-//    partial dot products, summed over the LPR lanes with DPP.
-//  * Online softmax in fp32, log2 domain, with a running max that is uniform
-//    over the wave and only moves when a score exceeds it by more than 2^8
-//    (one wave vote per page).  Keys outside [max(0, n - window), n) get
-//    score -inf and their V rows are replaced by zeros: NaN garbage in the
-//    unused rows of a page never reaches the output.
-//  * The probabilities, rounded to q's 16-bit format, go through a small
-//    per-wave LDS buffer to the V role: CH lanes share a V row, one chunk
-//    each, so every wave load reads 64 contiguous chunks.  Rows of two
-//    consecutive load instructions are paired so that P.V runs on packed
-//    dot2 (v[t1][e], v[t2][e]) . (p[t1][h], p[t2][h]) with fp32
-//    accumulation; the row sums use the same rounded probabilities.
-//  * The next page's K is loaded as soon as Q.K has consumed the registers,
-//    and the next V as soon as P.V has; these loads are unconditional (past
-//    the end of the stretch they read a spare page of the workspace, which
-//    stays in L2) so that the compiler can keep the buffers in flight across
-//    iterations.
+// Inside a wave the products run on the matrix cores (v_mfma_f32_16x16x32,
+// f16 or bf16 by q's format, fp32 accumulate).  Lane l is (n, kg) =
+// (l % 16, l / 16); the MFMA's operands are A[i][k] at lane (i, k / 8),
+// B[k][c] at lane (c, k / 8) and C[i][c] at lane (c, i / 4).  The query heads
+// of a unit (up to 16) are the MFMA columns; columns past the unit's G have
+// q = 0 and are never stored.  Pages go in pairs of 32 keys:
+//  * S^T = K Q^T per page in D / 32 k-steps: lane (n, kg) loads 16-byte
+//    pieces of K row n (load i covers bytes 64 i + 16 kg .. of the row, so
+//    every load instruction reads 64 contiguous bytes of each of 16 rows);
+//    FP8 codes are converted exactly to q's format.  Q^T, the B operand,
+//    takes the same element order.  Lane (n, kg) then holds the scores of
+//    head n for keys 4 kg + r of the page (r < 4).
+//  * Online softmax in fp32, log2 domain, with a running max per head that
+//    only moves when a score exceeds it by more than 2^8 (one wave vote per
+//    page pair; the head's maximum is reduced over its four lanes).  Keys
+//    outside [max(0, n - window), n) get score -inf and their V rows are
+//    replaced by zeros: NaN garbage in unused rows never reaches a product.
+//  * The probabilities are rounded to q's 16-bit format (the row sums use the
+//    rounded values).  Keys 4 kg + r of page A then of page B are exactly the
+//    A operand (head n, 8 keys) of O = P V, so the probabilities stay in
+//    place.
+//  * V: lane (n, kg) loads, for those 8 keys, the D / 16 elements
+//    (D / 16) n .. of each row (16 lanes cover a row, 4 rows per load
+//    instruction).  The B operand of output tile mt is element mt of the 8
+//    rows, paired by byte or half-word permutes (and converted exactly from
+//    FP8), so the accumulator of tile mt holds O[head 4 kg + r][(D/16) n + mt]
+//    and a lane finally stores D / 16 consecutive outputs of each of its heads.
+//  * PP page pairs of K and V are in flight per wave (2 for FP8 pages, 1 for
+//    16-bit: 16 KiB at D = 128).  The next pair's K is loaded as soon as
+//    S^T has consumed the registers and its V as soon as O has; past the end
+//    of the stretch the loads read a spare page of the workspace (kept hot in
+//    L2), so no buffer goes through a control-flow merge.
 #include <atomic>
 #include <cstdlib>
 #include <type_traits>
@@ -54,10 +63,6 @@ namespace vp {
 constexpr int kNW = kDecodeWaves;
 constexpr float kTau = 8.0f;       // rescale headroom, log2 units
 constexpr int kScanMax = 2048;     // sequences whose page prefix fits in LDS
-
-template <int KF> struct KvChunk { using T = uint4; };      // 8 x 16-bit
-template <> struct KvChunk<kE4M3> { using T = uint2; };     // 8 x fp8
-template <> struct KvChunk<kE5M2> { using T = uint2; };
 
 // Streaming (non-temporal) loads: every KV byte is read once per call.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -73,19 +78,6 @@ template <>
 __device__ __forceinline__ uint2 ld_stream<uint2>(const uint8_t* ptr) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ptr));
   return make_uint2(v.x, v.y);
-}
-
-// 8 K elements -> 4 packed pairs in q's format.
-template <int KF, int QF>
-__device__ __forceinline__ void k_pairs(const typename KvChunk<KF>::T& x, uint32_t (&w)[4]) {
-  if constexpr (!is_fp8(KF)) {
-    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-  } else {
-    w[0] = fp8x2_to_q16<KF, QF, false>(x.x);
-    w[1] = fp8x2_to_q16<KF, QF, true>(x.x);
-    w[2] = fp8x2_to_q16<KF, QF, false>(x.y);
-    w[3] = fp8x2_to_q16<KF, QF, true>(x.y);
-  }
 }
 
 // Two 16-bit values (low, high) of q's format from two floats, round to
@@ -107,47 +99,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(bitcast<half2_t>(a), bitcast<half2_t>(b), c, false);
   else
     return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a), bitcast<bf16x2_t>(b), c, false);
-}
-
-// V elements of two tokens, paired per element for dot2: o[e] holds
-// (element e of token A, element e of token B) in q's 16-bit format.
-template <int KF, int QF>
-__device__ __forceinline__ void v_pairs(const typename KvChunk<KF>::T& a,
-                                        const typename KvChunk<KF>::T& b, uint32_t (&o)[8]) {
-  if constexpr (!is_fp8(KF)) {
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = __builtin_amdgcn_perm(bw[i], aw[i], 0x05040100u);       // (a.lo, b.lo)
-      o[2 * i + 1] = __builtin_amdgcn_perm(bw[i], aw[i], 0x07060302u);   // (a.hi, b.hi)
-    }
-  } else {
-    const uint32_t aw[2] = {a.x, a.y};
-    const uint32_t bw[2] = {b.x, b.y};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      // byte interleave (a0, b0, a1, b1) and (a2, b2, a3, b3), then convert
-      // each byte pair exactly to two 16-bit values.
-      const uint32_t w01 = __builtin_amdgcn_perm(bw[i], aw[i], 0x05010400u);
-      const uint32_t w23 = __builtin_amdgcn_perm(bw[i], aw[i], 0x07030602u);
-      o[4 * i + 0] = fp8x2_to_q16<KF, QF, false>(w01);
-      o[4 * i + 1] = fp8x2_to_q16<KF, QF, true>(w01);
-      o[4 * i + 2] = fp8x2_to_q16<KF, QF, false>(w23);
-      o[4 * i + 3] = fp8x2_to_q16<KF, QF, true>(w23);
-    }
-  }
-}
-
-template <int QF>
-__device__ __forceinline__ float lo16_to_f32(uint32_t w) {
-  if constexpr (QF == kBF16) return bitcast<float>(w << 16);
-  else return (float)bitcast<half2_t>(w).x;
-}
-template <int QF>
-__device__ __forceinline__ float hi16_to_f32(uint32_t w) {
-  if constexpr (QF == kBF16) return bitcast<float>(w & 0xFFFF0000u);
-  else return (float)bitcast<half2_t>(w).y;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -286,38 +237,62 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int s, int hk,
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
 }
 
-// AP: with the fused cache write of each sequence's newest token (a variant
-// of its own, so that the plain decode keeps its registers).
-template <int D, int G, int KF, int QF, int LPR, int PD, bool AP>
-__global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
-  constexpr int CH = D / 8;
-  static_assert(LPR >= 4 && LPR <= CH, "lanes per K row");
-  constexpr int CPL = CH / LPR;          // chunks per lane per K row
-  constexpr int RPI = 64 / LPR;          // K rows per load instruction
-  constexpr int NKI = CH / 4;            // load instructions per page (K or V)
-  constexpr int TPL = 16 / RPI;          // K rows per lane per page
-  constexpr int RPIV = 64 / CH;          // V rows per load instruction
-  static_assert(NKI % 2 == 0, "V rows are paired");
-  constexpr int GW = (G + 1) / 2;        // dwords of packed probabilities per token
-  using LT = typename KvChunk<KF>::T;
-  constexpr int CB = (int)sizeof(LT);    // bytes per 8-element chunk
-  constexpr int ROWB = CH * CB;
-  constexpr int64_t kPageBytes = 16 * ROWB;
+// ---- the decode kernel (matrix cores; see the top of this file) -------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+template <int QF>
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+  if constexpr (QF == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+}
+
+template <int D, int KF>
+struct MmaShape {
+  static constexpr int EB = is_fp8(KF) ? 1 : 2;     // bytes per pool element
+  static constexpr int RB = D * EB;                  // bytes per K / V row
+  static constexpr int STEPS = D / 32;               // k-steps of S^T per page
+  static constexpr int NL = RB / 64;                 // 16-byte K loads per lane per page
+  static constexpr int TILES = D / 16;               // output tiles of 16 d
+  static constexpr int VW = TILES * EB / 4;          // 32-bit words of V per lane per row
+};
+
+template <int NW> struct Words { uint32_t w[NW]; };
+
+template <int NW>
+__device__ __forceinline__ Words<NW> ld_words(const uint8_t* ptr) {
+  Words<NW> r;
+  if constexpr (NW == 4) {
+    const uint4 x = ld_stream<uint4>(ptr);
+    r.w[0] = x.x; r.w[1] = x.y; r.w[2] = x.z; r.w[3] = x.w;
+  } else if constexpr (NW == 2) {
+    const uint2 x = ld_stream<uint2>(ptr);
+    r.w[0] = x.x; r.w[1] = x.y;
+  } else {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ptr));
+  }
+  return r;
+}
+
+template <int D, int KF, int QF, int PP, bool AP>
+__global__ __launch_bounds__(kNW * 64) void decode_mma_kernel(DecodeParams p) {
+  using S = MmaShape<D, KF>;
+  constexpr int EB = S::EB, RB = S::RB, STEPS = S::STEPS, NL = S::NL, TILES = S::TILES, VW = S::VW;
+  constexpr int64_t kPageBytes = 16 * RB;
 
   __shared__ int s_pre[kScanMax + 1];
-  __shared__ int s_ctx[kScanMax];      // context lengths (batches of up to kScanMax)
-  __shared__ uint32_t s_p[kNW][16][GW];
+  __shared__ int s_ctx[kScanMax];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rho = lane / LPR, c = lane % LPR;          // K role
-  const int rv = lane / CH, cv = lane % CH;            // V role
   const int B = p.num_seqs;
+  const int G = p.head_chunk;
   const int ngc = p.group / G;
   const int NY = p.num_kv_heads * ngc;                 // units per sequence
 
-  // Page prefix over the batch: in LDS for small batches (workgroup 0 also
-  // stores it for the merge), else precomputed in the workspace.
   const int* pre;
   if (B <= kScanMax) {
     page_prefix(p, s_pre, s_ctx);
@@ -330,8 +305,6 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
                                       : max((int64_t)1, (T + p.num_workers - 1) / p.num_workers);
   const int64_t num_chunks = (T + C - 1) / C;
 
-  // Sequences with no key to attend to get all-zero output rows (with a
-  // shared prefix the merge writes their rows from the prefix partials).
   for (int sq = blockIdx.x; sq < B; sq += gridDim.x) {
     if (pre[sq + 1] == pre[sq]) {
       if (p.skip_tokens == 0) {
@@ -343,16 +316,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
   }
 
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
-  int koff[NKI];
-#pragma unroll
-  for (int k = 0; k < NKI; ++k)
-    koff[k] = ((k / CPL) * RPI + rho) * ROWB + ((k % CPL) * LPR + c) * CB;
+  constexpr uint32_t kOnes = QF == kBF16 ? 0x3F803F80u : 0x3C003C00u;   // (1, 1)
 
   for (int64_t chunk = (int64_t)blockIdx.x * kNW + wave; chunk < num_chunks;
        chunk += p.num_workers) {
     int64_t g = chunk * C;
     const int64_t g_end = min(g + C, T);
-    // sequence holding global page g: last s with NY * pre[s] <= g
     int s = 0;
     {
       int lo_s = 0, hi_s = B - 1;
@@ -364,8 +333,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
     }
     bool first_seg = true;
     while (g < g_end) {
-      // (values read from LDS are wave-uniform: keep them in scalar registers)
-      while ((int64_t)NY * __builtin_amdgcn_readfirstlane(pre[s + 1]) <= g) ++s;   // skip empty seqs
+      while ((int64_t)NY * __builtin_amdgcn_readfirstlane(pre[s + 1]) <= g) ++s;
       const SeqRange sr = seq_range_of(
           p, B <= kScanMax ? __builtin_amdgcn_readfirstlane(s_ctx[s]) : p.context_lens[s]);
       const int64_t off = g - (int64_t)NY * __builtin_amdgcn_readfirstlane(pre[s]);
@@ -373,40 +341,42 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
       const int i0 = (int)(off - (int64_t)y * sr.np);
       const int i1 = (int)min((int64_t)sr.np, i0 + (g_end - g));
       const int slot = first_seg ? 0 : 1;
-      // A unit finished inside this chunk writes its output directly, or,
-      // when shared-prefix partials still have to be merged in, its partial
-      // to a slot of its own (a chunk may hold several whole units).
       const bool whole = (i0 == 0) && (i1 == sr.np);
       const bool complete = whole && p.skip_tokens == 0;
       const int hk = y / ngc;
       const int h0 = hk * p.group + (y - hk * ngc) * G;
-      // FP8 scales of this kv-head (per-head arrays, else the per-tensor ones)
       const float sscale = p.k_scales ? p.score_base * p.k_scales[hk] : p.score_scale;
       const float oscale = p.v_scales ? p.v_scales[hk] : p.out_scale;
+      // (the lane roles as opaque values: nothing lane-dependent is hoisted
+      // out of the segment loop to hold registers through the page stream)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int n = ln & 15, kg = ln >> 4;
+      const int k_lane = n * RB + 16 * kg;               // this lane's K bytes in a page (+ 64 i)
+      const int v_lane = n * (TILES * EB);               // this lane's V bytes in a row
+      const bool head_ok = n < G;
 
-      // ---- one segment: pages [i0, i1) of unit (s, y) ----
       if constexpr (AP) {
         if (i1 == sr.np) append_row<D, KF, QF>(p, s, hk, lane);
       }
-      uint4 qv[G][CPL];
+      // Q^T operand: head n, the k-step's 8 elements in the K loads' order
+      uint4 qv[STEPS];
       {
         const uint16_t* qp =
-            static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.num_q_heads + h0) * D;
+            static_cast<const uint16_t*>(p.q) + ((int64_t)s * p.num_q_heads + h0 + min(n, G - 1)) * D;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int sub = 0; sub < CPL; ++sub)
-            qv[h][sub] = *reinterpret_cast<const uint4*>(qp + h * D + (sub * LPR + c) * 8);
+        for (int t = 0; t < STEPS; ++t) {
+          const int e = is_fp8(KF) ? 64 * (t / 2) + 16 * kg + 8 * (t % 2) : 32 * t + 8 * kg;
+          const uint4 x = *reinterpret_cast<const uint4*>(qp + e);
+          qv[t] = head_ok ? x : make_uint4(0, 0, 0, 0);
+        }
       }
       const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride + sr.lo_page;
       const uint8_t* kbase = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
-      const uint8_t* vbase = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes +
-                             rv * ROWB + cv * CB;
+      const uint8_t* vbase = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes;
       const uint8_t* spare = static_cast<const uint8_t*>(p.ws_spare);
-      const uint8_t* spare_v = spare + rv * ROWB + cv * CB;
       const int count = i1 - i0;
-      // Block ids, 64 pages per lane vector; the next 64 are fetched one
-      // batch ahead so that reading them never waits on the page loads.
+      const int npairs = (count + 1) >> 1;
       int bt_base = 0;
       auto bt_fetch = [&](int base) __attribute__((always_inline)) {
         const int q = i0 + base + lane;
@@ -415,204 +385,192 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
       };
       int bt_cur = bt_fetch(0), bt_nxt = count > 64 ? bt_fetch(64) : 0;
       auto blk_of = [&](int jj) __attribute__((always_inline)) {
-        if (jj >= bt_base + 64) {          // pages are requested in increasing order
+        if (jj >= bt_base + 64) {
           bt_base += 64;
           bt_cur = bt_nxt;
           if (bt_base + 64 < count) bt_nxt = bt_fetch(bt_base + 64);
         }
         return __builtin_amdgcn_readlane(bt_cur, jj - bt_base);
       };
-      // kp: the page's K base (this kv-head); vp: its V base plus this lane's offset
-      auto load_k = [&](const uint8_t* kp, LT (&kd)[NKI]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int k = 0; k < NKI; ++k) kd[k] = ld_stream<LT>(kp + koff[k]);
+      // page of pair jp, half h (0: A, 1: B); past the segment: the spare page
+      auto page_ptr = [&](const uint8_t* base, int jp, int h) __attribute__((always_inline)) {
+        const int jj = 2 * jp + h;
+        return jj < count ? base + blk_of(min(jj, count - 1)) * blk_stride : spare;
       };
-      auto load_v = [&](const uint8_t* vp, LT (&vd)[NKI]) __attribute__((always_inline)) {
+      auto load_k = [&](int jp, uint4 (&kd)[2][NL]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < NKI; ++k) vd[k] = ld_stream<LT>(vp + k * RPIV * ROWB);
+        for (int h = 0; h < 2; ++h) {
+          const uint8_t* pg = page_ptr(kbase, jp, h) + k_lane;
+#pragma unroll
+          for (int i = 0; i < NL; ++i) kd[h][i] = ld_stream<uint4>(pg + 64 * i);
+        }
+      };
+      auto load_v = [&](int jp, Words<VW> (&vd)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint8_t* pg = page_ptr(vbase, jp, h) + v_lane;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vd[4 * h + r] = ld_words<VW>(pg + (4 * kg + r) * RB);
+        }
       };
 
-      float m[G], l[G], acc[G][8];
+      float m = -INFINITY, l = 0.0f;
+      f32x4_t o[TILES];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
+      for (int t = 0; t < TILES; ++t) o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+      uint4 kd[PP][2][NL];
+      Words<VW> vd[PP][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+      for (int u = 0; u < PP; ++u) {
+        load_k(u, kd[u]);
+        load_v(u, vd[u]);
       }
-      // PD pages of K and V in flight: buffer u holds page jb + u.  Loads are
-      // unconditional (past the end they re-read the last page) so that no
-      // buffer goes through a control-flow merge.
-      LT kd[PD][NKI], vd[PD][NKI];
+      for (int jb = 0; jb < npairs; jb += PP) {
 #pragma unroll
-      for (int u = 0; u < PD; ++u) {
-        const int b0 = blk_of(min(u, count - 1));
-        load_k(u < count ? kbase + b0 * blk_stride : spare, kd[u]);
-        load_v(u < count ? vbase + b0 * blk_stride : spare_v, vd[u]);
-      }
-      for (int jb = 0; jb < count; jb += PD) {
-#pragma unroll
-        for (int u = 0; u < PD; ++u) {
-          const int jj = jb + u;
-          const bool valid = jj < count;
-          const int t0 = (sr.lo_page + i0 + min(jj, count - 1)) * 16;
-          const bool full = (t0 >= sr.lo) && (t0 + 16 <= sr.n);
-          // page loaded into this buffer next; past the end of the stretch
-          // the loads read the spare page instead (kept hot in L2, its
-          // values are never used)
-          const bool past = jj + PD >= count;
-          const int bn = blk_of(min(jj + PD, count - 1));
-          const uint8_t* knext = past ? spare : kbase + bn * blk_stride;
-          const uint8_t* vnext = past ? spare_v : vbase + bn * blk_stride;
-          float sc[TPL][G];
+        for (int u = 0; u < PP; ++u) {
+          const int jp = jb + u;
+          const bool valid = jp < npairs;
+          const int t0 = (sr.lo_page + i0 + 2 * min(jp, npairs - 1)) * 16;   // first key of page A
+          const bool has_b = 2 * jp + 1 < count;
+          const bool full = has_b && (t0 >= sr.lo) && (t0 + 32 <= sr.n);
+          float sc[8];
           if (valid) {
-            // ---- Q.K (K role) ----
+            // ---- S^T = K Q^T, page A then page B ----
 #pragma unroll
-            for (int rg = 0; rg < TPL; ++rg)
+            for (int h = 0; h < 2; ++h) {
+              f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-              for (int h = 0; h < G; ++h) sc[rg][h] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < NKI; ++k) {
-              uint32_t kw[4];
-              k_pairs<KF, QF>(kd[u][k], kw);
-#pragma unroll
-              for (int h = 0; h < G; ++h) {
-                const uint4 qq = qv[h][k % CPL];
-                float a = sc[k / CPL][h];
-                a = dot2<QF>(qq.x, kw[0], a);
-                a = dot2<QF>(qq.y, kw[1], a);
-                a = dot2<QF>(qq.z, kw[2], a);
-                a = dot2<QF>(qq.w, kw[3], a);
-                sc[k / CPL][h] = a;
+              for (int t = 0; t < STEPS; ++t) {
+                uint4 ka;
+                if constexpr (!is_fp8(KF)) {
+                  ka = kd[u][h][t];
+                } else {
+                  const uint4 x = kd[u][h][t / 2];
+                  const uint32_t lo = (t % 2) ? x.z : x.x, hi = (t % 2) ? x.w : x.y;
+                  ka = make_uint4(fp8x2_to_q16<KF, QF, false>(lo), fp8x2_to_q16<KF, QF, true>(lo),
+                                  fp8x2_to_q16<KF, QF, false>(hi), fp8x2_to_q16<KF, QF, true>(hi));
+                }
+                acc = mfma16<QF>(ka, qv[t], acc);
               }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sc[4 * h + r] = acc[r] * sscale;
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-          load_k(knext, kd[u]);
+          load_k(jp + PP, kd[u]);
           __builtin_amdgcn_sched_barrier(0);
           if (valid) {
-#pragma unroll
-            for (int rg = 0; rg < TPL; ++rg)
-#pragma unroll
-              for (int h = 0; h < G; ++h) sc[rg][h] = group_sum<LPR>(sc[rg][h]) * sscale;
+            // keys outside [lo, n) and page B past the segment: -inf.  (Heads
+            // past G have q = 0, so finite scores; they only reach output rows
+            // that are never stored.)
             if (!full) {
 #pragma unroll
-              for (int rg = 0; rg < TPL; ++rg) {
-                const int t = t0 + rg * RPI + rho;
-                if (t < sr.lo || t >= sr.n) {
-#pragma unroll
-                  for (int h = 0; h < G; ++h) sc[rg][h] = -INFINITY;
-                }
+              for (int j = 0; j < 8; ++j) {
+                const int t = t0 + 16 * (j >> 2) + 4 * kg + (j & 3);
+                const bool keep = t >= sr.lo && t < sr.n && (j < 4 || has_b);
+                if (!keep) sc[j] = -INFINITY;
               }
             }
-
-            // ---- online softmax ----
+            // ---- online softmax (head n; its four lanes agree on m) ----
             bool need = false;
 #pragma unroll
-            for (int rg = 0; rg < TPL; ++rg)
-#pragma unroll
-              for (int h = 0; h < G; ++h) need |= sc[rg][h] > m[h] + kTau;
+            for (int j = 0; j < 8; ++j) need |= sc[j] > m + kTau;
             if (__any(need)) {
+              float pm = sc[0];
 #pragma unroll
-              for (int h = 0; h < G; ++h) {
-                float pm = sc[0][h];
+              for (int j = 1; j < 8; ++j) pm = fmaxf(pm, sc[j]);
+              pm = fmaxf(pm, __shfl_xor(pm, 16));
+              pm = fmaxf(pm, __shfl_xor(pm, 32));
+              const float mn = fmaxf(m, pm);
+              const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2(m - mn);
+              m = mn;
+              l *= alpha;
+              // accumulator rows are heads 4 kg + r: their factors from lanes 4 kg + r
 #pragma unroll
-                for (int rg = 1; rg < TPL; ++rg) pm = fmaxf(pm, sc[rg][h]);
-                pm = wave_max(pm);
-                const float mn = fmaxf(m[h], pm);
-                const float alpha = (m[h] == -INFINITY) ? 0.0f : fast_exp2(m[h] - mn);
-                m[h] = mn;
-                l[h] *= alpha;
+              for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * kg + r);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+                for (int t = 0; t < TILES; ++t) o[t][r] *= ar;
               }
             }
+            const float mu = (m == -INFINITY) ? 0.0f : m;
+            uint32_t pw[4];
 #pragma unroll
-            for (int rg = 0; rg < TPL; ++rg) {
-              uint32_t pw[GW];
+            for (int w = 0; w < 4; ++w) {
+              pw[w] = pack16<QF>(fast_exp2(sc[2 * w] - mu), fast_exp2(sc[2 * w + 1] - mu));
+              l = dot2<QF>(pw[w], kOnes, l);              // row sum of the rounded weights
+            }
+            const uint4 pa = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+            // ---- O += P V ----
+            Words<VW> vv[8];
 #pragma unroll
-              for (int i = 0; i < GW; ++i) {
-                const int ha = 2 * i, hb = 2 * i + 1;
-                const float ma = (m[ha] == -INFINITY) ? 0.0f : m[ha];
-                const float pa = fast_exp2(sc[rg][ha] - ma);
-                float pb = 0.0f;
-                if (hb < G) {
-                  const float mb = (m[hb] == -INFINITY) ? 0.0f : m[hb];
-                  pb = fast_exp2(sc[rg][hb] - mb);
-                }
-                pw[i] = pack16<QF>(pa, pb);
-                l[ha] += lo16_to_f32<QF>(pw[i]);
-                if (hb < G) l[hb] += hi16_to_f32<QF>(pw[i]);
-              }
-              if (c == 0) {
+            for (int j = 0; j < 8; ++j) {
+              vv[j] = vd[u][j];
+              if (!full) {
+                const int t = t0 + 16 * (j >> 2) + 4 * kg + (j & 3);
+                const bool keep = t >= sr.lo && t < sr.n && (j < 4 || has_b);
 #pragma unroll
-                for (int i = 0; i < GW; ++i) s_p[wave][rg * RPI + rho][i] = pw[i];
+                for (int w = 0; w < VW; ++w) vv[j].w[w] = keep ? vv[j].w[w] : 0u;
               }
             }
-
-            // ---- P.V (V role) ----
-            auto pv = [&](const LT (&vx)[NKI]) __attribute__((always_inline)) {
+            if constexpr (!is_fp8(KF)) {
 #pragma unroll
-              for (int pr = 0; pr < NKI / 2; ++pr) {
-                const int ta = (2 * pr) * RPIV + rv, tb = (2 * pr + 1) * RPIV + rv;
-                uint32_t vp2[8];
-                v_pairs<KF, QF>(vx[2 * pr], vx[2 * pr + 1], vp2);
-                uint32_t pp[G];
+              for (int t = 0; t < TILES; ++t) {
+                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t b[4];
 #pragma unroll
-                for (int i = 0; i < GW; ++i) {
-                  const uint32_t A = s_p[wave][ta][i], B2 = s_p[wave][tb][i];
-                  pp[2 * i] = __builtin_amdgcn_perm(B2, A, 0x05040100u);
-                  if (2 * i + 1 < G) pp[2 * i + 1] = __builtin_amdgcn_perm(B2, A, 0x07060302u);
-                }
-#pragma unroll
-                for (int h = 0; h < G; ++h)
-#pragma unroll
-                  for (int e = 0; e < 8; ++e) acc[h][e] = dot2<QF>(pp[h], vp2[e], acc[h][e]);
+                for (int w = 0; w < 4; ++w)
+                  b[w] = __builtin_amdgcn_perm(vv[2 * w + 1].w[t >> 1], vv[2 * w].w[t >> 1], sel);
+                o[t] = mfma16<QF>(pa, make_uint4(b[0], b[1], b[2], b[3]), o[t]);
               }
-            };
-            if (full) {
-              pv(vd[u]);
             } else {
-              // rows outside the kept range may hold NaN: replace them by zeros
-              LT vv[NKI];
 #pragma unroll
-              for (int k = 0; k < NKI; ++k) {
-                const int t = t0 + k * RPIV + rv;
-                vv[k] = (t < sr.lo || t >= sr.n) ? LT{} : vd[u][k];
+              for (int t = 0; t < TILES; t += 2) {
+                const int q = t & 3;                      // byte of the word (0 or 2)
+                const uint32_t sel = (uint32_t)q | ((uint32_t)(4 + q) << 8) |
+                                     ((uint32_t)(q + 1) << 16) | ((uint32_t)(5 + q) << 24);
+                uint32_t b0[4], b1[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                  const uint32_t x =
+                      __builtin_amdgcn_perm(vv[2 * w + 1].w[t >> 2], vv[2 * w].w[t >> 2], sel);
+                  b0[w] = fp8x2_to_q16<KF, QF, false>(x);
+                  b1[w] = fp8x2_to_q16<KF, QF, true>(x);
+                }
+                o[t] = mfma16<QF>(pa, make_uint4(b0[0], b0[1], b0[2], b0[3]), o[t]);
+                o[t + 1] = mfma16<QF>(pa, make_uint4(b1[0], b1[1], b1[2], b1[3]), o[t + 1]);
               }
-              pv(vv);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-          load_v(vnext, vd[u]);
+          load_v(jp + PP, vd[u]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      // Sum the V rows (lanes cv, cv + CH, ...) and the K-role row sums (one
-      // lane per row: c == 0).  m is uniform over the wave.
-#pragma unroll
-      for (int off = CH; off < 64; off <<= 1)
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
-#pragma unroll
-      for (int h = 0; h < G; ++h) l[h] = wave_sum(c == 0 ? l[h] : 0.0f);
-
+      // Sums of head n over its four lanes; accumulator rows 4 kg + r take
+      // theirs (and m) from lanes 4 kg + r.
+      float lt = l + __shfl_xor(l, 16);
+      lt += __shfl_xor(lt, 32);
       if (complete) {
-        if (rv == 0) {
+        const float inv = oscale / lt;
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float inv = oscale / l[h];
-            uint32_t w[4];
+        for (int r = 0; r < 4; ++r) {
+          const float ir = __shfl(inv, 4 * kg + r);
+          const int h = 4 * kg + r;
+          if (h < G) {
+            uint32_t w[TILES / 2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              w[i] = (uint32_t)f32_to_16<QF>(acc[h][2 * i] * inv) |
-                     ((uint32_t)f32_to_16<QF>(acc[h][2 * i + 1] * inv) << 16);
-            uint16_t* o = static_cast<uint16_t*>(p.out) +
-                          ((int64_t)s * p.num_q_heads + h0 + h) * D + cv * 8;
-            *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+            for (int t = 0; t < TILES / 2; ++t)
+              w[t] = (uint32_t)f32_to_16<QF>(o[2 * t][r] * ir) |
+                     ((uint32_t)f32_to_16<QF>(o[2 * t + 1][r] * ir) << 16);
+            uint16_t* op = static_cast<uint16_t*>(p.out) +
+                           ((int64_t)s * p.num_q_heads + h0 + h) * D + n * TILES;
+            if constexpr (TILES == 8)
+              *reinterpret_cast<uint4*>(op) = make_uint4(w[0], w[1], w[2], w[3]);
+            else
+              *reinterpret_cast<uint2*>(op) = make_uint2(w[0], w[1]);
           }
         }
       } else {
@@ -621,35 +579,30 @@ __global__ __launch_bounds__(kNW * 64) void decode_kernel(DecodeParams p) {
         float* wo = whole ? p.ws_uo + unit * G * D : p.ws_o + sl * G * D;
         float* wm = whole ? p.ws_um + unit * G : p.ws_m + sl * G;
         float* wl = whole ? p.ws_ul + unit * G : p.ws_l + sl * G;
-        if (rv == 0) {
+        const float inv = 1.0f / lt;
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float inv = 1.0f / l[h];
-            float* o = wo + h * D + cv * 8;
-            *reinterpret_cast<float4*>(o) =
-                make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
-            *reinterpret_cast<float4*>(o + 4) =
-                make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+        for (int r = 0; r < 4; ++r) {
+          const float ir = __shfl(inv, 4 * kg + r);
+          const int h = 4 * kg + r;
+          if (h < G) {
+            float* op = wo + h * D + n * TILES;
+#pragma unroll
+            for (int t = 0; t < TILES; t += 4)
+              *reinterpret_cast<float4*>(op + t) =
+                  make_float4(o[t][r] * ir, o[t + 1][r] * ir, o[t + 2][r] * ir, o[t + 3][r] * ir);
           }
         }
-        if (lane == 0) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            wm[h] = m[h];
-            wl[h] = l[h];
-          }
+        if (kg == 0 && head_ok) {
+          wm[n] = m;
+          wl[n] = lt;
         }
       }
-      // The wave holding page 0 of the unit records where its pieces are:
-      // (slot of the first piece, number of pieces), or 0 pieces if done
-      // (a unit inside one chunk with a shared prefix has 1 piece).
       if (i0 == 0 && lane == 0) {
         int npieces = 0;
         if (!complete) {
-          const int64_t base = g;                 // = NY * pre[s] + y * np
+          const int64_t base = g;
           npieces = (int)((base + sr.np - 1) / C - base / C + 1);
         }
-        // (first slot -1: the single piece sits in the unit's own slot)
         p.ws_unit[((int64_t)s * NY + y) * 2] = whole ? -1 : (int32_t)(chunk * 2 + slot);
         p.ws_unit[((int64_t)s * NY + y) * 2 + 1] = npieces;
       }
@@ -764,53 +717,30 @@ __global__ __launch_bounds__(kNW * 64) void decode_prefix_kernel(DecodeParams p)
   page_prefix(p, p.ws_prefix);
 }
 
-// Lanes per K row: fewer lanes -> fewer cross-lane sums but more query
-// registers per lane (CH / LPR chunks per head).
-template <int D, int G>
-constexpr int kLpr = (D == 64) ? (G <= 4 ? 4 : 8) : (G <= 2 ? 4 : (G <= 5 ? 8 : 16));
-
-// Pages of K and V in flight per wave.
-template <int D, int G>
-constexpr int kPd = 2;
-
-template <int D, int G, int KF, int QF>
-static const void* kernel_ptr(bool ap) {
-  return ap ? reinterpret_cast<const void*>(&decode_kernel<D, G, KF, QF, kLpr<D, G>, kPd<D, G>, true>)
-            : reinterpret_cast<const void*>(&decode_kernel<D, G, KF, QF, kLpr<D, G>, kPd<D, G>, false>);
-}
-
+// Decode kernels: 2 page pairs in flight for FP8 pages, 1 for 16-bit.
 template <int D, int KF, int QF>
-static const void* pick(int gc, bool ap) {
-  switch (gc) {
-    case 1: return kernel_ptr<D, 1, KF, QF>(ap);
-    case 2: return kernel_ptr<D, 2, KF, QF>(ap);
-    case 3: return kernel_ptr<D, 3, KF, QF>(ap);
-    case 4: return kernel_ptr<D, 4, KF, QF>(ap);
-    case 5: return kernel_ptr<D, 5, KF, QF>(ap);
-    case 6: return kernel_ptr<D, 6, KF, QF>(ap);
-    case 7: return kernel_ptr<D, 7, KF, QF>(ap);
-    case 8: return kernel_ptr<D, 8, KF, QF>(ap);
-    default: return nullptr;
-  }
+static const void* mma_ptr(bool ap) {
+  constexpr int PP = is_fp8(KF) ? 2 : 1;
+  return ap ? reinterpret_cast<const void*>(&decode_mma_kernel<D, KF, QF, PP, true>)
+            : reinterpret_cast<const void*>(&decode_mma_kernel<D, KF, QF, PP, false>);
 }
 
-static const void* decode_kernel_for(int D, int kv_fmt, int q_fmt, int gc, bool ap) {
-  if (D == 128) {
-    if (kv_fmt == kF16 && q_fmt == kF16) return pick<128, kF16, kF16>(gc, ap);
-    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<128, kBF16, kBF16>(gc, ap);
-    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<128, kE4M3, kF16>(gc, ap);
-    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<128, kE4M3, kBF16>(gc, ap);
-    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<128, kE5M2, kF16>(gc, ap);
-    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<128, kE5M2, kBF16>(gc, ap);
-  } else if (D == 64) {
-    if (kv_fmt == kF16 && q_fmt == kF16) return pick<64, kF16, kF16>(gc, ap);
-    if (kv_fmt == kBF16 && q_fmt == kBF16) return pick<64, kBF16, kBF16>(gc, ap);
-    if (kv_fmt == kE4M3 && q_fmt == kF16) return pick<64, kE4M3, kF16>(gc, ap);
-    if (kv_fmt == kE4M3 && q_fmt == kBF16) return pick<64, kE4M3, kBF16>(gc, ap);
-    if (kv_fmt == kE5M2 && q_fmt == kF16) return pick<64, kE5M2, kF16>(gc, ap);
-    if (kv_fmt == kE5M2 && q_fmt == kBF16) return pick<64, kE5M2, kBF16>(gc, ap);
-  }
+static const void* decode_mma_kernel_for(int D, int kv_fmt, int q_fmt, bool ap) {
+#define VP_MMA(DD)                                                                    \
+  if (kv_fmt == kF16 && q_fmt == kF16) return mma_ptr<DD, kF16, kF16>(ap);            \
+  if (kv_fmt == kBF16 && q_fmt == kBF16) return mma_ptr<DD, kBF16, kBF16>(ap);        \
+  if (kv_fmt == kE4M3 && q_fmt == kF16) return mma_ptr<DD, kE4M3, kF16>(ap);          \
+  if (kv_fmt == kE4M3 && q_fmt == kBF16) return mma_ptr<DD, kE4M3, kBF16>(ap);        \
+  if (kv_fmt == kE5M2 && q_fmt == kF16) return mma_ptr<DD, kE5M2, kF16>(ap);          \
+  if (kv_fmt == kE5M2 && q_fmt == kBF16) return mma_ptr<DD, kE5M2, kBF16>(ap);
+  if (D == 128) { VP_MMA(128) }
+  if (D == 64) { VP_MMA(64) }
+#undef VP_MMA
   return nullptr;
+}
+
+static const void* decode_kernel_for(int D, int kv_fmt, int q_fmt, bool ap) {
+  return decode_mma_kernel_for(D, kv_fmt, q_fmt, ap);
 }
 
 template <int D, int QF>
@@ -838,12 +768,11 @@ static const void* merge_kernel_for(int D, int q_fmt, int gc) {
 // workgroups per CU: filled on first use, read without locks (a racing first
 // use computes the same value twice).
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2 * 2 * 4 * 16;     // (append, D = 128, kv format, q format, G)
+constexpr int kVariants = 2 * 2 * 4 * 2;      // (append, D = 128, kv format, q format)
 static std::atomic<int> g_cus[kMaxDevices];
 static std::atomic<int> g_occ[kMaxDevices][kVariants];
 
-int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int head_chunk,
-                   bool append) {
+int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int, bool append) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
@@ -859,13 +788,13 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
     }
     if (cached) g_cus[dev].store(cus, std::memory_order_relaxed);
   }
-  int per_cu = 4;
-  const int vi = (((int)append * 2 + (head_dim == 128)) * 4 + kv_fmt) * 16 + q_fmt * 8 + (head_chunk - 1);
+  int per_cu = 2;
+  const int vi = (((int)append * 2 + (head_dim == 128)) * 4 + kv_fmt) * 2 + (q_fmt == kBF16);
   const bool vcached = cached && vi >= 0 && vi < kVariants;
   const int occ_seen = vcached ? g_occ[dev][vi].load(std::memory_order_relaxed) : 0;
   if (occ_seen > 0) {
     per_cu = occ_seen;
-  } else if (const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, head_chunk, append)) {
+  } else if (const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, append)) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, kNW * 64, 0) == hipSuccess && occ > 0) {
       per_cu = occ;
@@ -874,6 +803,10 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
       (void)hipGetLastError();
     }
   }
+  // The kernel fits three workgroups per CU at head_dim 128 (more at 64), but
+  // two are faster: a third makes the chunks a third shorter (more pieces to
+  // merge) and leaves no room beside the decode for the shared-prefix pass.
+  per_cu = min(per_cu, 2);
   if (const char* e = getenv("VLLM_PAGED_WG_PER_CU")) {
     const int v = atoi(e);
     if (v > 0) per_cu = v;
@@ -885,7 +818,7 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream,
                          bool split) {
   if (p.num_seqs == 0) return hipSuccess;
-  const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, p.head_chunk, p.new_slots != nullptr);
+  const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, p.new_slots != nullptr);
   const void* mk = merge_kernel_for(head_dim, q_fmt, p.head_chunk);
   if (!k || !mk) return hipErrorInvalidValue;
   DecodeParams a = p;
