@@ -629,11 +629,11 @@ def bench_decode(idx: int, case, args, steps: int, warmup: int, cpu=None,
                            "p50": round(float(np.percentile(dec_ms, 50)), 5),
                            "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("decode call (attn_tile_kernel shared-prefix pass + decode_kernel + "
+                     "kernel": ("decode call (attn_tile_kernel shared-prefix pass + decode_mma_kernel + "
                                 "decode_merge_kernel), unique bytes" if shared_pages else
-                                "decode call with the fused cache write (decode_kernel + "
+                                "decode call with the fused cache write (decode_mma_kernel + "
                                 "decode_merge_kernel)" if fused else
-                                "decode call (decode_kernel + decode_merge_kernel)"),
+                                "decode call (decode_mma_kernel + decode_merge_kernel)"),
                      "bytes_per_call": call_bytes, "ms_per_call": round(call_ms, 5),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

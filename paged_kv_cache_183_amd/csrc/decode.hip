@@ -712,7 +712,7 @@ __global__ __launch_bounds__(G * D / 4) void decode_merge_kernel(DecodeParams p)
   *reinterpret_cast<uint2*>(out) = make_uint2(lo, hi);
 }
 
-// Page prefix for batches too large for the LDS scan of decode_kernel.
+// Page prefix for batches too large for the LDS scan of decode_mma_kernel.
 __global__ __launch_bounds__(kNW * 64) void decode_prefix_kernel(DecodeParams p) {
   page_prefix(p, p.ws_prefix);
 }
