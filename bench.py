@@ -41,7 +41,12 @@ METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + seqs/s"
 PREFILL_METRIC = "chunked-prefill paged attention: TFLOP/s (% bf16 MFMA peak) + tokens/s"
 
 
-def measured_traffic(workload: str, sources=("decode.hip", "common.h")):
+DECODE_SOURCES = ("decode.hip", "common.h", "kernels.h")
+SHARED_SOURCES = ("decode.hip", "attn_tile.h", "common.h", "kernels.h")
+PREFILL_SOURCES = ("prefill.hip", "attn_tile.h", "common.h", "kernels.h")
+
+
+def measured_traffic(workload: str, sources=DECODE_SOURCES):
     """HBM bytes per call (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy)
     from the committed counter summary ``profiles/<workload>_hbm_counters.txt``,
     or None when there is none or the kernel sources changed since the
@@ -258,7 +263,7 @@ def bench_prefill(case, steps: int, warmup: int, chunk: int = 0) -> dict:
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": None if chunk else
-                         measured_traffic(case.name, ("prefill.hip", "common.h"))}}
+                         measured_traffic(case.name, PREFILL_SOURCES)}}
 
 
 def bench_block_manager(steps: int = 20, num_seqs: int = 256, prompt: int = 1024,
@@ -629,8 +634,8 @@ def bench_decode(idx: int, case, args, steps: int, warmup: int, cpu=None,
                            "p50": round(float(np.percentile(dec_ms, 50)), 5),
                            "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("decode call (attn_tile_kernel shared-prefix pass + decode_mma_kernel + "
-                                "decode_merge_kernel), unique bytes" if shared_pages else
+                     "kernel": ("decode call (decode_shared_kernel: decode and shared-prefix tiles in "
+                                "one grid, + decode_merge_kernel), unique bytes" if shared_pages else
                                 "decode call with the fused cache write (decode_mma_kernel + "
                                 "decode_merge_kernel)" if fused else
                                 "decode call (decode_mma_kernel + decode_merge_kernel)"),
@@ -639,8 +644,7 @@ def bench_decode(idx: int, case, args, steps: int, warmup: int, cpu=None,
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "read_ceiling": ceiling["GB_per_s"],
                      "frac_of_read_ceiling": round(achieved / ceiling["GB_per_s"], 4),
-                     "traffic": (measured_traffic(case.name + "_shared_prefix",
-                                                  ("decode.hip", "prefill.hip", "common.h"))
+                     "traffic": (measured_traffic(case.name + "_shared_prefix", SHARED_SOURCES)
                                  if shared_pages else measured_traffic(case.name))},
         "meets_70pct_of_peak": bool(achieved >= 0.7 * HBM_PEAK_GBPS),
         "read_ceiling": ceiling,

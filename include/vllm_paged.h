@@ -268,12 +268,10 @@ vllm_status vllm_paged_attn_decode_noalloc(vllm_tensor* out, const vllm_tensor* 
  * "Building and Deploying vllm.cpp", Step 3).  Those pages are read from
  * sequence 0's table (the other sequences' first shared_pages entries are not
  * read) once per kv-head for the whole batch: every sequence's query is
- * scored against them together on the matrix cores, in splits of 32 pages,
- * on a second stream that the library owns (default priority, one per
- * device, created on first use) forked from hip_stream and joined back to it
- * before the merge, so the call stays ordered on hip_stream.
- * The rest of each sequence is decoded as usual, and the parts are merged with
- * the log-sum-exp rule.  Keys of the shared pages are kept per sequence as in
+ * scored against them together on the matrix cores, in splits of 64 pages,
+ * by workgroups of the same launch as the decode of the rest of each
+ * sequence (so the call is two kernels on hip_stream and uses no other
+ * stream), and the parts are merged with the log-sum-exp rule.  Keys of the shared pages are kept per sequence as in
  * decode: t < n (a sequence shorter than the prefix uses its first n tokens)
  * and t >= n - window.  The probabilities of the shared part are rounded to
  * q's 16-bit format before the product with V, as in decode.

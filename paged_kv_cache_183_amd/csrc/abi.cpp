@@ -13,7 +13,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
-#include <map>
 #include <mutex>
 #include <string>
 
@@ -134,32 +133,6 @@ vllm_status check_data(const vllm_tensor* t, const char* name, uintptr_t align) 
 vllm_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return VLLM_OK;
   return fail(VLLM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
-}
-
-// A second stream per device, with a fork and a join event: the shared-prefix
-// pass (matrix cores) runs on it beside the suffix decode (memory bound) of
-// the same call.  Default priority; created on first use and kept for the
-// life of the process.  The mutex keeps each fork/launch/join sequence whole
-// when several host threads call at once.
-struct AuxStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_aux_mu;
-std::map<int, AuxStream> g_aux;
-
-hipError_t aux_stream(AuxStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  AuxStream& a = g_aux[dev];
-  if (!a.stream) {
-    if ((e = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming)) != hipSuccess) return e;
-  }
-  *out = &a;
-  return hipSuccess;
 }
 
 int fmt_of(int32_t d) {
@@ -643,19 +616,9 @@ vllm_status run_decode(vllm_tensor* out, const vllm_tensor* q, const vllm_tensor
   } else if (shared_pages == 0) {
     e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream);
   } else {
-    // Fork: the suffix decode goes first on the caller's stream, the prefix
-    // pass on the second stream fills the CUs as decode waves finish; the
-    // merge waits for both.
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    AuxStream* ax = nullptr;
-    e = aux_stream(&ax);
-    if (e == hipSuccess) e = hipEventRecord(ax->fork, stream);
-    if (e == hipSuccess) e = vp::launch_decode(p, (int)D, kv_fmt, q_fmt, stream, /*split=*/true);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ax->stream, ax->fork, 0);
-    if (e == hipSuccess) e = vp::launch_shared_prefix(sp, (int)D, kv_fmt, q_fmt, ax->stream);
-    if (e == hipSuccess) e = hipEventRecord(ax->join, ax->stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(stream, ax->join, 0);
-    if (e == hipSuccess) e = vp::launch_decode_merge(p, (int)D, q_fmt, stream);
+    // the prefix tiles and the decode of every sequence's own pages in one
+    // grid, then the merge, on the caller's stream
+    e = vp::launch_decode_shared(p, sp, (int)D, kv_fmt, q_fmt, stream);
   }
   if (owned) {
     hipError_t e2 = hipFreeAsync(ws, stream);

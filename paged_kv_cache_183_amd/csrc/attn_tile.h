@@ -1,0 +1,468 @@
+// Attention tiles on the matrix cores of gfx950, in two uses:
+//
+// Chunked prefill.  Sequence s has Q_s new query tokens at positions
+// n - Q_s .. n - 1 of its n cached tokens (their K/V are already in the
+// block-paged pool); the query row at position p attends to keys t <= p with
+// t > p - window (window 0: no lower bound).  This is the paged attention of
+// the vllm.cpp model forward (repository listing, "What's implemented") for a
+// chunk of several query tokens, with the sliding window of its
+// local-attention section.
+//
+// Shared prefix.  Every sequence of a decode batch maps its first P logical
+// pages to the same physical pages (a prefix hit binds a new sequence's block
+// table to existing pages, "Building and Deploying vllm.cpp", Step 3).  The
+// decode queries of all sequences (one row per sequence and query head) are
+// scored against those pages together, so each shared page is read once per
+// kv-head instead of once per sequence; the result is a (max, sum, output)
+// partial per row and split of the prefix, merged later with the rest of the
+// sequence by the log-sum-exp rule.
+//
+// The pages give no kernel design; this one is built for CDNA4.
+//
+// Work: a workgroup takes 128 query rows, 32 per wave, and one kv-head: in
+// prefill TQ = 128 / g consecutive tokens of one sequence times the g query
+// heads; for the shared prefix 128 consecutive (sequence, query head) rows
+// and one split of the prefix pages.  Every row has its own kept key range
+// [lo, hi); the workgroup walks the union of its rows' ranges in blocks of 32
+// keys (two 16-token pages), staged through LDS once for its four waves:
+//  * K block row-major ([key][D], rows padded by 16 bytes);
+//  * V block transposed ([D][key pair], rows padded to 18 dwords), so that
+//    the P.V operand of a lane is two 8-byte reads; the staging writes and
+//    these reads hit distinct banks.  FP8 pages (E4M3 or E5M2) are converted
+//    exactly to q's 16-bit format when staged.
+// Global loads run one block ahead of the matrix cores.
+// Per block and wave, on v_mfma_f32_32x32x16 (bf16 or f16, fp32 accumulate):
+//  * S^T = K Q^T: the output column of a lane is its query row, so each lane
+//    holds 16 scores of one row (keys 8j + 4h + i, h = lane / 32);
+//  * online softmax per row in fp32 (log2 domain), the two half-waves of a
+//    row combined with one lane exchange; the running max only moves when a
+//    score exceeds it by more than 2^8;
+//  * P is rounded to q's 16-bit format (the row sums, on v_dot2 against
+//    ones, use the rounded values) and used in place as the B operand of
+//    O^T += V^T P^T: the contraction over keys follows the same key order in
+//    both operands, so no transpose of P is needed and O^T keeps each query
+//    row in one lane as well.
+// Keys past every row's range (page tails, padding pages) are staged as zeros
+// and masked, and their block-table entries are never read.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace vp {
+namespace tile {
+
+constexpr int kPW = 4;                 // waves per workgroup
+constexpr int kRows = 32 * kPW;        // query rows per workgroup
+constexpr int kBK = 32;                // keys per block
+constexpr float kTauP = 8.0f;          // rescale headroom, log2 units
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int QF>
+__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
+  if constexpr (QF == kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+}
+
+template <int QF>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (QF == kBF16) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return bitcast<uint32_t>(v);
+  } else {
+    half2_t v = {(_Float16)lo, (_Float16)hi};
+    return bitcast<uint32_t>(v);
+  }
+}
+
+// a.lo * b.lo + a.hi * b.hi + c with fp32 accumulation.
+template <int QF>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (QF == kF16)
+    return __builtin_amdgcn_fdot2(bitcast<half2_t>(a), bitcast<half2_t>(b), c, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a), bitcast<bf16x2_t>(b), c, false);
+}
+
+// Max of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the halves).
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+  return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
+}
+
+// Raw pool data of one 8-element chunk: 16 bytes for 16-bit pools, 8 for FP8.
+template <int KF> struct Raw { using T = uint4; };
+template <> struct Raw<kE4M3> { using T = uint2; };
+template <> struct Raw<kE5M2> { using T = uint2; };
+
+// The chunk as 8 values of q's 16-bit format (FP8 codes converted exactly).
+template <int KF, int QF>
+__device__ __forceinline__ uint4 to_q16(const typename Raw<KF>::T& x) {
+  if constexpr (!is_fp8(KF)) {
+    return x;
+  } else {
+    return make_uint4(fp8x2_to_q16<KF, QF, false>(x.x), fp8x2_to_q16<KF, QF, true>(x.x),
+                      fp8x2_to_q16<KF, QF, false>(x.y), fp8x2_to_q16<KF, QF, true>(x.y));
+  }
+}
+
+// PFX = false: chunked prefill, normalized output rows.  PFX = true: shared
+// prefix, (max, sum, normalized output) partials per row and split.
+// b: the workgroup's index in the grid of tiles (the kernels pass blockIdx.x,
+// or its offset in a grid shared with the decode).
+template <int D, int QF, int KF, bool PFX>
+__device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int b) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  constexpr int CH = D / 8;                    // 8-element chunks per K/V row
+  constexpr int KS = D / 16;                   // k-steps of S^T = K Q^T (16 values of d each)
+  constexpr int KPT = CH / 8;                  // K chunks a thread stages per block (2 or 1)
+  constexpr int EB = is_fp8(KF) ? 1 : 2;       // bytes per pool element
+  constexpr int KROW = D * 2 + 16;             // bytes per LDS K row
+  constexpr int VROWW = kBK / 2 + 2;           // dwords per LDS V^T row (18)
+  constexpr int KBUF = kBK * KROW;             // bytes per K buffer
+  constexpr int VBUF = D * VROWW * 4;          // bytes per V^T buffer
+  constexpr int64_t kPageBytes = 16 * D * EB;
+  using RawT = typename Raw<KF>::T;
+  static_assert(kPW * 64 * KPT == 32 * CH, "staging map: K chunks of a block over the threads");
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][KBUF];
+  __shared__ __attribute__((aligned(16))) uint32_t s_v[2][VBUF / 4];
+  __shared__ int s_red[3];
+
+  const int g = p.group;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hf = lane >> 5;
+  const int row = wave * 32 + col;             // this lane's query row in the workgroup
+
+  // Workgroup -> (pair u, tile).  Workgroups go to the 8 XCDs round-robin;
+  // pair u runs on XCD u % 8 with all its tiles, which read the same K/V
+  // (they share it in that XCD's L2), and the XCDs get even work.  Later
+  // tiles attend to more keys (prefill) and are dispatched first.
+  //   prefill: u = (sequence, kv-head), tiles of TQ tokens;
+  //   shared prefix: u = (kv-head, split), tiles of 128 (sequence, head) rows.
+  const int ntiles = p.num_tiles;
+  const int npairs = PFX ? p.num_kv_heads * p.num_splits : p.num_seqs * p.num_kv_heads;
+  const int xcd = b % 8, kk = b / 8;
+  const int u = (kk / ntiles) * 8 + xcd;
+  if (u >= npairs) return;
+  const int tile = ntiles - 1 - (kk % ntiles);
+
+  int hk, seq_tbl;                             // kv-head, sequence whose table is read
+  int key_begin, key_end;                      // keys of this workgroup, before row ranges
+  int r_lo, r_hi;                              // this row's kept keys [r_lo, r_hi)
+  bool row_ok;
+  int64_t q_off;                               // element offset of this row in q (and out)
+  int split = 0;
+  if constexpr (!PFX) {
+    const int s = u / p.num_kv_heads;
+    hk = u - s * p.num_kv_heads;
+    seq_tbl = s;
+    const int tq = kRows / g;                  // query tokens per workgroup
+    // (clamped to the rows of q, so that no value of query_start_loc leads
+    // outside q / out)
+    const int q_begin = min(max(p.query_start_loc[s], 0), p.num_tokens);
+    const int Qs = min(max(p.query_start_loc[s + 1], q_begin), p.num_tokens) - q_begin;
+    const int q0 = tile * tq;
+    if (q0 >= Qs) return;
+    const int nt = min(tq, Qs - q0);           // tokens of this tile
+    const int n = min(p.context_lens[s], p.bt_stride * 16);
+    const int pos0 = n - Qs + q0;              // position of the tile's first token
+    row_ok = row < nt * g;
+    const int tok = min(row, nt * g - 1) / g;
+    const int head = min(row, nt * g - 1) - tok * g;
+    const int ppos = pos0 + tok;               // query position of the row
+    r_hi = ppos + 1;
+    r_lo = p.window > 0 ? max(0, ppos - p.window + 1) : 0;
+    key_begin = p.window > 0 ? max(0, pos0 - p.window + 1) : 0;
+    key_end = pos0 + nt;
+    q_off = ((int64_t)(q_begin + q0 + tok) * p.num_q_heads + hk * g + head) * D;
+  } else {
+    hk = u / p.num_splits;
+    split = u - hk * p.num_splits;
+    seq_tbl = 0;                               // the shared pages, as sequence 0 maps them
+    key_begin = split * p.split_pages * 16;
+    key_end = min(p.shared_pages, (split + 1) * p.split_pages) * 16;
+    const int rows_total = p.num_seqs * g;
+    if (tile * kRows >= rows_total) return;
+    const int rg = tile * kRows + row;
+    row_ok = rg < rows_total;
+    const int rgc = min(rg, rows_total - 1);
+    const int s = rgc / g;
+    const int head = rgc - s * g;
+    const int n = min(p.context_lens[s], p.bt_stride * 16);
+    const int lo = p.window > 0 ? max(0, n - p.window) : 0;
+    r_lo = max(lo, key_begin);
+    r_hi = min(n, key_end);
+    q_off = ((int64_t)s * p.num_q_heads + hk * g + head) * D;
+  }
+
+  // Q operand: lane (row, hf) holds d = D/2 hf + 8 t + i for k-step t.  The
+  // loads are in flight during the reduction below and waited for after it:
+  // once that wait has been seen, the block loop need not wait for them (the
+  // memory counter cannot tell them from the next block's loads, so an
+  // in-loop wait for Q would wait for those every block).
+  uint4 qr[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + q_off + (D / 2) * hf;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) qr[t] = *reinterpret_cast<const uint4*>(qp + 8 * t);
+  }
+
+  // Over the workgroup's rows: the largest lower and the smallest and largest
+  // upper bounds.  A block inside every row's range needs no per-key mask;
+  // keys at or past every row's range are staged as zeros.
+  if (threadIdx.x == 0) {
+    s_red[0] = INT32_MIN;
+    s_red[1] = INT32_MAX;
+    s_red[2] = INT32_MIN;
+  }
+  __syncthreads();
+  if (row_ok && hf == 0) {
+    atomicMax(&s_red[0], r_lo);
+    atomicMin(&s_red[1], r_hi);
+    atomicMax(&s_red[2], r_hi);
+  }
+  __syncthreads();
+  const int max_lo = __builtin_amdgcn_readfirstlane(s_red[0]);
+  const int min_hi = __builtin_amdgcn_readfirstlane(s_red[1]);
+  const int n_valid = min(key_end, __builtin_amdgcn_readfirstlane(s_red[2]));
+  const int kb0 = (key_begin / kBK) * kBK;
+  const int nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
+  __builtin_amdgcn_s_waitcnt(0);               // (the Q loads)
+
+
+  const int32_t* bt = p.block_tables + (int64_t)seq_tbl * p.bt_stride;
+  const uint8_t* kpool = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
+  const uint8_t* vpool = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes;
+  const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
+
+  // Staging maps (256 threads, one block = pages A and B of 16 rows):
+  //  K: thread i stages chunk i % CH of block row i / CH and, for D = 128,
+  //     of the same row of page B as well (block row + 16);
+  //  V: thread i loads rows 2 kp and 2 kp + 1 (kp = i % 16: key pair of the
+  //     block, page kp / 8) at chunk i / 16, and writes the 8 dwords
+  //     (V[2kp][d], V[2kp+1][d]) of V^T: 64 lanes hit 64 distinct banks
+  //     (D = 64: 16 x 8 items, the first 128 threads).
+  const int k_r = threadIdx.x / CH, k_c = threadIdx.x % CH;     // k_r: block row (D = 64) or page row
+  const int v_kp = threadIdx.x % 16, v_c = (threadIdx.x / 16) % CH;
+  const bool v_on = threadIdx.x < 16 * CH;
+  const int k_off = (k_r & 15) * (D * EB) + k_c * 8 * EB;
+  const bool k_pgB = k_r >= 16;                // (D = 64) the row is in page B
+  const int v_off = 2 * (v_kp & 7) * (D * EB) + v_c * 8 * EB;
+  const bool v_pgB = v_kp >= 8;
+  // Block ids: uniform over the workgroup, read through the constant address
+  // space (scalar loads, counted apart from the K/V loads) and clamped where
+  // they are used, so that no wait for them also waits for later K/V loads.
+  typedef const int32_t __attribute__((address_space(4)))* const_i32p;
+  const const_i32p bt_s = (const_i32p)bt;
+  auto page_blk = [&](int j) __attribute__((always_inline)) {
+    int blk = 0;
+    if (j * 16 < n_valid) blk = bt_s[j];
+    return blk;
+  };
+  auto clamp_blk = [&](int blk) __attribute__((always_inline)) {
+    return (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
+  };
+  // Loads are unconditional (rows at or past n_valid are replaced by zeros
+  // when written to LDS) so that nothing waits on them before the LDS write.
+  // (the two block ids of a block are read one block ahead of its K/V)
+  auto fetch = [&](RawT (&kr)[KPT], RawT (&vr)[2], int ida, int idb) __attribute__((always_inline)) {
+    const int64_t pa = (int64_t)__builtin_amdgcn_readfirstlane(clamp_blk(ida)) * blk_stride;
+    const int64_t pb = (int64_t)__builtin_amdgcn_readfirstlane(clamp_blk(idb)) * blk_stride;
+    if constexpr (KPT == 2) {
+      kr[0] = *reinterpret_cast<const RawT*>(kpool + pa + k_off);
+      kr[1] = *reinterpret_cast<const RawT*>(kpool + pb + k_off);
+    } else {
+      kr[0] = *reinterpret_cast<const RawT*>(kpool + (k_pgB ? pb : pa) + k_off);
+    }
+    const uint8_t* vp = vpool + (v_pgB ? pb : pa) + v_off;
+    vr[0] = *reinterpret_cast<const RawT*>(vp);
+    vr[1] = *reinterpret_cast<const RawT*>(vp + D * EB);
+  };
+  auto masked = [](uint4 x, bool keep) __attribute__((always_inline)) {
+    const uint32_t m = keep ? 0xFFFFFFFFu : 0u;    // value-level select (no pointer select)
+    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+  };
+  auto stage = [&](int buf, const RawT (&kr)[KPT], const RawT (&vr)[2], int kb)
+      __attribute__((always_inline)) {
+    const bool crossing = kb + kBK > n_valid;  // block crossing n_valid: zero the rows past it
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int r = k_r + 16 * j;              // block row
+      uint4 kx = to_q16<KF, QF>(kr[j]);
+      if (crossing) kx = masked(kx, kb + r < n_valid);
+      *reinterpret_cast<uint4*>(&s_k[buf][r * KROW + k_c * 16]) = kx;
+    }
+    if (!v_on) return;
+    uint4 va = to_q16<KF, QF>(vr[0]), vc = to_q16<KF, QF>(vr[1]);
+    if (crossing) {
+      va = masked(va, kb + 2 * v_kp < n_valid);
+      vc = masked(vc, kb + 2 * v_kp + 1 < n_valid);
+    }
+    const uint32_t a[4] = {va.x, va.y, va.z, va.w};
+    const uint32_t bb[4] = {vc.x, vc.y, vc.z, vc.w};
+    uint32_t* vt = &s_v[buf][(v_c * 8) * VROWW + v_kp];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vt[(2 * i) * VROWW] = __builtin_amdgcn_perm(bb[i], a[i], 0x05040100u);
+      vt[(2 * i + 1) * VROWW] = __builtin_amdgcn_perm(bb[i], a[i], 0x07060302u);
+    }
+  };
+
+  constexpr uint32_t kOnes = QF == kBF16 ? 0x3F803F80u : 0x3C003C00u;   // (1, 1)
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) o[m] = f32x16_t{};
+  float mrow = -INFINITY, lsum = 0.0f;
+  // scale * log2(e), times the K scale of this kv-head for FP8 pools
+  const float c = p.k_scales ? p.score_base * p.k_scales[hk] : p.score_scale;
+
+  // One block: S^T, online softmax, O^T update.  buf holds the block's K and
+  // V^T.  Lane reads: K rows col (16 bytes at d = D/2 hf + 8 t), V^T rows
+  // d = 32 m + col (8 bytes at key pairs 8 kap + 2 hf and + 4).
+  const uint8_t* k_rd = &s_k[0][col * KROW + D * hf];
+  const uint32_t* v_rd = &s_v[0][col * VROWW + 2 * hf];
+  auto block = [&](int buf, int kb) __attribute__((always_inline)) {
+    // ---- S^T = K Q^T ----
+    uint4 ka[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) ka[t] = *reinterpret_cast<const uint4*>(k_rd + buf * KBUF + 16 * t);
+    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) sacc = mfma32<QF>(ka[t], qr[t], sacc);
+
+    // ---- online softmax (row = col; this lane holds keys 8j + 4hf + i) ----
+    // Scores stay unscaled up to the exponent (scale > 0: max(c s) = c max(s)),
+    // which is then one fma per score: exp2(c s - m).
+    float sc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sc[k] = sacc[k];
+    const bool edge = kb < max_lo || kb + kBK > min_hi;
+    if (edge) {
+      asm volatile("");                        // keep this a branch (rarely taken)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = kb + 8 * j + 4 * hf + i;
+          if (t < r_lo || t >= r_hi) sc[4 * j + i] = -INFINITY;
+        }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) mx = fmaxf(mx, sc[k]);
+    mx = half_max(mx) * c;
+    const bool need = mx > mrow + kTauP;
+    if (__any(need)) {
+      const float mn = need ? fmaxf(mrow, mx) : mrow;
+      const float alpha = (mrow == -INFINITY) ? 0.0f : fast_exp2(mrow - mn);
+      mrow = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) o[m][k] *= alpha;
+    }
+    const float nmu = (mrow == -INFINITY) ? 0.0f : -mrow;
+    uint32_t pw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pw[k] = pack2<QF>(fast_exp2(fmaf(sc[2 * k], c, nmu)), fast_exp2(fmaf(sc[2 * k + 1], c, nmu)));
+      lsum = dot2<QF>(pw[k], kOnes, lsum);       // row sum of the rounded weights
+    }
+
+    // ---- O^T += V^T P^T ----
+    const uint32_t* vb = v_rd + buf * (VBUF / 4);
+#pragma unroll
+    for (int kap = 0; kap < 2; ++kap) {
+      const uint4 pb = make_uint4(pw[4 * kap], pw[4 * kap + 1], pw[4 * kap + 2], pw[4 * kap + 3]);
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        const uint32_t* vr = vb + 32 * m * VROWW + 8 * kap;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(vr);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 4);
+        o[m] = mfma32<QF>(make_uint4(a0.x, a0.y, a1.x, a1.y), pb, o[m]);
+      }
+    }
+  };
+
+  // The barriers order the LDS buffers only, so the K/V loads of the next
+  // block stay in flight across them.
+  auto lds_barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // Block bi + 1 is fetched into registers while block bi is computed, then
+  // written to the other LDS buffer.  (A single-block loop body keeps the
+  // accumulators in place; unrolling by two made the compiler copy them.)
+  RawT kr[KPT], vr[2];
+  auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
+  int ida = 0, idb = 0;                        // block ids of the block fetched next
+  if (nblk > 0) {
+    fetch(kr, vr, page_blk(kb_of(0) >> 4), page_blk((kb_of(0) >> 4) + 1));
+    ida = page_blk(kb_of(1) >> 4);
+    idb = page_blk((kb_of(1) >> 4) + 1);
+    stage(0, kr, vr, kb_of(0));
+  }
+  lds_barrier();
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int buf = bi & 1;
+    const int na = page_blk(kb_of(bi + 2) >> 4);
+    const int nb = page_blk((kb_of(bi + 2) >> 4) + 1);
+    fetch(kr, vr, ida, idb);                   // (past the end: re-reads the last block)
+    ida = na;
+    idb = nb;
+    __builtin_amdgcn_sched_barrier(0);
+    block(buf, kb0 + bi * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(buf ^ 1, kr, vr, kb_of(bi + 1));
+    lds_barrier();
+  }
+
+  // ---- finalize: row values at d = 32 m + 8 j + 4 hf + i ----
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (!row_ok) return;
+  if constexpr (!PFX) {
+    // FP8 pools: the V scale (per tensor or per kv-head) applies once here
+    const float w = inv * (p.v_scales ? p.v_scales[hk] : p.out_scale);
+    uint16_t* op = static_cast<uint16_t*>(p.out) + q_off + 4 * hf;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * j;
+        const uint32_t w0 = (uint32_t)f32_to_16<QF>(o[m][k] * w) |
+                            ((uint32_t)f32_to_16<QF>(o[m][k + 1] * w) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_16<QF>(o[m][k + 2] * w) |
+                            ((uint32_t)f32_to_16<QF>(o[m][k + 3] * w) << 16);
+        *reinterpret_cast<uint2*>(op + 32 * m + 8 * j) = make_uint2(w0, w1);
+      }
+  } else {
+    // partial rows [split][sequence][query head]; an empty row stores
+    // (-inf, 0, 0), which the merge weighs 0
+    const int64_t pr = (int64_t)split * p.num_seqs * p.num_q_heads + q_off / D;
+    float* op = p.pfx_o + pr * D + 4 * hf;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * j;
+        *reinterpret_cast<float4*>(op + 32 * m + 8 * j) =
+            make_float4(o[m][k] * inv, o[m][k + 1] * inv, o[m][k + 2] * inv, o[m][k + 3] * inv);
+      }
+    if (hf == 0) {
+      p.pfx_m[pr] = lt > 0.0f ? mrow : -INFINITY;
+      p.pfx_l[pr] = lt;
+    }
+  }
+}
+
+}  // namespace tile
+}  // namespace vp

@@ -55,6 +55,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -277,8 +278,10 @@ __device__ __forceinline__ Words<NW> ld_words(const uint8_t* ptr) {
   return r;
 }
 
+// bid, nbid: this workgroup's index among the decode workgroups and their
+// number (the whole grid, or its part after the shared-prefix tiles).
 template <int D, int KF, int QF, int PP, bool AP>
-__global__ __launch_bounds__(kNW * 64) void decode_mma_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_body(const DecodeParams& p, const int bid, const int nbid) {
   using S = MmaShape<D, KF>;
   constexpr int EB = S::EB, RB = S::RB, STEPS = S::STEPS, NL = S::NL, TILES = S::TILES, VW = S::VW;
   constexpr int64_t kPageBytes = 16 * RB;
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mma_kernel(DecodeParams p) {
                                       : max((int64_t)1, (T + p.num_workers - 1) / p.num_workers);
   const int64_t num_chunks = (T + C - 1) / C;
 
-  for (int sq = blockIdx.x; sq < B; sq += gridDim.x) {
+  for (int sq = bid; sq < B; sq += nbid) {
     if (pre[sq + 1] == pre[sq]) {
       if (p.skip_tokens == 0) {
         uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)sq * p.num_q_heads * D;
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mma_kernel(DecodeParams p) {
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
   constexpr uint32_t kOnes = QF == kBF16 ? 0x3F803F80u : 0x3C003C00u;   // (1, 1)
 
-  for (int64_t chunk = (int64_t)blockIdx.x * kNW + wave; chunk < num_chunks;
+  for (int64_t chunk = (int64_t)bid * kNW + wave; chunk < num_chunks;
        chunk += p.num_workers) {
     int64_t g = chunk * C;
     const int64_t g_end = min(g + C, T);
@@ -612,43 +615,110 @@ __global__ __launch_bounds__(kNW * 64) void decode_mma_kernel(DecodeParams p) {
   }
 }
 
+template <int D, int KF, int QF, int PP, bool AP>
+__global__ __launch_bounds__(kNW * 64) void decode_mma_kernel(DecodeParams p) {
+  decode_body<D, KF, QF, PP, AP>(p, blockIdx.x, gridDim.x);
+}
+
+// Decode with a shared prefix, in one grid: the decode of the sequences' own
+// pages first, then the npfx shared-prefix tiles, which fill the slot each CU
+// has left beside its two decode workgroups (dispatched in this order, the
+// decode waves have the memory system first: tiles first made the call
+// about 7% slower).  Both write partials that the merge kernel, launched next
+// on the same stream, combines.
+static_assert(kNW == tile::kPW, "decode and tile workgroups have the same size");
+template <int D, int KF, int QF, int PP>
+__global__ __launch_bounds__(kNW * 64) void decode_shared_kernel(DecodeParams p, PrefillParams sp,
+                                                                 int npfx) {
+  const int ndec = (int)gridDim.x - npfx;
+  if ((int)blockIdx.x < ndec)
+    decode_body<D, KF, QF, PP, false>(p, blockIdx.x, ndec);
+  else
+    tile::attn_tile_body<D, QF, KF, true>(sp, blockIdx.x - ndec);
+}
+
 // Log-sum-exp merge of the pieces of units cut by chunk boundaries (and, with
 // a shared prefix, of every unit with its prefix splits).  One workgroup per
 // unit, one thread per 4 consecutive outputs of its G x D block; the unit's
 // record (first slot, piece count) comes from the decode kernel.  Pieces are
-// read in rounds of kMergeBatch (units of more pieces: twice that) straight
-// into registers, every load of a round independent (padding pieces past the
-// count re-read the last piece and get weight 0), so a round costs one
-// memory latency:
+// read in rounds of kMergeBatch (units of more decode pieces: twice that)
+// straight into registers, every load of a round independent (padding pieces
+// past the count re-read the last piece and get weight 0), so a round costs
+// one memory latency; the prefix splits, whose rows need nothing from the
+// record, go first, so their loads overlap the record's:
 // M = max m, w = l 2^(m - M), out = sum w o / sum w.
 constexpr int kMergeBatch = 8;
 
 template <int D, int G, int QF>
 __global__ __launch_bounds__(G * D / 4) void decode_merge_kernel(DecodeParams p) {
+  const int64_t u = blockIdx.x;
+  const int ns = p.num_splits;
   const int ngc = p.group / G;
   const int NY = p.num_kv_heads * ngc;
-  const int64_t u = blockIdx.x;
-  const int nsuf = p.ws_unit[u * 2 + 1];
-  const int npieces = nsuf + p.num_splits;
-  if (npieces == 0) return;                   // finished inside one chunk, or empty
-  const int64_t sl0 = p.ws_unit[u * 2];
   const int s = (int)(u / NY);
   const int y = (int)(u - (int64_t)s * NY);
   const int hk = y / ngc;
   const int h0 = hk * p.group + (y - hk * ngc) * G;
   const int64_t prow = (int64_t)s * p.num_q_heads + h0;    // row of head h0 in the prefix partials
-  const int64_t fk = sl0 >> 1;
   const int64_t split_rows = (int64_t)p.num_seqs * p.num_q_heads;
   const int e = threadIdx.x * 4;
   const int h = e / D;
-  // Piece k < nsuf: a piece of the decode (the first sits in the slot its
-  // wave recorded, or in the unit's own slot when that is -1; the later ones
-  // open the following chunks, slot 0 of each); piece nsuf + i: split i of
-  // the shared-prefix partials.  Gives the row of head 0 of the unit in the
-  // piece's (o, m, l) arrays.
-  auto ml_row = [&](int k, const float*& op, const float*& mp, const float*& lp)
+  float M = -INFINITY, den = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // One round: NB pieces (rows given by row_of(k), k < n; padding re-reads
+  // piece n - 1 with weight 0), all loads independent.
+  auto round = [&](auto nb, int k0, int n, auto row_of) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb)::value;
+    float mk[NB], lk[NB];
+    float4 ok[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const float *op, *mp, *lp;
+      const int64_t r = row_of(min(k0 + k, n - 1), op, mp, lp) + h;
+      mk[k] = mp[r];
+      lk[k] = lp[r];
+      ok[k] = *reinterpret_cast<const float4*>(op + r * D + (e - h * D));
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      if (k0 + k < n) Mn = fmaxf(Mn, mk[k]);
+    const float a = (M == -INFINITY) ? 0.0f : fast_exp2(M - Mn);
+    den *= a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] *= a;
+    M = Mn;
+    const float Mu = (M == -INFINITY) ? 0.0f : M;   // (every piece so far empty)
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const float w = (k0 + k < n) ? lk[k] * fast_exp2(mk[k] - Mu) : 0.0f;  // 0: padding, empty
+      den += w;
+      acc[0] = fmaf(w, ok[k].x, acc[0]);
+      acc[1] = fmaf(w, ok[k].y, acc[1]);
+      acc[2] = fmaf(w, ok[k].z, acc[2]);
+      acc[3] = fmaf(w, ok[k].w, acc[3]);
+    }
+  };
+  // The shared-prefix splits first: their rows need nothing from the decode
+  // kernel's record of the unit, so their loads overlap the record's.
+  auto split_row = [&](int k, const float*& op, const float*& mp, const float*& lp)
       __attribute__((always_inline)) {
-    if (k < nsuf) {
+    op = p.pfx_o;
+    mp = p.pfx_m;
+    lp = p.pfx_l;
+    return (int64_t)k * split_rows + prow;
+  };
+  for (int k0 = 0; k0 < ns; k0 += kMergeBatch) round(std::integral_constant<int, kMergeBatch>{}, k0, ns, split_row);
+  const int nsuf = p.ws_unit[u * 2 + 1];
+  if (nsuf == 0 && ns == 0) return;           // finished inside one chunk, or empty
+  if (nsuf > 0) {
+    const int64_t sl0 = p.ws_unit[u * 2];
+    const int64_t fk = sl0 >> 1;
+    // piece k of the decode: the first in the slot its wave recorded (or the
+    // unit's own slot when that is -1), the later ones open the following
+    // chunks, slot 0 of each
+    auto piece_row = [&](int k, const float*& op, const float*& mp, const float*& lp)
+        __attribute__((always_inline)) {
       if (sl0 < 0) {
         op = p.ws_uo;
         mp = p.ws_um;
@@ -659,51 +729,13 @@ __global__ __launch_bounds__(G * D / 4) void decode_merge_kernel(DecodeParams p)
       mp = p.ws_m;
       lp = p.ws_l;
       return (k == 0 ? sl0 : (fk + k) * 2) * G;
-    }
-    op = p.pfx_o;
-    mp = p.pfx_m;
-    lp = p.pfx_l;
-    return (int64_t)(k - nsuf) * split_rows + prow;
-  };
-  float M = -INFINITY, den = 0.0f;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto rounds = [&](auto nb) __attribute__((always_inline)) {
-    constexpr int NB = decltype(nb)::value;
-    for (int k0 = 0; k0 < npieces; k0 += NB) {
-      float mk[NB], lk[NB];
-      float4 ok[NB];
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const float *op, *mp, *lp;
-        const int64_t r = ml_row(min(k0 + k, npieces - 1), op, mp, lp) + h;
-        mk[k] = mp[r];
-        lk[k] = lp[r];
-        ok[k] = *reinterpret_cast<const float4*>(op + r * D + (e - h * D));
-      }
-      float Mn = M;
-#pragma unroll
-      for (int k = 0; k < NB; ++k)
-        if (k0 + k < npieces) Mn = fmaxf(Mn, mk[k]);
-      const float a = (M == -INFINITY) ? 0.0f : fast_exp2(M - Mn);
-      den *= a;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] *= a;
-      M = Mn;
-      const float Mu = (M == -INFINITY) ? 0.0f : M;   // (every piece so far empty)
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const float w = (k0 + k < npieces) ? lk[k] * fast_exp2(mk[k] - Mu) : 0.0f;  // 0: padding, empty
-        den += w;
-        acc[0] = fmaf(w, ok[k].x, acc[0]);
-        acc[1] = fmaf(w, ok[k].y, acc[1]);
-        acc[2] = fmaf(w, ok[k].z, acc[2]);
-        acc[3] = fmaf(w, ok[k].w, acc[3]);
-      }
-    }
-  };
-  // (npieces is uniform over the workgroup)
-  if (npieces <= kMergeBatch) rounds(std::integral_constant<int, kMergeBatch>{});
-  else rounds(std::integral_constant<int, 2 * kMergeBatch>{});
+    };
+    // (nsuf is uniform over the workgroup)
+    if (nsuf <= kMergeBatch) round(std::integral_constant<int, kMergeBatch>{}, 0, nsuf, piece_row);
+    else
+      for (int k0 = 0; k0 < nsuf; k0 += 2 * kMergeBatch)
+        round(std::integral_constant<int, 2 * kMergeBatch>{}, k0, nsuf, piece_row);
+  }
   const float oscale = p.v_scales ? p.v_scales[hk] : p.out_scale;
   const float f = den > 0.0f ? oscale / den : 0.0f;
   uint16_t* out = static_cast<uint16_t*>(p.out) + prow * D + e;
@@ -741,6 +773,20 @@ static const void* decode_mma_kernel_for(int D, int kv_fmt, int q_fmt, bool ap) 
 
 static const void* decode_kernel_for(int D, int kv_fmt, int q_fmt, bool ap) {
   return decode_mma_kernel_for(D, kv_fmt, q_fmt, ap);
+}
+
+static const void* decode_shared_kernel_for(int D, int kv_fmt, int q_fmt) {
+#define VP_SHARED(DD, KK, QQ)                                                         \
+  if (kv_fmt == KK && q_fmt == QQ)                                                    \
+    return reinterpret_cast<const void*>(&decode_shared_kernel<DD, KK, QQ, is_fp8(KK) ? 2 : 1>);
+#define VP_SHARED_D(DD)                                                               \
+  VP_SHARED(DD, kF16, kF16) VP_SHARED(DD, kBF16, kBF16) VP_SHARED(DD, kE4M3, kF16)     \
+  VP_SHARED(DD, kE4M3, kBF16) VP_SHARED(DD, kE5M2, kF16) VP_SHARED(DD, kE5M2, kBF16)
+  if (D == 128) { VP_SHARED_D(128) }
+  if (D == 64) { VP_SHARED_D(64) }
+#undef VP_SHARED_D
+#undef VP_SHARED
+  return nullptr;
 }
 
 template <int D, int QF>
@@ -815,8 +861,7 @@ int decode_workers(int64_t pages_bound, int head_dim, int kv_fmt, int q_fmt, int
   return (int)min(decode_workers_bound(pages_bound), (w + kNW - 1) / kNW * kNW);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream,
-                         bool split) {
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
   const void* k = decode_kernel_for(head_dim, kv_fmt, q_fmt, p.new_slots != nullptr);
   const void* mk = merge_kernel_for(head_dim, q_fmt, p.head_chunk);
@@ -829,7 +874,34 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_
     if (e != hipSuccess) return e;
   }
   hipError_t e = hipLaunchKernel(k, dim3(p.num_workers / kNW), dim3(kNW * 64), args, 0, stream);
-  if (e != hipSuccess || split) return e;
+  if (e != hipSuccess) return e;
+  return launch_decode_merge(p, head_dim, q_fmt, stream);
+}
+
+hipError_t launch_decode_shared(const DecodeParams& p, const PrefillParams& sp, int head_dim,
+                                int kv_fmt, int q_fmt, hipStream_t stream) {
+  if (p.num_seqs == 0) return hipSuccess;
+  const void* k = decode_shared_kernel_for(head_dim, kv_fmt, q_fmt);
+  if (!k || sp.num_splits < 1) return hipErrorInvalidValue;
+  DecodeParams a = p;
+  PrefillParams x = sp;
+  // the tile grid of the prefix pass: (kv-head, split) pairs over the 8 XCDs,
+  // times the tiles of 128 (sequence, query head) rows
+  x.num_tiles = (int)(((int64_t)sp.num_seqs * sp.group + tile::kRows - 1) / tile::kRows);
+  const int64_t pairs = (int64_t)sp.num_kv_heads * sp.num_splits;
+  const int64_t npfx = (pairs + 7) / 8 * 8 * x.num_tiles;
+  const int64_t grid = npfx + p.num_workers / kNW;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  int n = (int)npfx;
+  if (p.num_seqs > kScanMax) {
+    void* pargs[] = {&a};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_prefix_kernel), dim3(1),
+                                   dim3(kNW * 64), pargs, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  void* args[] = {&a, &x, &n};
+  hipError_t e = hipLaunchKernel(k, dim3((unsigned)grid), dim3(kNW * 64), args, 0, stream);
+  if (e != hipSuccess) return e;
   return launch_decode_merge(p, head_dim, q_fmt, stream);
 }
 

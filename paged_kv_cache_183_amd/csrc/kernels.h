@@ -86,11 +86,9 @@ struct DecodeParams {
 };
 
 // kv_fmt: kF16 / kBF16 / kE4M3 / kE5M2; q_fmt: kF16 / kBF16.  Launches the
-// decode kernel, then the merge; with split = true only the decode kernel
-// (launch_decode_merge then follows, once the partials it also reads --
-// from work on another stream -- are ordered before it).
+// decode kernel, then the merge.
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int kv_fmt, int q_fmt,
-                         hipStream_t stream, bool split = false);
+                         hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int q_fmt, hipStream_t stream);
 
 struct PrefillParams {
@@ -116,7 +114,7 @@ struct PrefillParams {
   const float* k_scales;       // FP8 pools: [Hkv] per-head K scales (null: folded in score_scale)
   float out_scale;             // chunked prefill: V scale of FP8 pools, else 1
   const float* v_scales;       // chunked prefill, FP8 pools: [Hkv] per-head V scales (or null)
-  // shared-prefix partials (launch_shared_prefix only): the first
+  // shared-prefix partials (launch_decode_shared only): the first
   // shared_pages pages of every sequence, in splits of split_pages pages
   int32_t shared_pages;
   int32_t split_pages;
@@ -130,10 +128,17 @@ struct PrefillParams {
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
                           hipStream_t stream);
 // Shared-prefix partials: kv_fmt = q_fmt, kE4M3 or kE5M2.
-hipError_t launch_shared_prefix(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
-                                hipStream_t stream);
-// Pages per split of the shared-prefix pass.
-constexpr int kPrefixSplitPages = 32;
+// Shared-prefix decode: the prefix tiles (p.shared_pages, split_pages,
+// num_splits and the partial arrays of sp) and the decode of every
+// sequence's own pages (p.skip_tokens = 16 shared_pages) in one grid, then
+// the merge, all on one stream.
+hipError_t launch_decode_shared(const DecodeParams& p, const PrefillParams& sp, int head_dim,
+                                int kv_fmt, int q_fmt, hipStream_t stream);
+// Pages per split of the shared-prefix pass.  (A 4096-token prefix in 4
+// splits: 8 splits of 32 pages made the prefix-shared FP8 decode 3% slower
+// through the merge's reads of the partials, 2 splits 19% slower through the
+// tiles' longer walk.)
+constexpr int kPrefixSplitPages = 64;
 
 struct LocalPlanParams {
   const int32_t* query_start_loc;  // [B + 1]

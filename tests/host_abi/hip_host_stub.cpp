@@ -93,18 +93,6 @@ hipError_t hipFreeAsync(void* p, hipStream_t) {
   std::free(p);
   return hipSuccess;
 }
-hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
-  static int dummy;
-  *s = reinterpret_cast<hipStream_t>(&dummy);
-  return hipSuccess;
-}
-hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
-  static int dummy;
-  *e = reinterpret_cast<hipEvent_t>(&dummy);
-  return hipSuccess;
-}
-hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
-hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned int) { return hipSuccess; }
 // The library's scratch array is a host array of this size in this build.
 hipError_t hipGetSymbolAddress(void** p, const void* sym) {
   *p = const_cast<void*>(sym);
@@ -138,9 +126,8 @@ hipError_t launch_cache_write(const CacheWriteParams& p, int src_fmt, int dst_fm
   return hipSuccess;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int D, int kv_fmt, int q_fmt, hipStream_t s,
-                         bool split) {
-  ++stub_launches;
+// The bytes the decode kernel reads and writes.
+static void decode_touch(const DecodeParams& p, int D, int kv_fmt, int q_fmt) {
   const int64_t B = p.num_seqs, G = p.head_chunk;
   const int64_t units = B * p.num_kv_heads * (p.group / G);
   check(p.group % G == 0 && G >= 1 && G <= 8, "decode head chunk");
@@ -176,7 +163,12 @@ hipError_t launch_decode(const DecodeParams& p, int D, int kv_fmt, int q_fmt, hi
     touch_r(p.new_slots, B * 8, "decode new_slots");
     check(p.num_slots == (int64_t)p.num_blocks * 16, "decode num_slots");
   }
-  return split ? hipSuccess : launch_decode_merge(p, D, q_fmt, s);
+}
+
+hipError_t launch_decode(const DecodeParams& p, int D, int kv_fmt, int q_fmt, hipStream_t s) {
+  ++stub_launches;
+  decode_touch(p, D, kv_fmt, q_fmt);
+  return launch_decode_merge(p, D, q_fmt, s);
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, int D, int q_fmt, hipStream_t) {
@@ -211,8 +203,12 @@ hipError_t launch_prefill(const PrefillParams& p, int D, int kv_fmt, int q_fmt, 
   return hipSuccess;
 }
 
-hipError_t launch_shared_prefix(const PrefillParams& p, int D, int kv_fmt, int q_fmt, hipStream_t) {
+hipError_t launch_decode_shared(const DecodeParams& dp, const PrefillParams& p, int D, int kv_fmt,
+                                int q_fmt, hipStream_t s) {
   ++stub_launches;
+  decode_touch(dp, D, kv_fmt, q_fmt);
+  check(dp.skip_tokens == 16 * p.shared_pages && dp.num_splits == p.num_splits,
+        "shared prefix: decode and prefix parts agree");
   // prefix mode: q holds one row per sequence
   PrefillParams c = p;
   c.num_tokens = p.num_seqs;
@@ -222,7 +218,7 @@ hipError_t launch_shared_prefix(const PrefillParams& p, int D, int kv_fmt, int q
   touch_w(p.pfx_o, rows * D * 4, "shared prefix pfx_o");
   touch_w(p.pfx_m, rows * 4, "shared prefix pfx_m");
   touch_w(p.pfx_l, rows * 4, "shared prefix pfx_l");
-  return hipSuccess;
+  return launch_decode_merge(dp, D, q_fmt, s);
 }
 
 hipError_t launch_chunked_local_plan(const LocalPlanParams& p, hipStream_t) {
