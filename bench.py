@@ -259,7 +259,7 @@ def bench_prefill(case, steps: int, warmup: int, chunk: int = 0) -> dict:
             "wall_ms_per_call": round(wall * 1e3, 5),
             "tflops": round(tf, 2), "tokens_per_s": round(w["tokens"] / (mean * 1e-3), 1),
             "flops_per_call": w["flops"], "kept_pairs": w["pairs"], "bytes_per_call": w["bytes"],
-            "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 2),
+            "roofline": {"bound": "mfma", "kernel": "attn_tile_kernel", "achieved": round(tf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": None if chunk else
