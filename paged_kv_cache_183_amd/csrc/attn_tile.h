@@ -26,10 +26,12 @@
 // [lo, hi); the workgroup walks the union of its rows' ranges in blocks of 32
 // keys (two 16-token pages), staged through LDS once for its four waves:
 //  * K block row-major ([key][D], rows padded by 16 bytes);
-//  * V block transposed ([D][key pair], rows padded to 18 dwords), so that
-//    the P.V operand of a lane is two 8-byte reads; the staging writes and
-//    these reads hit distinct banks.  FP8 pages (E4M3 or E5M2) are converted
-//    exactly to q's 16-bit format when staged.
+//  * V block row-major as well (rows padded by 32 bytes), staged exactly like
+//    K; the P.V operand of a lane is two transposing 8-byte reads
+//    (ds_read_b64_tr_b16), each giving 4 consecutive keys at the lane's own d.
+//    The padding puts the four rows one read touches in distinct banks.
+//  FP8 pages (E4M3 or E5M2) are converted exactly to q's 16-bit format when
+//  staged.
 // Global loads run one block ahead of the matrix cores.
 // Per block and wave, on v_mfma_f32_32x32x16 (bf16 or f16, fp32 accumulate):
 //  * S^T = K Q^T: the output column of a lane is its query row, so each lane
@@ -123,14 +125,14 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   constexpr int KPT = CH / 8;                  // K chunks a thread stages per block (2 or 1)
   constexpr int EB = is_fp8(KF) ? 1 : 2;       // bytes per pool element
   constexpr int KROW = D * 2 + 16;             // bytes per LDS K row
-  constexpr int VROWW = kBK / 2 + 2;           // dwords per LDS V^T row (18)
+  constexpr int VROW = D * 2 + 32;             // bytes per LDS V row (bank offset 8 per row)
   constexpr int KBUF = kBK * KROW;             // bytes per K buffer
-  constexpr int VBUF = D * VROWW * 4;          // bytes per V^T buffer
+  constexpr int VBUF = kBK * VROW;             // bytes per V buffer
   constexpr int64_t kPageBytes = 16 * D * EB;
   using RawT = typename Raw<KF>::T;
   static_assert(kPW * 64 * KPT == 32 * CH, "staging map: K chunks of a block over the threads");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][KBUF];
-  __shared__ __attribute__((aligned(16))) uint32_t s_v[2][VBUF / 4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][VBUF];
   __shared__ int s_red[3];
 
   const int g = p.group;
@@ -241,20 +243,13 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   const uint8_t* vpool = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes;
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
 
-  // Staging maps (256 threads, one block = pages A and B of 16 rows):
-  //  K: thread i stages chunk i % CH of block row i / CH and, for D = 128,
-  //     of the same row of page B as well (block row + 16);
-  //  V: thread i loads rows 2 kp and 2 kp + 1 (kp = i % 16: key pair of the
-  //     block, page kp / 8) at chunk i / 16, and writes the 8 dwords
-  //     (V[2kp][d], V[2kp+1][d]) of V^T: 64 lanes hit 64 distinct banks
-  //     (D = 64: 16 x 8 items, the first 128 threads).
+  // Staging map (256 threads, one block = pages A and B of 16 rows), the same
+  // for K and V: thread i stages chunk i % CH of block row i / CH and, for
+  // D = 128, of the same row of page B as well (block row + 16); for D = 64
+  // the waves 2 and 3 take page B.
   const int k_r = threadIdx.x / CH, k_c = threadIdx.x % CH;     // k_r: block row (D = 64) or page row
-  const int v_kp = threadIdx.x % 16, v_c = (threadIdx.x / 16) % CH;
-  const bool v_on = threadIdx.x < 16 * CH;
-  const int k_off = (k_r & 15) * (D * EB) + k_c * 8 * EB;
-  const bool k_pgB = k_r >= 16;                // (D = 64) the row is in page B
-  const int v_off = 2 * (v_kp & 7) * (D * EB) + v_c * 8 * EB;
-  const bool v_pgB = v_kp >= 8;
+  const uint32_t k_off = (uint32_t)((k_r & 15) * (D * EB) + k_c * 8 * EB);
+  const bool k_pgB = wave >= 2;                // (D = 64) rows 16..31: page B, uniform per wave
   // Block ids: uniform over the workgroup, read through the constant address
   // space (scalar loads, counted apart from the K/V loads) and clamped where
   // they are used, so that no wait for them also waits for later K/V loads.
@@ -271,46 +266,43 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // Loads are unconditional (rows at or past n_valid are replaced by zeros
   // when written to LDS) so that nothing waits on them before the LDS write.
   // (the two block ids of a block are read one block ahead of its K/V)
-  auto fetch = [&](RawT (&kr)[KPT], RawT (&vr)[2], int ida, int idb) __attribute__((always_inline)) {
+  // K and V rows take the same map: the page bases are uniform, the lane
+  // offset is k_off.
+  auto fetch = [&](RawT (&kr)[KPT], RawT (&vr)[KPT], int ida, int idb) __attribute__((always_inline)) {
     const int64_t pa = (int64_t)__builtin_amdgcn_readfirstlane(clamp_blk(ida)) * blk_stride;
     const int64_t pb = (int64_t)__builtin_amdgcn_readfirstlane(clamp_blk(idb)) * blk_stride;
     if constexpr (KPT == 2) {
-      kr[0] = *reinterpret_cast<const RawT*>(kpool + pa + k_off);
-      kr[1] = *reinterpret_cast<const RawT*>(kpool + pb + k_off);
+      const uint8_t* ka = kpool + pa;
+      const uint8_t* kb = kpool + pb;
+      const uint8_t* va = vpool + pa;
+      const uint8_t* vb = vpool + pb;
+      kr[0] = *reinterpret_cast<const RawT*>(ka + k_off);
+      kr[1] = *reinterpret_cast<const RawT*>(kb + k_off);
+      vr[0] = *reinterpret_cast<const RawT*>(va + k_off);
+      vr[1] = *reinterpret_cast<const RawT*>(vb + k_off);
     } else {
-      kr[0] = *reinterpret_cast<const RawT*>(kpool + (k_pgB ? pb : pa) + k_off);
+      const int64_t pg = k_pgB ? pb : pa;
+      kr[0] = *reinterpret_cast<const RawT*>(kpool + pg + k_off);
+      vr[0] = *reinterpret_cast<const RawT*>(vpool + pg + k_off);
     }
-    const uint8_t* vp = vpool + (v_pgB ? pb : pa) + v_off;
-    vr[0] = *reinterpret_cast<const RawT*>(vp);
-    vr[1] = *reinterpret_cast<const RawT*>(vp + D * EB);
   };
   auto masked = [](uint4 x, bool keep) __attribute__((always_inline)) {
     const uint32_t m = keep ? 0xFFFFFFFFu : 0u;    // value-level select (no pointer select)
     return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
   };
-  auto stage = [&](int buf, const RawT (&kr)[KPT], const RawT (&vr)[2], int kb)
+  auto stage = [&](int buf, const RawT (&kr)[KPT], const RawT (&vr)[KPT], int kb)
       __attribute__((always_inline)) {
     const bool crossing = kb + kBK > n_valid;  // block crossing n_valid: zero the rows past it
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int r = k_r + 16 * j;              // block row
-      uint4 kx = to_q16<KF, QF>(kr[j]);
-      if (crossing) kx = masked(kx, kb + r < n_valid);
+      uint4 kx = to_q16<KF, QF>(kr[j]), vx = to_q16<KF, QF>(vr[j]);
+      if (crossing) {
+        kx = masked(kx, kb + r < n_valid);
+        vx = masked(vx, kb + r < n_valid);
+      }
       *reinterpret_cast<uint4*>(&s_k[buf][r * KROW + k_c * 16]) = kx;
-    }
-    if (!v_on) return;
-    uint4 va = to_q16<KF, QF>(vr[0]), vc = to_q16<KF, QF>(vr[1]);
-    if (crossing) {
-      va = masked(va, kb + 2 * v_kp < n_valid);
-      vc = masked(vc, kb + 2 * v_kp + 1 < n_valid);
-    }
-    const uint32_t a[4] = {va.x, va.y, va.z, va.w};
-    const uint32_t bb[4] = {vc.x, vc.y, vc.z, vc.w};
-    uint32_t* vt = &s_v[buf][(v_c * 8) * VROWW + v_kp];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vt[(2 * i) * VROWW] = __builtin_amdgcn_perm(bb[i], a[i], 0x05040100u);
-      vt[(2 * i + 1) * VROWW] = __builtin_amdgcn_perm(bb[i], a[i], 0x07060302u);
+      *reinterpret_cast<uint4*>(&s_v[buf][r * VROW + k_c * 16]) = vx;
     }
   };
 
@@ -326,7 +318,12 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // V^T.  Lane reads: K rows col (16 bytes at d = D/2 hf + 8 t), V^T rows
   // d = 32 m + col (8 bytes at key pairs 8 kap + 2 hf and + 4).
   const uint8_t* k_rd = &s_k[0][col * KROW + D * hf];
-  const uint32_t* v_rd = &s_v[0][col * VROWW + 2 * hf];
+  // V operand of O^T += V^T P^T by transposing LDS reads: in each 16-lane
+  // group (d = 16 (g % 2) + i, key half kh = g / 2) lane i addresses row
+  // 4 kh + i / 4, columns 16 (g % 2) + 4 (i % 4) .. + 3, and receives the
+  // 4 keys of that half at its own d.
+  const int vg = lane >> 4, vi = lane & 15;
+  const uint8_t* v_rd = &s_v[0][(4 * (vg >> 1) + (vi >> 2)) * VROW + (16 * (vg & 1) + 4 * (vi & 3)) * 2];
   auto block = [&](int buf, int kb) __attribute__((always_inline)) {
     // ---- S^T = K Q^T ----
     uint4 ka[KS];
@@ -377,16 +374,20 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     }
 
     // ---- O^T += V^T P^T ----
-    const uint32_t* vb = v_rd + buf * (VBUF / 4);
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    typedef v4i16_t __attribute__((address_space(3)))* lds_v4p;
+    const uint8_t* vb = v_rd + buf * VBUF;
 #pragma unroll
     for (int kap = 0; kap < 2; ++kap) {
       const uint4 pb = make_uint4(pw[4 * kap], pw[4 * kap + 1], pw[4 * kap + 2], pw[4 * kap + 3]);
 #pragma unroll
       for (int m = 0; m < D / 32; ++m) {
-        const uint32_t* vr = vb + 32 * m * VROWW + 8 * kap;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(vr);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 4);
-        o[m] = mfma32<QF>(make_uint4(a0.x, a0.y, a1.x, a1.y), pb, o[m]);
+        // keys 16 kap + 4 kh .. + 3 and 16 kap + 8 + 4 kh .. + 3 at d = 32 m + col
+        const uint8_t* vr = vb + 16 * kap * VROW + 64 * m;
+        const v4i16_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(vr));
+        const v4i16_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(vr + 8 * VROW));
+        const uint2 u0 = bitcast<uint2>(a0), u1 = bitcast<uint2>(a1);
+        o[m] = mfma32<QF>(make_uint4(u0.x, u0.y, u1.x, u1.y), pb, o[m]);
       }
     }
   };
@@ -401,7 +402,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // Block bi + 1 is fetched into registers while block bi is computed, then
   // written to the other LDS buffer.  (A single-block loop body keeps the
   // accumulators in place; unrolling by two made the compiler copy them.)
-  RawT kr[KPT], vr[2];
+  RawT kr[KPT], vr[KPT];
   auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
   int ida = 0, idb = 0;                        // block ids of the block fetched next
   if (nblk > 0) {
