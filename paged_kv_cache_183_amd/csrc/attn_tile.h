@@ -58,6 +58,9 @@ constexpr int kPW = 4;                 // waves per workgroup
 constexpr int kRows = 32 * kPW;        // query rows per workgroup
 constexpr int kBK = 32;                // keys per block
 constexpr float kTauP = 8.0f;          // rescale headroom, log2 units
+// Word 3 of a raw buffer resource on gfx9-family GPUs: 32-bit data format,
+// no swizzle, no thread-id offset.
+constexpr int kBufferFlags = 0x00020000;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -266,24 +269,31 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // Loads are unconditional (rows at or past n_valid are replaced by zeros
   // when written to LDS) so that nothing waits on them before the LDS write.
   // (the two block ids of a block are read one block ahead of its K/V)
-  // K and V rows take the same map: the page bases are uniform, the lane
-  // offset is k_off.
+  // K and V rows take the same map: each page is read through a buffer
+  // resource of its own (base and size in scalar registers, the size one
+  // page, so the hardware bounds every access to it) with the lane offset
+  // k_off: no 64-bit vector arithmetic per load.
+  auto page_load = [&](const uint8_t* page) __attribute__((always_inline)) {
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(page), (short)0, (int)kPageBytes, kBufferFlags);
+    if constexpr (sizeof(RawT) == 16) {
+      return bitcast<RawT>(__builtin_amdgcn_raw_buffer_load_b128(r, (int)k_off, 0, 0));
+    } else {
+      return bitcast<RawT>(__builtin_amdgcn_raw_buffer_load_b64(r, (int)k_off, 0, 0));
+    }
+  };
   auto fetch = [&](RawT (&kr)[KPT], RawT (&vr)[KPT], int ida, int idb) __attribute__((always_inline)) {
     const int64_t pa = (int64_t)__builtin_amdgcn_readfirstlane(clamp_blk(ida)) * blk_stride;
     const int64_t pb = (int64_t)__builtin_amdgcn_readfirstlane(clamp_blk(idb)) * blk_stride;
     if constexpr (KPT == 2) {
-      const uint8_t* ka = kpool + pa;
-      const uint8_t* kb = kpool + pb;
-      const uint8_t* va = vpool + pa;
-      const uint8_t* vb = vpool + pb;
-      kr[0] = *reinterpret_cast<const RawT*>(ka + k_off);
-      kr[1] = *reinterpret_cast<const RawT*>(kb + k_off);
-      vr[0] = *reinterpret_cast<const RawT*>(va + k_off);
-      vr[1] = *reinterpret_cast<const RawT*>(vb + k_off);
+      kr[0] = page_load(kpool + pa);
+      kr[1] = page_load(kpool + pb);
+      vr[0] = page_load(vpool + pa);
+      vr[1] = page_load(vpool + pb);
     } else {
       const int64_t pg = k_pgB ? pb : pa;
-      kr[0] = *reinterpret_cast<const RawT*>(kpool + pg + k_off);
-      vr[0] = *reinterpret_cast<const RawT*>(vpool + pg + k_off);
+      kr[0] = page_load(kpool + pg);
+      vr[0] = page_load(vpool + pg);
     }
   };
   auto masked = [](uint4 x, bool keep) __attribute__((always_inline)) {

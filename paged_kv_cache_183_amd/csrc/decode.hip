@@ -625,11 +625,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mma_kernel(DecodeParams p) {
 // has left beside its two decode workgroups (dispatched in this order, the
 // decode waves have the memory system first: tiles first made the call
 // about 7% slower).  Both write partials that the merge kernel, launched next
-// on the same stream, combines.
+// on the same stream, combines.  (Three waves per SIMD: the two decode
+// workgroups and the tile share each CU, so the kernel keeps to 168 VGPRs.)
 static_assert(kNW == tile::kPW, "decode and tile workgroups have the same size");
 template <int D, int KF, int QF, int PP>
-__global__ __launch_bounds__(kNW * 64) void decode_shared_kernel(DecodeParams p, PrefillParams sp,
-                                                                 int npfx) {
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_shared_kernel(DecodeParams p, PrefillParams sp, int npfx) {
   const int ndec = (int)gridDim.x - npfx;
   if ((int)blockIdx.x < ndec)
     decode_body<D, KF, QF, PP, false>(p, blockIdx.x, ndec);
