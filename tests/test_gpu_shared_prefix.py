@@ -48,6 +48,18 @@ def shared_case(seed, **over):
     return make_case(3, seed=seed, **cfg)
 
 
+@pytest.mark.parametrize("partition", [0, 32])
+def test_shared_prefix_batch_beyond_lds_prefix(partition):
+    """More sequences (2,100) than the decode keeps its page prefix for in LDS
+    (2,048): in the one-grid launch the page prefix then comes from its own
+    kernel first, and the prefix tiles cover 4,200 rows per kv-head."""
+    case = shared_case(46, B=2100, shared_tokens=32, suffix_range=(1, 40), Hq=4, Hkv=2)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    out = shared_decode(case, kc, vc, 2, partition=partition)
+    assert_close(case, to_f64(out), oracle(case, kp, vp))
+
+
 @pytest.mark.parametrize("kvq", [("e4m3", "f16"), ("e4m3", "bf16"), ("f16", "f16"), ("bf16", "bf16")])
 def test_shared_prefix_dtypes(kvq):
     kv, qd = kvq
