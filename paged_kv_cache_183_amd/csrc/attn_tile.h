@@ -24,7 +24,13 @@
 // heads; for the shared prefix 128 consecutive (sequence, query head) rows
 // and one split of the prefix pages.  Every row has its own kept key range
 // [lo, hi); the workgroup walks the union of its rows' ranges in blocks of 32
-// keys (two 16-token pages), staged through LDS once for its four waves:
+// keys (two 16-token pages), staged through LDS once for its four waves.
+// 16-bit pages at D = 128 in prefill go from HBM straight into LDS (buffer
+// loads that write LDS, no registers on the way), two blocks ahead of the
+// block being computed, in three LDS stages; the layouts are given where that
+// loop is.  The other tiles (FP8 pages, D = 64, the shared prefix, which runs
+// beside the decode in one grid and shares its LDS budget) stage through
+// registers, one block ahead:
 //  * K block row-major ([key][D], rows padded by 16 bytes);
 //  * V block row-major as well (rows padded by 32 bytes), staged exactly like
 //    K; the P.V operand of a lane is two transposing 8-byte reads
@@ -32,7 +38,6 @@
 //    The padding puts the four rows one read touches in distinct banks.
 //  FP8 pages (E4M3 or E5M2) are converted exactly to q's 16-bit format when
 //  staged.
-// Global loads run one block ahead of the matrix cores.
 // Per block and wave, on v_mfma_f32_32x32x16 (bf16 or f16, fp32 accumulate):
 //  * S^T = K Q^T: the output column of a lane is its query row, so each lane
 //    holds 16 scores of one row (keys 8j + 4h + i, h = lane / 32);
@@ -47,6 +52,8 @@
 // Keys past every row's range (page tails, padding pages) are staged as zeros
 // and masked, and their block-table entries are never read.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -134,8 +141,11 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   constexpr int64_t kPageBytes = 16 * D * EB;
   using RawT = typename Raw<KF>::T;
   static_assert(kPW * 64 * KPT == 32 * CH, "staging map: K chunks of a block over the threads");
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][KBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][VBUF];
+  // Direct path (HBM -> LDS) for 16-bit pages at D = 128 in prefill; the
+  // register-staged buffers shrink to placeholders there.
+  constexpr bool DMA = !PFX && !is_fp8(KF) && D == 128;
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[DMA ? 1 : 2][DMA ? 16 : KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[DMA ? 1 : 2][DMA ? 16 : VBUF];
   __shared__ int s_red[3];
 
   const int g = p.group;
@@ -334,16 +344,9 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // 4 keys of that half at its own d.
   const int vg = lane >> 4, vi = lane & 15;
   const uint8_t* v_rd = &s_v[0][(4 * (vg >> 1) + (vi >> 2)) * VROW + (16 * (vg & 1) + 4 * (vi & 3)) * 2];
-  auto block = [&](int buf, int kb) __attribute__((always_inline)) {
-    // ---- S^T = K Q^T ----
-    uint4 ka[KS];
-#pragma unroll
-    for (int t = 0; t < KS; ++t) ka[t] = *reinterpret_cast<const uint4*>(k_rd + buf * KBUF + 16 * t);
-    f32x16_t sacc = f32x16_t{};
-#pragma unroll
-    for (int t = 0; t < KS; ++t) sacc = mfma32<QF>(ka[t], qr[t], sacc);
-
-    // ---- online softmax (row = col; this lane holds keys 8j + 4hf + i) ----
+  // Online softmax of one block's scores (row = col; this lane holds keys
+  // 8j + 4hf + i): masks, running maximum, rescale, weights pw, row sum.
+  auto softmax = [&](const f32x16_t& sacc, int kb, uint32_t (&pw)[8]) __attribute__((always_inline)) {
     // Scores stay unscaled up to the exponent (scale > 0: max(c s) = c max(s)),
     // which is then one fma per score: exp2(c s - m).
     float sc[16];
@@ -376,12 +379,25 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
         for (int k = 0; k < 16; ++k) o[m][k] *= alpha;
     }
     const float nmu = (mrow == -INFINITY) ? 0.0f : -mrow;
-    uint32_t pw[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       pw[k] = pack2<QF>(fast_exp2(fmaf(sc[2 * k], c, nmu)), fast_exp2(fmaf(sc[2 * k + 1], c, nmu)));
       lsum = dot2<QF>(pw[k], kOnes, lsum);       // row sum of the rounded weights
     }
+
+  };
+
+  auto block = [&](int buf, int kb) __attribute__((always_inline)) {
+    // ---- S^T = K Q^T ----
+    uint4 ka[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) ka[t] = *reinterpret_cast<const uint4*>(k_rd + buf * KBUF + 16 * t);
+    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) sacc = mfma32<QF>(ka[t], qr[t], sacc);
+
+    uint32_t pw[8];
+    softmax(sacc, kb, pw);
 
     // ---- O^T += V^T P^T ----
     typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -402,6 +418,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     }
   };
 
+  if constexpr (!DMA) {
   // The barriers order the LDS buffers only, so the K/V loads of the next
   // block stay in flight across them.
   auto lds_barrier = []() __attribute__((always_inline)) {
@@ -434,6 +451,126 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     __builtin_amdgcn_sched_barrier(0);
     stage(buf ^ 1, kr, vr, kb_of(bi + 1));
     lds_barrier();
+  }
+
+  } else {
+    // Direct path: each wave issues four buffer loads into LDS per block (K
+    // and V, two 1 KiB pieces each), two blocks ahead of the one computed, into
+    // three stages of 16 KiB (K at +0, V at +8 KiB).  Every page's resource is
+    // sized to its valid rows, so rows at or past n_valid arrive as zeros.
+    //  K stage: [page][chunk (16 B)][row] -- load i of wave w covers chunks
+    //    8 (w & 1) + 4 i .. + 3 of page w >> 1, lane l chunk + l / 16, row l % 16;
+    //    the score operand of lane (col, hf) at k-step t is then at a fixed
+    //    lane offset + 256 t, and 16 lanes read 256 contiguous bytes.
+    //  V stage: row-major [32 rows][16 chunks], chunk c of row r at position
+    //    c ^ 4 (r % 4) -- load i of wave w covers rows 8 (w & 1) + 4 i .. + 3
+    //    of page w >> 1; the transposing reads of two 16-lane groups then hit
+    //    64 distinct banks.
+    __shared__ __attribute__((aligned(16))) uint8_t d_s0[16384], d_s1[16384], d_s2[16384];
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int dpage = wave >> 1;                 // the page this wave loads (uniform)
+    const int dhalf = wave & 1;
+    const int k_dma = l16 * 256 + lq * 16;       // + 16 c0
+    const int v_dma = lq * 256 + ((l16 ^ (4 * lq)) * 16);   // + 256 R0
+    auto dma = [&](uint8_t* dk, uint8_t* dv, int ida, int idb, int kb) __attribute__((always_inline)) {
+      const int id = __builtin_amdgcn_readfirstlane(clamp_blk(dpage ? idb : ida));
+      const uint64_t pg = (uint64_t)(uint32_t)id * (uint64_t)blk_stride;
+      const int bytes = __builtin_amdgcn_readfirstlane(min(max(n_valid - (kb + 16 * dpage), 0), 16) * 256);
+      __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(kpool + pg), (short)0, bytes, kBufferFlags);
+      __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(vpool + pg), (short)0, bytes, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c0 = 8 * dhalf + 4 * i;        // K chunks of this load
+        const int r0 = 8 * dhalf + 4 * i;        // V rows of this load
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(dk + dpage * 4096 + c0 * 256), 16,
+                                                 k_dma, c0 * 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(dv + (16 * dpage + r0) * 256), 16,
+                                                 v_dma, r0 * 256, 0, 0);
+      }
+    };
+    // the block ids of a block, read a block before its loads
+    auto ids_of = [&](int (&ids)[2], int kb) __attribute__((always_inline)) {
+      ids[0] = page_blk(kb >> 4);
+      ids[1] = page_blk((kb >> 4) + 1);
+    };
+    const int kbase = (col >> 4) * 4096 + 8 * hf * 256 + (col & 15) * 16;
+    const int vgq = lane >> 4, vj = (lane & 15) >> 2;
+    const int vrow = (4 * (vgq >> 1) + vj) * 256 + 32 * (vgq & 1) + 8 * (lane & 3);
+    int vb[D / 32];
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) vb[m] = vrow + 64 * (m ^ vj);
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    typedef v4i16_t __attribute__((address_space(3)))* lds_v4p;
+    auto block_dma = [&](const uint8_t* dk, const uint8_t* dv, int kb) __attribute__((always_inline)) {
+      uint4 ka[KS];
+#pragma unroll
+      for (int t = 0; t < KS; ++t) ka[t] = *reinterpret_cast<const uint4*>(dk + kbase + 256 * t);
+      f32x16_t sacc = f32x16_t{};
+#pragma unroll
+      for (int t = 0; t < KS; ++t) sacc = mfma32<QF>(ka[t], qr[t], sacc);
+      uint32_t pw[8];
+      softmax(sacc, kb, pw);
+#pragma unroll
+      for (int kap = 0; kap < 2; ++kap) {
+        const uint4 pb = make_uint4(pw[4 * kap], pw[4 * kap + 1], pw[4 * kap + 2], pw[4 * kap + 3]);
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+          const uint8_t* vr = dv + vb[m] + 16 * kap * 256;
+          const v4i16_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(vr));
+          const v4i16_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(vr + 8 * 256));
+          const uint2 u0 = bitcast<uint2>(a0), u1 = bitcast<uint2>(a1);
+          o[m] = mfma32<QF>(make_uint4(u0.x, u0.y, u1.x, u1.y), pb, o[m]);
+        }
+      }
+    };
+    // A barrier that the compiler keeps in place for memory operations but
+    // that waits for nothing by itself: the waits are explicit.
+    auto raw_barrier = []() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
+    int ids[2];
+    if (nblk > 0) {
+      int i0[2], i1[2];
+      ids_of(i0, kb_of(0));
+      ids_of(i1, kb_of(1));
+      dma(d_s0, d_s0 + 8192, i0[0], i0[1], kb_of(0));
+      dma(d_s1, d_s1 + 8192, i1[0], i1[1], kb_of(1));
+      ids_of(ids, kb_of(2));
+    }
+    // step of block bi in stage S: its loads done (the next block's four may
+    // still fly), this wave's reads of the stage loaded next done; barrier;
+    // the loads of block bi + 2 into the stage block bi - 1 used; compute.
+    // Every step issues exactly four loads, which keeps the vmcnt(4) exact,
+    // and the loop runs whole rounds of three: the steps past the last block
+    // only load (the last block again) and wait.  Skipping whole steps
+    // instead puts branches between the loads and the reads of a stage, and
+    // at those joins the compiler's wait insertion no longer tells the three
+    // stages apart: it then waits for the next block's loads as well before
+    // the K reads, which leaves a single block in flight.
+    auto step = [&](auto S, int bi) __attribute__((always_inline)) {
+      constexpr int s = decltype(S)::value;
+      uint8_t* dk = s == 0 ? d_s0 : s == 1 ? d_s1 : d_s2;
+      uint8_t* dv = dk + 8192;
+      uint8_t* nk = s == 0 ? d_s2 : s == 1 ? d_s0 : d_s1;
+      uint8_t* nv = nk + 8192;
+      __builtin_amdgcn_s_waitcnt(0x0074);       // vmcnt(4) lgkmcnt(0)
+      raw_barrier();
+      dma(nk, nv, ids[0], ids[1], kb_of(bi + 2));
+      ids_of(ids, kb_of(bi + 3));
+      if (bi < nblk) block_dma(dk, dv, kb0 + bi * kBK);
+    };
+    for (int bo = 0; bo < nblk; bo += 3) {
+      step(std::integral_constant<int, 0>{}, bo);
+      step(std::integral_constant<int, 1>{}, bo + 1);
+      step(std::integral_constant<int, 2>{}, bo + 2);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);         // vmcnt(0): no load into LDS outlives the workgroup
   }
 
   // ---- finalize: row values at d = 32 m + 8 j + 4 hf + i ----
