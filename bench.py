@@ -215,9 +215,14 @@ def bench_prefill(case, steps: int, warmup: int, chunk: int = 0) -> dict:
     bt, qsl, ctx = (case.block_tables.to(dev), case.query_start_loc.to(dev),
                     case.context_lens.to(dev))
 
+    # the tile order's workspace, allocated once as a serving loop would
+    ws = torch.empty(max(P.vllm_paged_attn_prefill_workspace_size(
+        case.num_seqs, case.num_q_heads, case.num_kv_heads, case.max_query_len), 1),
+        dtype=torch.uint8, device=dev)
+
     def call():
         P.vllm_paged_attn_prefill(out, q, view(kc), view(vc), bt, qsl, ctx, case.max_query_len,
-                                  case.scale, case.window)
+                                  case.scale, case.window, workspace=ws)
 
     if chunk:
         V = P.vllm_paged_chunked_local_virtual_count(case.num_seqs, int(case.query_start_loc[-1]),
@@ -226,10 +231,13 @@ def bench_prefill(case, steps: int, warmup: int, chunk: int = 0) -> dict:
         vcx = torch.empty(V, dtype=torch.int32, device=dev)
         vbt = torch.empty(V, chunk // 16, dtype=torch.int32, device=dev)
         mq = min(case.max_query_len, chunk)
+        ws = torch.empty(max(P.vllm_paged_attn_prefill_workspace_size(
+            V, case.num_q_heads, case.num_kv_heads, mq), 1), dtype=torch.uint8, device=dev)
 
         def call():  # noqa: F811
             P.vllm_paged_chunked_local_plan(qsl, ctx, bt, chunk, vq, vcx, vbt)
-            P.vllm_paged_attn_prefill(out, q, view(kc), view(vc), vbt, vq, vcx, mq, case.scale, 0)
+            P.vllm_paged_attn_prefill(out, q, view(kc), view(vc), vbt, vq, vcx, mq, case.scale, 0,
+                                      workspace=ws)
 
     for _ in range(warmup):
         call()

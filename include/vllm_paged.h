@@ -61,8 +61,9 @@ extern "C" {
 /* Version 2 appended k_scales / v_scales to vllm_attn_opts; version 3 added
  * FP8 pools in vllm_paged_attn_prefill and the local-attention and block
  * manager entry points; version 4 added vllm_paged_attn_decode_noalloc (no
- * struct changed). */
-#define VLLM_PAGED_ABI_VERSION 4
+ * struct changed); version 5 added vllm_paged_attn_prefill_workspace_size
+ * (vllm_paged_attn_prefill now takes opts->workspace; no struct changed). */
+#define VLLM_PAGED_ABI_VERSION 5
 #define VLLM_PAGED_BLOCK_SIZE 16
 
 typedef enum vllm_status {
@@ -109,13 +110,16 @@ typedef struct vllm_attn_opts {
                                multiple of 16.  Pieces of a sequence cut by chunk boundaries
                                are merged with the log-sum-exp rule by a second kernel */
   int32_t flags;            /* reserved, must be 0 */
-  void* workspace;          /* device scratch of the decode (piece records, page prefix,
-                               partial results of cut sequences, a spare page read by
-                               prefetches past the end), 256-byte aligned; needs no
-                               initialisation; calls that share a workspace must not overlap.
-                               NULL = the library allocates one stream-ordered
-                               (hipMallocAsync / hipFreeAsync on hip_stream) for the call */
-  size_t workspace_bytes;   /* size of `workspace`; see vllm_paged_attn_workspace_size */
+  void* workspace;          /* device scratch, 256-byte aligned; needs no initialisation;
+                               calls that share a workspace must not overlap.  Decode:
+                               piece records, page prefix, partial results of cut
+                               sequences, a spare page read by prefetches past the end.
+                               Chunked prefill: the order of its tiles.  NULL = the library
+                               allocates one stream-ordered (hipMallocAsync / hipFreeAsync
+                               on hip_stream) for the call */
+  size_t workspace_bytes;   /* size of `workspace`; see vllm_paged_attn_workspace_size,
+                               vllm_paged_attn_shared_prefix_workspace_size and
+                               vllm_paged_attn_prefill_workspace_size */
   /* appended in ABI version 2 (callers must be built against this header;
      check vllm_abi_version() >= 2): */
   const float* k_scales;    /* FP8 pools only: device pointer to Hkv fp32 scales, one per
@@ -332,6 +336,15 @@ size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
  *   scale        softmax scale applied to q.k, finite and > 0
  * Supported: D in {64, 128}; g = Hq / Hkv <= 128.  sumQ = 0 is a no-op.  Values of
  * query_start_loc are clamped to [0, sumQ], so no value leads outside q/out.
+ * Work order: a first kernel on hip_stream sorts the sequences by the keys of
+ * their longest tile and lays out the tiles of every (sequence, kv-head) pair
+ * together, longest sequences first, with no empty tiles in between; the tile
+ * kernel follows that order (the workgroup scheduler serves workgroups in
+ * launch order).  The order lives in opts->workspace
+ * (vllm_paged_attn_prefill_workspace_size bytes; VLLM_ERR_WORKSPACE if
+ * smaller) or in memory allocated stream-ordered for the call.  Batches of
+ * more than 4096 sequences run in launch order and need no workspace.  The
+ * order changes no result: every tile computes the same values in any order.
  */
 vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
                                     const vllm_tensor* k_cache, const vllm_tensor* v_cache,
@@ -340,6 +353,14 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
                                     const vllm_tensor* context_lens,
                                     int32_t max_query_len, float scale, int32_t window,
                                     const vllm_attn_opts* opts, void* hip_stream);
+
+/*
+ * Bytes of workspace vllm_paged_attn_prefill needs for these sizes (0: none,
+ * also for invalid arguments).  The same sizes as the call: B sequences,
+ * Hq and Hkv heads, max_query_len.
+ */
+size_t vllm_paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t max_query_len);
 
 /*
  * Chunked-local attention as a virtual batch (the local-attention section of

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     vllm_paged_attn_decode_shared_prefix,
     vllm_paged_attn_prefill,
     vllm_paged_attn_shared_prefix_workspace_size,
+    vllm_paged_attn_prefill_workspace_size,
     vllm_paged_attn_workspace_size,
     vllm_block_manager_init,
     vllm_block_manager_release,

@@ -34,7 +34,8 @@ EXPORTED = ["vllm_abi_version", "vllm_last_error", "vllm_paged_cache_write",
             "vllm_paged_attn_decode", "vllm_paged_attn_workspace_size",
             "vllm_paged_attn_decode_noalloc", "vllm_paged_read_pages",
             "vllm_paged_attn_decode_shared_prefix", "vllm_paged_attn_shared_prefix_workspace_size",
-            "vllm_paged_attn_prefill", "vllm_paged_attn_decode_append", "vllm_paged_chunked_local_plan",
+            "vllm_paged_attn_prefill", "vllm_paged_attn_prefill_workspace_size",
+            "vllm_paged_attn_decode_append", "vllm_paged_chunked_local_plan",
             "vllm_paged_chunked_local_virtual_count", "vllm_paged_recycle_pages",
             "vllm_block_manager_state_size", "vllm_block_manager_state_layout",
             "vllm_block_manager_init", "vllm_block_manager_workspace_size",
@@ -85,6 +86,8 @@ def _load():
                                                          ctypes.c_void_p]
     lib.vllm_paged_attn_shared_prefix_workspace_size.restype = ctypes.c_size_t
     lib.vllm_paged_attn_shared_prefix_workspace_size.argtypes = [ctypes.c_int32] * 7
+    lib.vllm_paged_attn_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.vllm_paged_attn_prefill_workspace_size.argtypes = [ctypes.c_int32] * 4
     lib.vllm_paged_attn_prefill.restype = ctypes.c_int
     lib.vllm_paged_attn_prefill.argtypes = [T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float,
                                             ctypes.c_int32, O, ctypes.c_void_p]
@@ -268,15 +271,23 @@ def vllm_paged_attn_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v
 
 def vllm_paged_attn_prefill(out, q, k_cache, v_cache, block_tables, query_start_loc,
                             context_lens, max_query_len, scale, window=0, k_scale=0.0, v_scale=0.0,
-                            stream=None) -> None:
-    """Chunked-prefill attention into ``out`` [sumQ, Hq, D]."""
+                            workspace=None, stream=None) -> None:
+    """Chunked-prefill attention into ``out`` [sumQ, Hq, D].  ``workspace``: a
+    uint8 device tensor of vllm_paged_attn_prefill_workspace_size bytes for the
+    tile order (None: the library allocates it for the call)."""
     args = [tensor_desc(x) for x in (out, q, k_cache, v_cache, block_tables, query_start_loc,
                                      context_lens)]
-    o = _opts(k_scale, v_scale)
+    o = _opts(k_scale, v_scale, workspace=workspace)
     _check(LIB.vllm_paged_attn_prefill(*[ctypes.byref(a) for a in args],
                                        ctypes.c_int32(max_query_len), ctypes.c_float(scale),
                                        ctypes.c_int32(window), ctypes.byref(o),
                                        ctypes.c_void_p(_stream(stream))))
+
+
+def vllm_paged_attn_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                           max_query_len) -> int:
+    return int(LIB.vllm_paged_attn_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                          max_query_len))
 
 
 def vllm_paged_chunked_local_virtual_count(num_seqs, num_tokens, chunk_size) -> int:

@@ -768,10 +768,40 @@ vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
   p.out_scale = vs;
   p.k_scales = (fp8 && opts) ? opts->k_scales : nullptr;
   p.v_scales = (fp8 && opts) ? opts->v_scales : nullptr;
-  VP_TRY(hip_status(vp::launch_prefill(p, (int)D, fmt_of(k_cache->dtype), fmt_of(q->dtype),
-                                       (hipStream_t)hip_stream),
-                    "prefill launch"));
+  // the tile order's memory: the caller's workspace, else stream-ordered
+  const size_t plan_bytes = vp::prefill_plan_bytes(B, Hkv, Hq / Hkv, max_query_len);
+  const hipStream_t stream = (hipStream_t)hip_stream;
+  void* ws = nullptr;
+  bool owned = false;
+  if (plan_bytes > 0) {
+    if (opts && opts->workspace) {
+      if (opts->workspace_bytes < plan_bytes)
+        return fail(VLLM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", opts->workspace_bytes,
+                    plan_bytes);
+      ws = opts->workspace;
+      VP_TRY(check_align(ws, "workspace", 256));
+      VP_TRY(check_device_ptr(ws, "workspace"));
+    } else {
+      VP_TRY(hip_status(hipMallocAsync(&ws, plan_bytes, stream), "workspace hipMallocAsync"));
+      owned = true;
+    }
+    p.plan = static_cast<int2*>(ws);
+  }
+  hipError_t e = vp::launch_prefill(p, (int)D, fmt_of(k_cache->dtype), fmt_of(q->dtype), stream);
+  if (owned) {
+    const hipError_t e2 = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = e2;
+  }
+  VP_TRY(hip_status(e, "prefill launch"));
   return ok();
+}
+
+size_t vllm_paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t max_query_len) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      num_q_heads / num_kv_heads > 128 || max_query_len < 0)
+    return 0;
+  return vp::prefill_plan_bytes(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, max_query_len);
 }
 
 int64_t vllm_paged_chunked_local_virtual_count(int32_t num_seqs, int32_t num_tokens,

@@ -160,12 +160,23 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // tiles attend to more keys (prefill) and are dispatched first.
   //   prefill: u = (sequence, kv-head), tiles of TQ tokens;
   //   shared prefix: u = (kv-head, split), tiles of 128 (sequence, head) rows.
+  // A prefill with a tile order takes entry b / 8 of list b % 8 instead
+  // (sorted pairs, still one XCD per pair, no empty tiles in between).
   const int ntiles = p.num_tiles;
   const int npairs = PFX ? p.num_kv_heads * p.num_splits : p.num_seqs * p.num_kv_heads;
   const int xcd = b % 8, kk = b / 8;
-  const int u = (kk / ntiles) * 8 + xcd;
+  int u = (kk / ntiles) * 8 + xcd;
+  int tile = ntiles - 1 - (kk % ntiles);
+  if constexpr (!PFX) {
+    if (p.plan) {
+      if (kk >= p.plan_stride) return;
+      const int2 e = p.plan[(int64_t)xcd * p.plan_stride + kk];
+      if (e.x < 0) return;
+      u = e.x;
+      tile = e.y;
+    }
+  }
   if (u >= npairs) return;
-  const int tile = ntiles - 1 - (kk % ntiles);
 
   int hk, seq_tbl;                             // kv-head, sequence whose table is read
   int key_begin, key_end;                      // keys of this workgroup, before row ranges

@@ -122,9 +122,37 @@ struct PrefillParams {
   float* pfx_o;                // [num_splits, B, Hq, D] normalized partial outputs
   float* pfx_m;                // [num_splits, B, Hq] running max, log2 units (-inf: empty)
   float* pfx_l;                // [num_splits, B, Hq] sum of exp2(s - m)
+  // chunked prefill: tile order built on the device ahead of the tiles (null:
+  // the grid order).  List x (of plan_stride entries) holds the tiles run by
+  // the workgroups b with b % 8 == x, in dispatch order: (s Hkv + kv-head,
+  // tile), or x = -1 past the list's tiles.
+  int2* plan;
+  int32_t plan_stride;
 };
 
-// Chunked prefill: kv_fmt = q_fmt, kE4M3 or kE5M2.
+// Chunked-prefill grid: ceil(B Hkv / 8) * 8 pair slots times the row tiles of
+// the longest chunk (kRows = 128 rows per tile, 128 / g tokens).
+inline int64_t prefill_grid(int64_t num_seqs, int64_t num_kv_heads, int64_t group,
+                            int64_t max_query_len) {
+  const int64_t tq = 128 / group;
+  if (tq < 1 || num_seqs <= 0 || max_query_len <= 0) return 0;
+  return (num_seqs * num_kv_heads + 7) / 8 * 8 * ((max_query_len + tq - 1) / tq);
+}
+// The tile order is built for batches of at most kPlanMaxSeqs sequences and
+// grids of at most kPlanMaxGrid workgroups (one int2 per workgroup); larger
+// calls run in the grid order.
+constexpr int kPlanMaxSeqs = 4096;
+constexpr int64_t kPlanMaxGrid = int64_t(1) << 22;
+inline size_t prefill_plan_bytes(int64_t num_seqs, int64_t num_kv_heads, int64_t group,
+                                 int64_t max_query_len) {
+  const int64_t grid = prefill_grid(num_seqs, num_kv_heads, group, max_query_len);
+  if (grid <= 0 || num_seqs > kPlanMaxSeqs || grid > kPlanMaxGrid) return 0;
+  return (size_t)grid * sizeof(int2);
+}
+
+// Chunked prefill: kv_fmt = q_fmt, kE4M3 or kE5M2.  With p.plan set
+// (prefill_plan_bytes of memory) the tile order is built first, on the same
+// stream.
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int q_fmt,
                           hipStream_t stream);
 // Shared-prefix partials: kv_fmt = q_fmt, kE4M3 or kE5M2.

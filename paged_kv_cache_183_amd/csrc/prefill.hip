@@ -11,6 +11,109 @@ __global__ __launch_bounds__(tile::kPW * 64) void attn_tile_kernel(PrefillParams
   tile::attn_tile_body<D, QF, KF, PFX>(p, blockIdx.x);
 }
 
+// Tile order of a chunked-prefill call, one workgroup.  Workgroups are handed
+// out in grid order, and the hardware deals consecutive ones to the XCDs and,
+// inside an XCD, to its shader engines in a fixed rotation: a workgroup waits
+// until the engine it is dealt to has room, and every later one waits behind
+// it.  Tiles of very different lengths in a row therefore leave slots idle
+// while work is still queued, and so do the empty tiles of short chunks.  The
+// order built here removes both:
+//  * sequences sorted by the key blocks of their last tile (their longest),
+//    longest first, ties by index; the (sequence, kv-head) pairs of sorted
+//    sequence r are v = r Hkv + h, run on XCD v % 8, all tiles of a pair
+//    together (they read the same K/V, which then stays in that XCD's L2),
+//    last tile first;
+//  * per XCD, the tiles packed in that order with no empty ones, and every
+//    entry past them marked empty (those workgroups exit at once).
+// The cost of a tile is the kernel's own block count, from the same clamped
+// metadata.  Sorting: bitonic over (~cost << 16 | s) in LDS.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillParams p) {
+  __shared__ uint32_t s_key[kPlanMaxSeqs];     // sort keys; after the sort, rank -> sequence
+  __shared__ int32_t s_nt[kPlanMaxSeqs];       // tiles of sequence s
+  __shared__ int32_t s_scan[kPlanThreads];
+  __shared__ int32_t s_run[8];
+  const int tid = threadIdx.x;
+  const int B = p.num_seqs, H = p.num_kv_heads;
+  const int tq = tile::kRows / p.group;
+  int N = 2;
+  while (N < B) N <<= 1;
+  for (int s = tid; s < N; s += kPlanThreads) {
+    uint32_t key = 0xFFFFFFFFu;                // padding: after every sequence
+    if (s < B) {
+      const int q_begin = min(max(p.query_start_loc[s], 0), p.num_tokens);
+      const int Qs = min(max(p.query_start_loc[s + 1], q_begin), p.num_tokens) - q_begin;
+      const int nt = min((Qs + tq - 1) / tq, p.num_tiles);
+      int cost = 0;
+      if (nt > 0) {
+        const int q0 = (nt - 1) * tq;
+        const int n = min(p.context_lens[s], p.bt_stride * 16);
+        const int pos0 = n - Qs + q0;
+        const int kend = pos0 + min(tq, Qs - q0);
+        const int kbeg = p.window > 0 ? max(0, pos0 - p.window + 1) : 0;
+        cost = kend > kbeg ? (kend - 1) / 32 - kbeg / 32 + 1 : 0;
+      }
+      s_nt[s] = nt;
+      key = ((uint32_t)(0xFFFF - min(cost, 0xFFFF)) << 16) | (uint32_t)s;
+    }
+    s_key[s] = key;
+  }
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += kPlanThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t a = s_key[i], c = s_key[l];
+          if ((a > c) == ((i & k) == 0)) {     // ascending where (i & k) == 0
+            s_key[i] = c;
+            s_key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Pairs in chunks of kPlanThreads: thread t takes v = base + t, on XCD
+  // t % 8, and its place in that XCD's list is the running count of earlier
+  // tiles there (a scan over the chunk's 128 pairs of each XCD).
+  if (tid < 8) s_run[tid] = 0;
+  __syncthreads();
+  const int64_t npairs = (int64_t)B * H;
+  const int x = tid & 7, k = tid >> 3;
+  constexpr int kPerXcd = kPlanThreads / 8;
+  for (int64_t base = 0; base < npairs; base += kPlanThreads) {
+    const int64_t v = base + tid;
+    int u = 0, cnt = 0;
+    if (v < npairs) {
+      const int r = (int)(v / H);
+      const int h = (int)(v - (int64_t)r * H);
+      const int s = (int)(s_key[r] & 0xFFFFu);
+      u = s * H + h;
+      cnt = s_nt[s];
+    }
+    s_scan[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < kPerXcd; d <<= 1) {
+      const int add = k >= d ? s_scan[tid - 8 * d] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    const int pos = s_run[x] + s_scan[tid] - cnt;
+    int2* list = p.plan + (int64_t)x * p.plan_stride;
+    for (int i = 0; i < cnt; ++i) list[pos + i] = make_int2(u, cnt - 1 - i);
+    __syncthreads();
+    if (k == kPerXcd - 1) s_run[x] += s_scan[tid];
+    __syncthreads();
+  }
+  for (int xx = 0; xx < 8; ++xx) {
+    int2* list = p.plan + (int64_t)xx * p.plan_stride;
+    for (int i = s_run[xx] + tid; i < p.plan_stride; i += kPlanThreads) list[i] = make_int2(-1, 0);
+  }
+}
+
 template <int QF, int KF, bool PFX>
 static hipError_t launch_tiles(const PrefillParams& x, int head_dim, int64_t grid, hipStream_t stream) {
   if (head_dim == 128)
@@ -35,6 +138,13 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int 
   const int64_t grid = (pairs + 7) / 8 * 8 * x.num_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (x.plan) {
+    if (p.num_seqs > kPlanMaxSeqs || grid > kPlanMaxGrid) return hipErrorInvalidValue;
+    x.plan_stride = (int32_t)(grid / 8);
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, x);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (kv_fmt == kE4M3)
     return q_fmt == kBF16 ? launch_tiles<kBF16, kE4M3, false>(x, head_dim, grid, stream)
                           : launch_tiles<kF16, kE4M3, false>(x, head_dim, grid, stream);

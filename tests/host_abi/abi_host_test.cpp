@@ -243,7 +243,21 @@ void prefill_cases() {
                    VLLM_OK, "prefill Hq=%d B=%d", Hq, B);
         EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 7, 0.0f, 0, nullptr, nullptr) ==
                    VLLM_ERR_INVALID_ARG, "prefill scale 0");
+        const size_t pw = vllm_paged_attn_prefill_workspace_size(B, Hq, Hkv, 7);
+        EXPECT(pw > 0, "prefill workspace size Hq=%d B=%d", Hq, B);
+        Buf pws(pw);
+        vllm_attn_opts o{};
+        o.workspace = pws.p;
+        o.workspace_bytes = pw;
+        EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 7, 0.1f, 0, &o, nullptr) ==
+                   VLLM_OK, "prefill, caller workspace");
+        o.workspace_bytes = pw - 1;
+        EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 7, 0.1f, 0, &o, nullptr) ==
+                   VLLM_ERR_WORKSPACE, "prefill, small workspace");
       }
+  EXPECT(vllm_paged_attn_prefill_workspace_size(4097, 8, 8, 7) == 0, "no order beyond 4096 sequences");
+  EXPECT(vllm_paged_attn_prefill_workspace_size(4, 8, 3, 7) == 0, "prefill workspace, Hq % Hkv");
+  EXPECT(vllm_paged_attn_prefill_workspace_size(4, 8, 8, 0) == 0, "prefill workspace, no rows");
 }
 
 void local_and_manager_cases() {

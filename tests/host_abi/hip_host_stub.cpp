@@ -200,6 +200,13 @@ hipError_t launch_prefill(const PrefillParams& p, int D, int kv_fmt, int q_fmt, 
   touch_r(p.query_start_loc, ((int64_t)p.num_seqs + 1) * 4, "prefill query_start_loc");
   touch_w(p.out, (int64_t)p.num_tokens * p.num_q_heads * D * esize(q_fmt), "prefill out");
   if (p.v_scales) touch_r(p.v_scales, p.num_kv_heads * 4, "prefill v_scales");
+  const size_t plan = prefill_plan_bytes(p.num_seqs, p.num_kv_heads, p.group, p.max_query_len);
+  if (p.plan) {
+    check(plan > 0, "prefill plan only where the order is built");
+    touch_w(p.plan, (int64_t)plan, "prefill plan");
+  } else {
+    check(plan == 0, "prefill plan given where the order is built");
+  }
   return hipSuccess;
 }
 

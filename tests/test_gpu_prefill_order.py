@@ -1,0 +1,80 @@
+"""GPU checks of the chunked prefill's tile order: the order kernel builds a
+per-XCD list of tiles (sequences sorted by their longest tile, every pair's
+tiles together, no empty tiles), and the tile kernel runs whatever the list
+holds.  A tile missing from the list would leave its rows of ``out`` at the
+NaN they start with; a list that were wrong in any other way would move rows
+to the wrong query.  Every case is compared with the fp64 oracle, on batches
+that take the order kernel's several code paths: more pairs than one pass of
+its workgroup (1,024), sort sizes above one key per thread, kv-head counts
+that do not divide by 8 (the lists of the XCDs then differ), chunks of length
+0 between the others, and a batch above the 4,096 sequences the order is built
+for (it runs in launch order, without a workspace)."""
+import pytest
+import torch
+
+from workloads import make_case
+
+from _util import oracle_pools
+from _gpu import gpu_fill, to_f64, pool_view, assert_close, DEV
+from test_gpu_prefill import oracle_prefill, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+import paged_kv_cache_183_amd as P  # noqa: E402
+
+
+def call(case, kc, vc, out, workspace=None):
+    P.vllm_paged_attn_prefill(out, case.q.to(DEV), pool_view(kc, case.kv_dtype),
+                              pool_view(vc, case.kv_dtype), case.block_tables.to(DEV),
+                              case.query_start_loc.to(DEV), case.context_lens.to(DEV),
+                              case.max_query_len, case.scale, case.window, workspace=workspace)
+
+
+def test_prefill_order_caller_workspace_matches_own():
+    """A caller's workspace of exactly the reported size gives the same bits
+    as the library's own; one byte less is refused before any launch."""
+    case = make_case(4, seed=51, B=9, qlen_range=(0, 200), cached_range=(0, 300), Hq=8, Hkv=2)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    own = run_prefill(case, kc, vc)
+    assert_close(case, to_f64(own), oracle_prefill(case, kp, vp))
+    n = P.vllm_paged_attn_prefill_workspace_size(case.num_seqs, case.num_q_heads,
+                                                 case.num_kv_heads, case.max_query_len)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    out = torch.full_like(own, float("nan"))
+    call(case, kc, vc, out, workspace=ws)
+    assert torch.equal(out, own)
+    # a second call reuses the workspace as it was left
+    out2 = torch.full_like(own, float("nan"))
+    call(case, kc, vc, out2, workspace=ws)
+    assert torch.equal(out2, own)
+    small = torch.empty(n - 1, dtype=torch.uint8, device=DEV)
+    with pytest.raises(P.VllmError) as err:
+        call(case, kc, vc, torch.empty_like(own), workspace=small)
+    assert err.value.status == 4
+
+
+@pytest.mark.parametrize("hkv,g", [(1, 4), (3, 2), (8, 2)])
+def test_prefill_order_many_sequences(hkv, g):
+    """1,500 sequences, a fifth of them with no query rows: 1,500 Hkv pairs
+    (beyond one pass of the order kernel for Hkv = 3 and 8) and a sort of
+    2,048 keys."""
+    case = make_case(4, seed=60 + hkv, B=1500, qlen_range=(0, 40), cached_range=(0, 100),
+                     Hq=g * hkv, Hkv=hkv, D=64, window=0 if hkv == 3 else 50)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    assert P.vllm_paged_attn_prefill_workspace_size(case.num_seqs, case.num_q_heads,
+                                                    case.num_kv_heads, case.max_query_len) > 0
+    assert_close(case, to_f64(run_prefill(case, kc, vc)), oracle_prefill(case, kp, vp))
+
+
+def test_prefill_beyond_order_limit():
+    """4,100 sequences: no tile order (workspace size 0), launch order."""
+    case = make_case(4, seed=70, B=4100, qlen_range=(0, 3), cached_range=(0, 30), Hq=2, Hkv=1,
+                     D=64, window=0)
+    assert P.vllm_paged_attn_prefill_workspace_size(case.num_seqs, case.num_q_heads,
+                                                    case.num_kv_heads, case.max_query_len) == 0
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    assert_close(case, to_f64(run_prefill(case, kc, vc)), oracle_prefill(case, kp, vp))
