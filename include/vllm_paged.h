@@ -342,9 +342,11 @@ size_t vllm_paged_attn_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
  * kernel follows that order (the workgroup scheduler serves workgroups in
  * launch order).  The order lives in opts->workspace
  * (vllm_paged_attn_prefill_workspace_size bytes; VLLM_ERR_WORKSPACE if
- * smaller) or in memory allocated stream-ordered for the call.  Batches of
- * more than 4096 sequences run in launch order and need no workspace.  The
- * order changes no result: every tile computes the same values in any order.
+ * smaller) or in memory allocated stream-ordered for the call.  Calls of
+ * fewer than 2048 workgroups (ceil(B Hkv / 8) * 8 * ceil(max_query_len /
+ * (128 / g))) or more than 4096 sequences run in launch order and need no
+ * workspace.  The order changes no result: every tile computes the same
+ * values in any order.
  */
 vllm_status vllm_paged_attn_prefill(vllm_tensor* out, const vllm_tensor* q,
                                     const vllm_tensor* k_cache, const vllm_tensor* v_cache,

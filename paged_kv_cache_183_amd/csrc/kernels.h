@@ -138,15 +138,18 @@ inline int64_t prefill_grid(int64_t num_seqs, int64_t num_kv_heads, int64_t grou
   if (tq < 1 || num_seqs <= 0 || max_query_len <= 0) return 0;
   return (num_seqs * num_kv_heads + 7) / 8 * 8 * ((max_query_len + tq - 1) / tq);
 }
-// The tile order is built for batches of at most kPlanMaxSeqs sequences and
-// grids of at most kPlanMaxGrid workgroups (one int2 per workgroup); larger
-// calls run in the grid order.
+// The tile order is built for grids of kPlanMinGrid to kPlanMaxGrid
+// workgroups (one int2 each) of at most kPlanMaxSeqs sequences; other calls
+// run in the grid order.  Below kPlanMinGrid (under three rounds of the 768
+// tiles the GPU holds at once) most tiles start together anyway, and the
+// order's own kernel would cost more than it saves.
 constexpr int kPlanMaxSeqs = 4096;
+constexpr int64_t kPlanMinGrid = 2048;
 constexpr int64_t kPlanMaxGrid = int64_t(1) << 22;
 inline size_t prefill_plan_bytes(int64_t num_seqs, int64_t num_kv_heads, int64_t group,
                                  int64_t max_query_len) {
   const int64_t grid = prefill_grid(num_seqs, num_kv_heads, group, max_query_len);
-  if (grid <= 0 || num_seqs > kPlanMaxSeqs || grid > kPlanMaxGrid) return 0;
+  if (grid < kPlanMinGrid || num_seqs > kPlanMaxSeqs || grid > kPlanMaxGrid) return 0;
   return (size_t)grid * sizeof(int2);
 }
 

@@ -26,8 +26,9 @@ __global__ __launch_bounds__(tile::kPW * 64) void attn_tile_kernel(PrefillParams
 //  * per XCD, the tiles packed in that order with no empty ones, and every
 //    entry past them marked empty (those workgroups exit at once).
 // The cost of a tile is the kernel's own block count, from the same clamped
-// metadata.  Sorting: bitonic over (~cost << 16 | s) in LDS.
-constexpr int kPlanThreads = 1024;
+// metadata.  Sorting: bitonic over (~cost << 16 | s) in LDS.  The kernel is
+// all latency (a few global loads, then barriers), so it runs as 4 waves.
+constexpr int kPlanThreads = 256;
 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillParams p) {
   __shared__ uint32_t s_key[kPlanMaxSeqs];     // sort keys; after the sort, rank -> sequence
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillParam
   }
   // Pairs in chunks of kPlanThreads: thread t takes v = base + t, on XCD
   // t % 8, and its place in that XCD's list is the running count of earlier
-  // tiles there (a scan over the chunk's 128 pairs of each XCD).
+  // tiles there (a scan over the chunk's kPlanThreads / 8 pairs of each XCD).
   if (tid < 8) s_run[tid] = 0;
   __syncthreads();
   const int64_t npairs = (int64_t)B * H;
@@ -139,7 +140,7 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, int kv_fmt, int 
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (x.plan) {
-    if (p.num_seqs > kPlanMaxSeqs || grid > kPlanMaxGrid) return hipErrorInvalidValue;
+    if (p.num_seqs > kPlanMaxSeqs || grid < kPlanMinGrid || grid > kPlanMaxGrid) return hipErrorInvalidValue;
     x.plan_stride = (int32_t)(grid / 8);
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, x);
     const hipError_t e = hipGetLastError();

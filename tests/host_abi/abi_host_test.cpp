@@ -243,19 +243,29 @@ void prefill_cases() {
                    VLLM_OK, "prefill Hq=%d B=%d", Hq, B);
         EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 7, 0.0f, 0, nullptr, nullptr) ==
                    VLLM_ERR_INVALID_ARG, "prefill scale 0");
-        const size_t pw = vllm_paged_attn_prefill_workspace_size(B, Hq, Hkv, 7);
-        EXPECT(pw > 0, "prefill workspace size Hq=%d B=%d", Hq, B);
+        EXPECT(vllm_paged_attn_prefill_workspace_size(B, Hq, Hkv, 7) == 0, "small grid: no order");
+        // max_query_len is an upper bound: 8192 makes grids of 2048 and more
+        // workgroups (the order is built) except at B = 1, Hq = 8 (512)
+        const int tqk = 128 / (Hq / Hkv);
+        const int64_t grid = (int64_t)(B * Hkv + 7) / 8 * 8 * ((8192 + tqk - 1) / tqk);
+        const size_t pw = vllm_paged_attn_prefill_workspace_size(B, Hq, Hkv, 8192);
+        EXPECT((pw > 0) == (grid >= 2048) && (pw == 0 || pw == (size_t)grid * 8),
+               "prefill workspace size Hq=%d B=%d", Hq, B);
+        if (pw == 0) continue;
         Buf pws(pw);
         vllm_attn_opts o{};
         o.workspace = pws.p;
         o.workspace_bytes = pw;
-        EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 7, 0.1f, 0, &o, nullptr) ==
+        EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 8192, 0.1f, 0, &o, nullptr) ==
                    VLLM_OK, "prefill, caller workspace");
+        EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 8192, 0.1f, 0, nullptr, nullptr) ==
+                   VLLM_OK, "prefill, own workspace");
         o.workspace_bytes = pw - 1;
-        EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 7, 0.1f, 0, &o, nullptr) ==
+        EXPECT(vllm_paged_attn_prefill(&to, &tq, &tk, &tv, &tb, &tqs, &tc, 8192, 0.1f, 0, &o, nullptr) ==
                    VLLM_ERR_WORKSPACE, "prefill, small workspace");
       }
-  EXPECT(vllm_paged_attn_prefill_workspace_size(4097, 8, 8, 7) == 0, "no order beyond 4096 sequences");
+  EXPECT(vllm_paged_attn_prefill_workspace_size(4097, 8, 8, 8192) == 0, "no order beyond 4096 sequences");
+  EXPECT(vllm_paged_attn_prefill_workspace_size(4096, 8, 8, 8192) > 0, "order up to 4096 sequences");
   EXPECT(vllm_paged_attn_prefill_workspace_size(4, 8, 3, 7) == 0, "prefill workspace, Hq % Hkv");
   EXPECT(vllm_paged_attn_prefill_workspace_size(4, 8, 8, 0) == 0, "prefill workspace, no rows");
 }

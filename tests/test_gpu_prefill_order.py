@@ -23,35 +23,40 @@ pytestmark = pytest.mark.gpu
 import paged_kv_cache_183_amd as P  # noqa: E402
 
 
-def call(case, kc, vc, out, workspace=None):
+def call(case, kc, vc, out, workspace=None, max_query_len=None):
     P.vllm_paged_attn_prefill(out, case.q.to(DEV), pool_view(kc, case.kv_dtype),
                               pool_view(vc, case.kv_dtype), case.block_tables.to(DEV),
                               case.query_start_loc.to(DEV), case.context_lens.to(DEV),
-                              case.max_query_len, case.scale, case.window, workspace=workspace)
+                              max_query_len or case.max_query_len, case.scale, case.window,
+                              workspace=workspace)
 
 
 def test_prefill_order_caller_workspace_matches_own():
     """A caller's workspace of exactly the reported size gives the same bits
-    as the library's own; one byte less is refused before any launch."""
+    as the library's own; one byte less is refused before any launch.  The
+    generous max_query_len (an upper bound) makes a grid of 2,256 workgroups,
+    most of them empty tiles, which the order leaves out."""
     case = make_case(4, seed=51, B=9, qlen_range=(0, 200), cached_range=(0, 300), Hq=8, Hkv=2)
+    mq = 3000
     kc, vc = gpu_fill(case)
     kp, vp = oracle_pools(case)
-    own = run_prefill(case, kc, vc)
+    own = run_prefill(case, kc, vc, max_query_len=mq)
     assert_close(case, to_f64(own), oracle_prefill(case, kp, vp))
+    assert torch.equal(own, run_prefill(case, kc, vc))      # the small grid: launch order
     n = P.vllm_paged_attn_prefill_workspace_size(case.num_seqs, case.num_q_heads,
-                                                 case.num_kv_heads, case.max_query_len)
+                                                 case.num_kv_heads, mq)
     assert n > 0
     ws = torch.empty(n, dtype=torch.uint8, device=DEV)
     out = torch.full_like(own, float("nan"))
-    call(case, kc, vc, out, workspace=ws)
+    call(case, kc, vc, out, workspace=ws, max_query_len=mq)
     assert torch.equal(out, own)
     # a second call reuses the workspace as it was left
     out2 = torch.full_like(own, float("nan"))
-    call(case, kc, vc, out2, workspace=ws)
+    call(case, kc, vc, out2, workspace=ws, max_query_len=mq)
     assert torch.equal(out2, own)
     small = torch.empty(n - 1, dtype=torch.uint8, device=DEV)
     with pytest.raises(P.VllmError) as err:
-        call(case, kc, vc, torch.empty_like(own), workspace=small)
+        call(case, kc, vc, torch.empty_like(own), workspace=small, max_query_len=mq)
     assert err.value.status == 4
 
 
