@@ -104,7 +104,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // Max of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the halves).
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
-  return fmaxf(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
+  return __builtin_elementwise_maximum(bitcast<float>((uint32_t)r[0]), bitcast<float>((uint32_t)r[1]));
 }
 
 // Raw pool data of one 8-element chunk: 16 bytes for 16-bit pools, 8 for FP8.
@@ -344,6 +344,8 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   float mrow = -INFINITY, lsum = 0.0f;
   // scale * log2(e), times the K scale of this kv-head for FP8 pools
   const float c = p.k_scales ? p.score_base * p.k_scales[hk] : p.score_scale;
+  const float inv_c = 1.0f / c;
+  float thr = -INFINITY;                       // (mrow + kTauP) / c: compared with raw scores
 
   // One block: S^T, online softmax, O^T update.  buf holds the block's K and
   // V^T.  Lane reads: K rows col (16 bytes at d = D/2 hf + 8 t), V^T rows
@@ -376,13 +378,17 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     }
     float mx = sc[0];
 #pragma unroll
-    for (int k = 1; k < 16; ++k) mx = fmaxf(mx, sc[k]);
-    mx = half_max(mx) * c;
-    const bool need = mx > mrow + kTauP;
+    // (the NaN-propagating maximum is v_maximum3_f32 with no canonicalising
+    // of its operands; the raw maximum is compared with the threshold
+    // (mrow + tau) / c, which only changes with mrow)
+    for (int k = 1; k < 16; ++k) mx = __builtin_elementwise_maximum(mx, sc[k]);
+    mx = half_max(mx);
+    const bool need = mx > thr;
     if (__any(need)) {
-      const float mn = need ? fmaxf(mrow, mx) : mrow;
+      const float mn = need ? fmaxf(mrow, mx * c) : mrow;
       const float alpha = (mrow == -INFINITY) ? 0.0f : fast_exp2(mrow - mn);
       mrow = mn;
+      thr = (mrow + kTauP) * inv_c;
       lsum *= alpha;
 #pragma unroll
       for (int m = 0; m < D / 32; ++m)
