@@ -376,11 +376,11 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
           if (t < r_lo || t >= r_hi) sc[4 * j + i] = -INFINITY;
         }
     }
-    float mx = sc[0];
-#pragma unroll
     // (the NaN-propagating maximum is v_maximum3_f32 with no canonicalising
     // of its operands; the raw maximum is compared with the threshold
     // (mrow + tau) / c, which only changes with mrow)
+    float mx = sc[0];
+#pragma unroll
     for (int k = 1; k < 16; ++k) mx = __builtin_elementwise_maximum(mx, sc[k]);
     mx = half_max(mx);
     const bool need = mx > thr;
