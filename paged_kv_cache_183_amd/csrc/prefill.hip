@@ -26,19 +26,22 @@ __global__ __launch_bounds__(tile::kPW * 64) void attn_tile_kernel(PrefillParams
 //  * per XCD, the tiles packed in that order with no empty ones, and every
 //    entry past them marked empty (those workgroups exit at once).
 // The cost of a tile is the kernel's own block count, from the same clamped
-// metadata.  Sorting: bitonic over (~cost << 16 | s) in LDS.  The kernel is
-// all latency (a few global loads, then barriers), so it runs as 4 waves.
+// metadata.  Sort keys are (~cost << 16 | s), so they are distinct.  Up to
+// kPlanThreads sequences a key's rank is the count of smaller keys (one pass
+// over LDS, no barriers); larger batches sort bitonically in LDS.  The list of
+// XCD x is written by the 32 lanes of half-wave x, which carry its running
+// length in registers: no barrier in that loop either.  The kernel is all
+// latency, so it runs as one workgroup of 4 waves.
 constexpr int kPlanThreads = 256;
 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillParams p) {
-  __shared__ uint32_t s_key[kPlanMaxSeqs];     // sort keys; after the sort, rank -> sequence
+  __shared__ __attribute__((aligned(16))) uint32_t s_key[kPlanMaxSeqs];   // sort keys
+  __shared__ uint32_t s_ord[kPlanMaxSeqs];     // rank -> key (rank sort)
   __shared__ int32_t s_nt[kPlanMaxSeqs];       // tiles of sequence s
-  __shared__ int32_t s_scan[kPlanThreads];
-  __shared__ int32_t s_run[8];
   const int tid = threadIdx.x;
   const int B = p.num_seqs, H = p.num_kv_heads;
   const int tq = tile::kRows / p.group;
-  int N = 2;
+  int N = 4;
   while (N < B) N <<= 1;
   for (int s = tid; s < N; s += kPlanThreads) {
     uint32_t key = 0xFFFFFFFFu;                // padding: after every sequence
@@ -61,58 +64,64 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillParam
     s_key[s] = key;
   }
   __syncthreads();
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += kPlanThreads) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint32_t a = s_key[i], c = s_key[l];
-          if ((a > c) == ((i & k) == 0)) {     // ascending where (i & k) == 0
-            s_key[i] = c;
-            s_key[l] = a;
+  const uint32_t* ord = s_key;                 // rank -> key
+  if (N <= kPlanThreads) {
+    if (tid < N) {
+      const uint32_t mine = s_key[tid];
+      int r = 0;
+      for (int i = 0; i < N; i += 4) {
+        const uint4 k4 = *reinterpret_cast<const uint4*>(&s_key[i]);
+        r += (k4.x < mine) + (k4.y < mine) + (k4.z < mine) + (k4.w < mine);
+      }
+      s_ord[r] = mine;                         // (padding keys share a rank >= B)
+    }
+    ord = s_ord;
+  } else {
+    for (int k = 2; k <= N; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < N; i += kPlanThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const uint32_t a = s_key[i], c = s_key[l];
+            if ((a > c) == ((i & k) == 0)) {   // ascending where (i & k) == 0
+              s_key[i] = c;
+              s_key[l] = a;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
-  // Pairs in chunks of kPlanThreads: thread t takes v = base + t, on XCD
-  // t % 8, and its place in that XCD's list is the running count of earlier
-  // tiles there (a scan over the chunk's kPlanThreads / 8 pairs of each XCD).
-  if (tid < 8) s_run[tid] = 0;
   __syncthreads();
+  // Pairs in chunks of kPlanThreads: lane k of half-wave x takes
+  // v = base + 8 k + x (on XCD x); its place in list x is the list's length
+  // so far plus the tiles of the half-wave's earlier lanes.
+  const int x = tid >> 5, k = tid & 31;
+  int2* list = p.plan + (int64_t)x * p.plan_stride;
+  int run = 0;
   const int64_t npairs = (int64_t)B * H;
-  const int x = tid & 7, k = tid >> 3;
-  constexpr int kPerXcd = kPlanThreads / 8;
   for (int64_t base = 0; base < npairs; base += kPlanThreads) {
-    const int64_t v = base + tid;
+    const int64_t v = base + 8 * k + x;
     int u = 0, cnt = 0;
     if (v < npairs) {
       const int r = (int)(v / H);
       const int h = (int)(v - (int64_t)r * H);
-      const int s = (int)(s_key[r] & 0xFFFFu);
+      const int s = (int)(ord[r] & 0xFFFFu);
       u = s * H + h;
       cnt = s_nt[s];
     }
-    s_scan[tid] = cnt;
-    __syncthreads();
-    for (int d = 1; d < kPerXcd; d <<= 1) {
-      const int add = k >= d ? s_scan[tid - 8 * d] : 0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
+    int inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int y = __shfl_up(inc, d, 32);
+      if (k >= d) inc += y;
     }
-    const int pos = s_run[x] + s_scan[tid] - cnt;
-    int2* list = p.plan + (int64_t)x * p.plan_stride;
+    const int pos = run + inc - cnt;
     for (int i = 0; i < cnt; ++i) list[pos + i] = make_int2(u, cnt - 1 - i);
-    __syncthreads();
-    if (k == kPerXcd - 1) s_run[x] += s_scan[tid];
-    __syncthreads();
+    run += __shfl(inc, 31, 32);
   }
-  for (int xx = 0; xx < 8; ++xx) {
-    int2* list = p.plan + (int64_t)xx * p.plan_stride;
-    for (int i = s_run[xx] + tid; i < p.plan_stride; i += kPlanThreads) list[i] = make_int2(-1, 0);
-  }
+  for (int i = run + k; i < p.plan_stride; i += 32) list[i] = make_int2(-1, 0);
 }
 
 template <int QF, int KF, bool PFX>
