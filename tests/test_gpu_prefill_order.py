@@ -100,3 +100,45 @@ def test_prefill_order_sort_forms(B):
     kp, vp = oracle_pools(case)
     assert_close(case, to_f64(run_prefill(case, kc, vc, max_query_len=mq)),
                  oracle_prefill(case, kp, vp))
+
+
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+def test_prefill_order_direct_loads(qd):
+    """D = 128 with 16-bit pools (K/V loaded straight into LDS) under the tile
+    order: 3 kv-heads (the XCD lists differ), a window of 50, chunks of 0 to
+    100 tokens over caches of up to 300; max_query_len = 1,600 makes a grid of
+    7,600 workgroups."""
+    case = make_case(4, seed=90, B=100, qlen_range=(0, 100), cached_range=(0, 300), Hq=6, Hkv=3,
+                     kv=qd, q=qd, window=50)
+    mq = 1600
+    assert P.vllm_paged_attn_prefill_workspace_size(case.num_seqs, case.num_q_heads,
+                                                    case.num_kv_heads, mq) > 0
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    out = run_prefill(case, kc, vc, max_query_len=mq)
+    assert_close(case, to_f64(out), oracle_prefill(case, kp, vp))
+    assert torch.equal(out, run_prefill(case, kc, vc))      # the launch order, same bits
+
+
+SWEEP_HEADS = [(8, 8), (16, 8), (4, 1), (12, 3), (16, 4), (6, 2), (5, 5), (16, 2)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_random_shapes(seed):
+    """Seeded random metadata through whichever path and order a call takes:
+    1 to 120 sequences, head groupings of 1 to 8, D = 64 or 128, bf16 or f16,
+    windows of 0 to 1,000, chunks of 0 to 150 tokens over caches of 0 to 300,
+    max_query_len tight or 8 or 64 times generous."""
+    import numpy as np
+    r = np.random.RandomState(1000 + seed)
+    hq, hkv = SWEEP_HEADS[r.randint(len(SWEEP_HEADS))]
+    qd = ["bf16", "f16"][r.randint(2)]
+    case = make_case(4, seed=2000 + seed, B=int(r.randint(1, 121)),
+                     qlen_range=(0, int(r.randint(1, 151))), cached_range=(0, int(r.randint(0, 301))),
+                     Hq=hq, Hkv=hkv, D=[64, 128][r.randint(2)], kv=qd, q=qd,
+                     window=[0, 16, 100, 1000][r.randint(4)])
+    mq = max(case.max_query_len, 1) * [1, 8, 64][r.randint(3)]
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    assert_close(case, to_f64(run_prefill(case, kc, vc, max_query_len=mq)),
+                 oracle_prefill(case, kp, vp))
