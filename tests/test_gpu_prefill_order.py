@@ -85,12 +85,13 @@ def test_prefill_beyond_order_limit():
     assert_close(case, to_f64(run_prefill(case, kc, vc)), oracle_prefill(case, kp, vp))
 
 
-@pytest.mark.parametrize("B", [256, 257])
+@pytest.mark.parametrize("B", [256, 257, 4096])
 def test_prefill_order_sort_forms(B):
-    """256 sequences are ranked in one pass, 257 sorted bitonically (512
-    keys): both orders give every row its query.  Many sequences share a
-    cost (ties broken by index); max_query_len = 320 (an upper bound) makes a
-    grid of 2,560 or more workgroups, most tiles empty."""
+    """256 sequences are ranked in one pass, 257 and 4,096 (the most the
+    order takes) sorted bitonically (512 and 4,096 keys): every order gives
+    every row its query.  Many sequences share a cost (ties broken by index);
+    max_query_len = 320 (an upper bound) makes a grid of 2,560 or more
+    workgroups, most tiles empty."""
     case = make_case(4, seed=80 + B, B=B, qlen_range=(0, 40), cached_range=(0, 60), Hq=4, Hkv=1,
                      D=64, window=0)
     mq = 320
