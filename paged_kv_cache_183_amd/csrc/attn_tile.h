@@ -436,6 +436,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   };
 
   if constexpr (!DMA) {
+  // ---- register staging (FP8 pools, D = 64, shared-prefix tiles) ----
   // The barriers order the LDS buffers only, so the K/V loads of the next
   // block stay in flight across them.
   auto lds_barrier = []() __attribute__((always_inline)) {
@@ -471,7 +472,8 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   }
 
   } else {
-    // Direct path: each wave issues four buffer loads into LDS per block (K
+    // ---- direct loads into LDS (16-bit pools, D = 128, prefill) ----
+    // Each wave issues four buffer loads into LDS per block (K
     // and V, two 1 KiB pieces each), two blocks ahead of the one computed, into
     // three stages of 16 KiB (K at +0, V at +8 KiB).  Every page's resource is
     // sized to its valid rows, so rows at or past n_valid arrive as zeros.
