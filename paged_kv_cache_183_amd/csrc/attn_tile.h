@@ -182,6 +182,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   int key_begin, key_end;                      // keys of this workgroup, before row ranges
   int r_lo, r_hi;                              // this row's kept keys [r_lo, r_hi)
   bool row_ok;
+  bool wave_on;                                // some row of this wave is valid (uniform)
   int64_t q_off;                               // element offset of this row in q (and out)
   int split = 0;
   if constexpr (!PFX) {
@@ -199,6 +200,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     const int n = min(p.context_lens[s], p.bt_stride * 16);
     const int pos0 = n - Qs + q0;              // position of the tile's first token
     row_ok = row < nt * g;
+    wave_on = __builtin_amdgcn_readfirstlane(wave * 32 < nt * g);
     const int tok = min(row, nt * g - 1) / g;
     const int head = min(row, nt * g - 1) - tok * g;
     const int ppos = pos0 + tok;               // query position of the row
@@ -217,6 +219,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     if (tile * kRows >= rows_total) return;
     const int rg = tile * kRows + row;
     row_ok = rg < rows_total;
+    wave_on = __builtin_amdgcn_readfirstlane(tile * kRows + wave * 32 < rows_total);
     const int rgc = min(rg, rows_total - 1);
     const int s = rgc / g;
     const int head = rgc - s * g;
@@ -465,7 +468,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     ida = na;
     idb = nb;
     __builtin_amdgcn_sched_barrier(0);
-    block(buf, kb0 + bi * kBK);
+    if (wave_on) block(buf, kb0 + bi * kBK);   // (a wave of padding rows only stages)
     __builtin_amdgcn_sched_barrier(0);
     stage(buf ^ 1, kr, vr, kb_of(bi + 1));
     lds_barrier();
@@ -582,7 +585,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
       raw_barrier();
       dma(nk, nv, ids[0], ids[1], kb_of(bi + 2));
       ids_of(ids, kb_of(bi + 3));
-      if (bi < nblk) block_dma(dk, dv, kb0 + bi * kBK);
+      if (bi < nblk && wave_on) block_dma(dk, dv, kb0 + bi * kBK);   // (padding waves: loads only)
     };
     for (int bo = 0; bo < nblk; bo += 3) {
       step(std::integral_constant<int, 0>{}, bo);
