@@ -349,6 +349,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   const float c = p.k_scales ? p.score_base * p.k_scales[hk] : p.score_scale;
   const float inv_c = 1.0f / c;
   float thr = -INFINITY;                       // (mrow + kTauP) / c: compared with raw scores
+  float nmu = 0.0f;                            // -mrow (0 while mrow is -inf)
 
   // One block: S^T, online softmax, O^T update.  buf holds the block's K and
   // V^T.  Lane reads: K rows col (16 bytes at d = D/2 hf + 8 t), V^T rows
@@ -392,13 +393,13 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
       const float alpha = (mrow == -INFINITY) ? 0.0f : fast_exp2(mrow - mn);
       mrow = mn;
       thr = (mrow + kTauP) * inv_c;
+      nmu = (mrow == -INFINITY) ? 0.0f : -mrow;
       lsum *= alpha;
 #pragma unroll
       for (int m = 0; m < D / 32; ++m)
 #pragma unroll
         for (int k = 0; k < 16; ++k) o[m][k] *= alpha;
     }
-    const float nmu = (mrow == -INFINITY) ? 0.0f : -mrow;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       pw[k] = pack2<QF>(fast_exp2(fmaf(sc[2 * k], c, nmu)), fast_exp2(fmaf(sc[2 * k + 1], c, nmu)));
