@@ -382,13 +382,15 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     }
     // (the NaN-propagating maximum is v_maximum3_f32 with no canonicalising
     // of its operands; the raw maximum is compared with the threshold
-    // (mrow + tau) / c, which only changes with mrow)
+    // (mrow + tau) / c, which only changes with mrow.  A row's two half-waves
+    // each test their own 16 scores: the row needs a new maximum exactly when
+    // one of them does, so the exchange of the halves' maxima waits for that.)
     float mx = sc[0];
 #pragma unroll
     for (int k = 1; k < 16; ++k) mx = __builtin_elementwise_maximum(mx, sc[k]);
-    mx = half_max(mx);
-    const bool need = mx > thr;
-    if (__any(need)) {
+    if (__any(mx > thr)) {
+      mx = half_max(mx);                       // the row's 32 scores
+      const bool need = mx > thr;
       const float mn = need ? fmaxf(mrow, mx * c) : mrow;
       const float alpha = (mrow == -INFINITY) ? 0.0f : fast_exp2(mrow - mn);
       mrow = mn;
