@@ -501,7 +501,9 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     auto dma = [&](uint8_t* dk, uint8_t* dv, int ida, int idb, int kb) __attribute__((always_inline)) {
       const int id = __builtin_amdgcn_readfirstlane(clamp_blk(dpage ? idb : ida));
       const uint64_t pg = (uint64_t)(uint32_t)id * (uint64_t)blk_stride;
-      const int bytes = __builtin_amdgcn_readfirstlane(min(max(n_valid - (kb + 16 * dpage), 0), 16) * 256);
+      // (clamped in two steps: as one min-max the compiler forms a vector med3)
+      const int rows = __builtin_amdgcn_readfirstlane(max(n_valid - (kb + 16 * dpage), 0));
+      const int bytes = min(rows, 16) * 256;
       __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(kpool + pg), (short)0, bytes, kBufferFlags);
       __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
