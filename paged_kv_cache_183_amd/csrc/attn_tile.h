@@ -146,6 +146,9 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   constexpr bool DMA = !PFX && !is_fp8(KF) && D == 128;
   __shared__ __attribute__((aligned(16))) uint8_t s_k[DMA ? 1 : 2][DMA ? 16 : KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[DMA ? 1 : 2][DMA ? 16 : VBUF];
+  // direct path: three stages of 16 KiB (K at +0, V at +8 KiB)
+  __shared__ __attribute__((aligned(16))) uint8_t d_s0[DMA ? 16384 : 16], d_s1[DMA ? 16384 : 16],
+      d_s2[DMA ? 16384 : 16];
   __shared__ int s_red[3];
 
   const int g = p.group;
@@ -242,34 +245,17 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     for (int t = 0; t < KS; ++t) qr[t] = *reinterpret_cast<const uint4*>(qp + 8 * t);
   }
 
-  // Over the workgroup's rows: the largest lower and the smallest and largest
-  // upper bounds.  A block inside every row's range needs no per-key mask;
-  // keys at or past every row's range are staged as zeros.
-  if (threadIdx.x == 0) {
-    s_red[0] = INT32_MIN;
-    s_red[1] = INT32_MAX;
-    s_red[2] = INT32_MIN;
-  }
-  __syncthreads();
-  if (row_ok && hf == 0) {
-    atomicMax(&s_red[0], r_lo);
-    atomicMin(&s_red[1], r_hi);
-    atomicMax(&s_red[2], r_hi);
-  }
-  __syncthreads();
-  const int max_lo = __builtin_amdgcn_readfirstlane(s_red[0]);
-  const int min_hi = __builtin_amdgcn_readfirstlane(s_red[1]);
-  const int n_valid = min(key_end, __builtin_amdgcn_readfirstlane(s_red[2]));
-  const int kb0 = (key_begin / kBK) * kBK;
-  const int nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
-  __builtin_amdgcn_s_waitcnt(0);               // (the Q loads)
-
-
   const int32_t* bt = p.block_tables + (int64_t)seq_tbl * p.bt_stride;
   const uint8_t* kpool = static_cast<const uint8_t*>(p.k_cache) + (int64_t)hk * kPageBytes;
   const uint8_t* vpool = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes;
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
-
+  // Keys of the block walk.  In prefill every row's range ends at or below
+  // key_end and the tile's last row reaches it, so n_valid = key_end is
+  // known before the reduction below; the direct path issues its first
+  // loads right away.  (The other paths take n_valid from the reduction.)
+  int n_valid = key_end;
+  int kb0 = (key_begin / kBK) * kBK;
+  int nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
   // Staging map (256 threads, one block = pages A and B of 16 rows), the same
   // for K and V: thread i stages chunk i % CH of block row i / CH and, for
   // D = 128, of the same row of page B as well (block row + 16); for D = 64
@@ -290,6 +276,87 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   auto clamp_blk = [&](int blk) __attribute__((always_inline)) {
     return (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
   };
+  // A barrier for LDS values only that leaves the loads into LDS in flight:
+  // this wave's LDS operations done (lgkmcnt(0)), then s_barrier.  (A
+  // workgroup fence on LDS would also wait for the loads that write LDS.)
+  auto lds_only_barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Direct path: the loads of one block into a stage (see the block loop)
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int dpage = wave >> 1;                 // the page this wave loads (uniform)
+  const int dhalf = wave & 1;
+  const int k_dma = l16 * 256 + lq * 16;       // + 16 c0
+  const int v_dma = lq * 256 + ((l16 ^ (4 * lq)) * 16);   // + 256 R0
+  auto dma = [&](uint8_t* dk, uint8_t* dv, int ida, int idb, int kb) __attribute__((always_inline)) {
+    const int id = __builtin_amdgcn_readfirstlane(clamp_blk(dpage ? idb : ida));
+    const uint64_t pg = (uint64_t)(uint32_t)id * (uint64_t)blk_stride;
+    // (clamped in two steps: as one min-max the compiler forms a vector med3)
+    const int rows = __builtin_amdgcn_readfirstlane(max(n_valid - (kb + 16 * dpage), 0));
+    const int bytes = min(rows, 16) * 256;
+    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kpool + pg), (short)0, bytes, kBufferFlags);
+    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(vpool + pg), (short)0, bytes, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c0 = 8 * dhalf + 4 * i;        // K chunks of this load
+      const int r0 = 8 * dhalf + 4 * i;        // V rows of this load
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(dk + dpage * 4096 + c0 * 256), 16,
+                                               k_dma, c0 * 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(dv + (16 * dpage + r0) * 256), 16,
+                                               v_dma, r0 * 256, 0, 0);
+    }
+  };
+  // the block ids of a block, read a block before its loads
+  auto ids_of = [&](int (&ids)[2], int kb) __attribute__((always_inline)) {
+    ids[0] = page_blk(kb >> 4);
+    ids[1] = page_blk((kb >> 4) + 1);
+  };
+  auto kb_of = [&](int bi) __attribute__((always_inline)) {
+    return kb0 + max(min(bi, nblk - 1), 0) * kBK;
+  };
+  int ids[2] = {0, 0};
+
+  // Over the workgroup's rows: the largest lower and the smallest and largest
+  // upper bounds.  A block inside every row's range needs no per-key mask;
+  // keys at or past every row's range are staged as zeros.
+  if (threadIdx.x == 0) {
+    s_red[0] = INT32_MIN;
+    s_red[1] = INT32_MAX;
+    s_red[2] = INT32_MIN;
+  }
+  if constexpr (DMA) lds_only_barrier(); else __syncthreads();
+  if (row_ok && hf == 0) {
+    atomicMax(&s_red[0], r_lo);
+    atomicMin(&s_red[1], r_hi);
+    atomicMax(&s_red[2], r_hi);
+  }
+  if constexpr (DMA) {
+    // blocks 0 and 1, unconditionally (with no block the loads have size 0);
+    // after the LDS atomics above, which would otherwise wait for them
+    int i0[2], i1[2];
+    ids_of(i0, kb_of(0));
+    ids_of(i1, kb_of(1));
+    dma(d_s0, d_s0 + 8192, i0[0], i0[1], kb_of(0));
+    dma(d_s1, d_s1 + 8192, i1[0], i1[1], kb_of(1));
+    ids_of(ids, kb_of(2));
+  }
+  if constexpr (DMA) lds_only_barrier(); else __syncthreads();
+  const int max_lo = __builtin_amdgcn_readfirstlane(s_red[0]);
+  const int min_hi = __builtin_amdgcn_readfirstlane(s_red[1]);
+  if constexpr (!DMA) {
+    n_valid = min(key_end, __builtin_amdgcn_readfirstlane(s_red[2]));
+    nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
+    __builtin_amdgcn_s_waitcnt(0);             // (the Q loads)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8): the Q loads (blocks 0 and 1 may fly)
+  }
+
   // Loads are unconditional (rows at or past n_valid are replaced by zeros
   // when written to LDS) so that nothing waits on them before the LDS write.
   // (the two block ids of a block are read one block ahead of its K/V)
@@ -454,7 +521,6 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // written to the other LDS buffer.  (A single-block loop body keeps the
   // accumulators in place; unrolling by two made the compiler copy them.)
   RawT kr[KPT], vr[KPT];
-  auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
   int ida = 0, idb = 0;                        // block ids of the block fetched next
   if (nblk > 0) {
     fetch(kr, vr, page_blk(kb_of(0) >> 4), page_blk((kb_of(0) >> 4) + 1));
@@ -491,38 +557,6 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     //    c ^ 4 (r % 4) -- load i of wave w covers rows 8 (w & 1) + 4 i .. + 3
     //    of page w >> 1; the transposing reads of two 16-lane groups then hit
     //    64 distinct banks.
-    __shared__ __attribute__((aligned(16))) uint8_t d_s0[16384], d_s1[16384], d_s2[16384];
-    typedef __attribute__((address_space(3))) void* lds_ptr;
-    const int l16 = lane & 15, lq = lane >> 4;
-    const int dpage = wave >> 1;                 // the page this wave loads (uniform)
-    const int dhalf = wave & 1;
-    const int k_dma = l16 * 256 + lq * 16;       // + 16 c0
-    const int v_dma = lq * 256 + ((l16 ^ (4 * lq)) * 16);   // + 256 R0
-    auto dma = [&](uint8_t* dk, uint8_t* dv, int ida, int idb, int kb) __attribute__((always_inline)) {
-      const int id = __builtin_amdgcn_readfirstlane(clamp_blk(dpage ? idb : ida));
-      const uint64_t pg = (uint64_t)(uint32_t)id * (uint64_t)blk_stride;
-      // (clamped in two steps: as one min-max the compiler forms a vector med3)
-      const int rows = __builtin_amdgcn_readfirstlane(max(n_valid - (kb + 16 * dpage), 0));
-      const int bytes = min(rows, 16) * 256;
-      __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(kpool + pg), (short)0, bytes, kBufferFlags);
-      __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(vpool + pg), (short)0, bytes, kBufferFlags);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c0 = 8 * dhalf + 4 * i;        // K chunks of this load
-        const int r0 = 8 * dhalf + 4 * i;        // V rows of this load
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(dk + dpage * 4096 + c0 * 256), 16,
-                                                 k_dma, c0 * 16, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(dv + (16 * dpage + r0) * 256), 16,
-                                                 v_dma, r0 * 256, 0, 0);
-      }
-    };
-    // the block ids of a block, read a block before its loads
-    auto ids_of = [&](int (&ids)[2], int kb) __attribute__((always_inline)) {
-      ids[0] = page_blk(kb >> 4);
-      ids[1] = page_blk((kb >> 4) + 1);
-    };
     const int kbase = (col >> 4) * 4096 + 8 * hf * 256 + (col & 15) * 16;
     const int vgq = lane >> 4, vj = (lane & 15) >> 2;
     const int vrow = (4 * (vgq >> 1) + vj) * 256 + 32 * (vgq & 1) + 8 * (lane & 3);
@@ -560,16 +594,6 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    auto kb_of = [&](int bi) __attribute__((always_inline)) { return kb0 + min(bi, nblk - 1) * kBK; };
-    int ids[2];
-    if (nblk > 0) {
-      int i0[2], i1[2];
-      ids_of(i0, kb_of(0));
-      ids_of(i1, kb_of(1));
-      dma(d_s0, d_s0 + 8192, i0[0], i0[1], kb_of(0));
-      dma(d_s1, d_s1 + 8192, i1[0], i1[1], kb_of(1));
-      ids_of(ids, kb_of(2));
-    }
     // step of block bi in stage S: its loads done (the next block's four may
     // still fly), this wave's reads of the stage loaded next done; barrier;
     // the loads of block bi + 2 into the stage block bi - 1 used; compute.
