@@ -17,8 +17,15 @@
 // offsets) and their table entries set to -1: keys t <= n - W with a sliding
 // window W, keys below floor(n / L) * L with chunked-local attention of L.
 //
-// Both run as one workgroup: the per-sequence counts are prefix-summed with a
-// block scan, then every thread writes the entries of its own sequences.
+// Both prefix-sum per-sequence counts with a block scan over the threads of
+// a workgroup.  The recycling runs as one workgroup; every thread writes the
+// entries of its own sequences.  The plan's tables are most of its output
+// (V rows of L / 16 entries), so it runs on several workgroups: each one
+// repeats the scan (a few loads per thread), describes its share of the
+// virtual rows in LDS and then writes their table entries, consecutive
+// threads on consecutive entries with several reads in flight per thread.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -26,7 +33,10 @@ namespace vp {
 
 namespace {
 
-constexpr int kLT = 1024;     // threads of the metadata workgroup
+constexpr int kLT = 1024;     // threads of a metadata workgroup
+constexpr int kRowBatch = 1024;    // virtual rows a plan workgroup describes in LDS at once
+constexpr int kCopyUnroll = 8;     // table entries in flight per thread
+constexpr int kPlanMaxGroups = 64;
 
 // Exclusive prefix of per-thread totals over the workgroup; returns this
 // thread's offset and writes the grand total to *total.
@@ -74,34 +84,73 @@ __global__ __launch_bounds__(kLT) void chunked_local_plan_kernel(LocalPlanParams
     if (qb > qa) cnt += (n - 1) / L - (n - (qb - qa)) / L + 1;
   }
   int64_t total = 0;
-  int64_t v = block_exclusive_scan(cnt, &total);
+  const int64_t v0 = block_exclusive_scan(cnt, &total);   // this thread's first row
   const int64_t V = p.num_virtual;
-  for (int i = 0; i < per; ++i) {
-    const int s = s0 + i;
-    if (s >= B) break;
-    int qa, qb, n;
-    seq(s, qa, qb, n);
-    if (qb <= qa) continue;
-    const int first = n - (qb - qa);            // position of the first query token
-    const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
-    for (int c = first / L; c <= (n - 1) / L; ++c, ++v) {
-      if (v >= V) break;
-      const int lo = max(first, c * L), hi = min(n - 1, c * L + L - 1);
-      const int vlen = hi + 1 - c * L;
-      p.v_query_start_loc[v] = qa + (lo - first);
-      p.v_context_lens[v] = vlen;
-      const int npg = (vlen + 15) / 16;
-      int32_t* row = p.v_block_tables + v * P;
-      for (int j = 0; j < P; ++j) row[j] = j < npg ? bt[c * P + j] : -1;
+  const int64_t used = min(total, V);
+  // this workgroup's rows [r0, r1), in batches of nb rows (nb P < 2^31)
+  const int64_t span = (V + gridDim.x - 1) / gridDim.x;
+  const int64_t r0 = min(V, (int64_t)blockIdx.x * span), r1 = min(V, r0 + span);
+  const int nb = max(1, min(kRowBatch, (1 << 30) / P));
+  __shared__ int64_t s_src[kRowBatch];          // block_tables offset of a row's first entry
+  __shared__ int s_npg[kRowBatch];              // the row's pages (0: an unused row)
+  for (int64_t b0 = r0; b0 < r1; b0 += nb) {
+    const int64_t b1 = min(r1, b0 + nb);
+    // unused virtual sequences: no rows, no keys
+    for (int64_t w = max(used, b0) + threadIdx.x; w < b1; w += kLT) {
+      p.v_query_start_loc[w] = sumq;
+      p.v_context_lens[w] = 0;
+      s_src[w - b0] = 0;
+      s_npg[w - b0] = 0;
     }
+    // the rows of this thread's sequences that fall in the batch
+    int64_t v = v0;
+    for (int i = 0; i < per && v < b1; ++i) {
+      const int s = s0 + i;
+      if (s >= B) break;
+      int qa, qb, n;
+      seq(s, qa, qb, n);
+      if (qb <= qa) continue;
+      const int first = n - (qb - qa);          // position of the first query token
+      const int c_first = first / L, c_last = (n - 1) / L;
+      if (v + (c_last - c_first + 1) <= b0) {   // all before the batch
+        v += c_last - c_first + 1;
+        continue;
+      }
+      for (int c = c_first; c <= c_last && v < b1; ++c, ++v) {
+        if (v < b0) continue;
+        const int lo = max(first, c * L), hi = min(n - 1, c * L + L - 1);
+        const int vlen = hi + 1 - c * L;
+        p.v_query_start_loc[v] = qa + (lo - first);
+        p.v_context_lens[v] = vlen;
+        s_src[v - b0] = (int64_t)s * p.bt_stride + (int64_t)c * P;
+        s_npg[v - b0] = (vlen + 15) / 16;
+      }
+    }
+    __syncthreads();
+    // their table entries: the slice of the sequence's table, -1 past the
+    // context (and for unused rows)
+    int32_t* dst = p.v_block_tables + b0 * P;
+    const uint32_t ne = (uint32_t)((b1 - b0) * P);
+    for (uint32_t e = threadIdx.x; e < ne; e += kCopyUnroll * kLT) {
+      int32_t x[kCopyUnroll];
+#pragma unroll
+      for (int k = 0; k < kCopyUnroll; ++k) {
+        const uint32_t ek = e + k * kLT;
+        x[k] = -1;
+        if (ek < ne) {
+          const uint32_t r = ek / (uint32_t)P, j = ek - r * (uint32_t)P;
+          if ((int)j < s_npg[r]) x[k] = p.block_tables[s_src[r] + j];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kCopyUnroll; ++k) {
+        const uint32_t ek = e + k * kLT;
+        if (ek < ne) dst[ek] = x[k];
+      }
+    }
+    __syncthreads();
   }
-  // unused virtual sequences: no rows, no keys
-  for (int64_t w = min(total, V) + threadIdx.x; w < V; w += kLT) {
-    p.v_query_start_loc[w] = sumq;
-    p.v_context_lens[w] = 0;
-    for (int j = 0; j < P; ++j) p.v_block_tables[w * P + j] = -1;
-  }
-  if (threadIdx.x == 0) p.v_query_start_loc[V] = sumq;
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.v_query_start_loc[V] = sumq;
 }
 
 __global__ __launch_bounds__(kLT) void recycle_pages_kernel(RecycleParams p) {
@@ -141,7 +190,11 @@ __global__ __launch_bounds__(kLT) void recycle_pages_kernel(RecycleParams p) {
 }
 
 hipError_t launch_chunked_local_plan(const LocalPlanParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(chunked_local_plan_kernel, dim3(1), dim3(kLT), 0, stream, p);
+  // about kCopyUnroll table entries per thread, at most one workgroup per row
+  const int64_t entries = p.num_virtual * (int64_t)(p.chunk / 16);
+  int64_t groups = (entries + (int64_t)kCopyUnroll * kLT - 1) / ((int64_t)kCopyUnroll * kLT);
+  groups = std::max<int64_t>(1, std::min<int64_t>({groups, (int64_t)kPlanMaxGroups, p.num_virtual}));
+  hipLaunchKernelGGL(chunked_local_plan_kernel, dim3((unsigned)groups), dim3(kLT), 0, stream, p);
   return hipGetLastError();
 }
 

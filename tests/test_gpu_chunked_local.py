@@ -29,9 +29,9 @@ def random_meta(seed, B, chunk, qmax=300, cmax=900, zero_q=True):
     return qsl, n.astype(np.int32), bt
 
 
-def run_plan(qsl, ctx, bt, chunk):
+def run_plan(qsl, ctx, bt, chunk, spare=0):
     B = len(ctx)
-    V = P.vllm_paged_chunked_local_virtual_count(B, int(qsl[-1]), chunk)
+    V = P.vllm_paged_chunked_local_virtual_count(B, int(qsl[-1]), chunk) + spare
     vq = torch.full((V + 1,), -7, dtype=torch.int32, device=DEV)
     vc = torch.full((V,), -7, dtype=torch.int32, device=DEV)
     vb = torch.full((V, chunk // 16), -7, dtype=torch.int32, device=DEV)
@@ -46,6 +46,20 @@ def run_plan(qsl, ctx, bt, chunk):
 def test_plan_bit_exact(chunk, B, seed):
     qsl, ctx, bt = random_meta(seed, B, chunk, qmax=200 if B > 100 else 700)
     V, vq, vc, vb = run_plan(qsl, ctx, bt, chunk)
+    wq, wc, wb = A.chunked_local_plan(qsl, ctx, bt, chunk, V)
+    assert np.array_equal(vq.cpu().numpy(), wq)
+    assert np.array_equal(vc.cpu().numpy(), wc)
+    assert np.array_equal(vb.cpu().numpy(), wb)
+
+
+@pytest.mark.parametrize("chunk,B,spare", [(16, 2500, 3000), (48, 300, 37), (8192, 40, 700)])
+def test_plan_spare_rows(chunk, B, spare):
+    """More virtual sequences than the batch needs: the spare ones get no
+    rows, context 0 and -1 tables.  The rows are split over several
+    workgroups of the plan (up to 64) and, for chunk 16, over several
+    batches of rows within a workgroup."""
+    qsl, ctx, bt = random_meta(40 + B, B, chunk, qmax=200 if B > 100 else 700)
+    V, vq, vc, vb = run_plan(qsl, ctx, bt, chunk, spare=spare)
     wq, wc, wb = A.chunked_local_plan(qsl, ctx, bt, chunk, V)
     assert np.array_equal(vq.cpu().numpy(), wq)
     assert np.array_equal(vc.cpu().numpy(), wc)
