@@ -18,8 +18,10 @@
 // window W, keys below floor(n / L) * L with chunked-local attention of L.
 //
 // Both prefix-sum per-sequence counts with a block scan over the threads of
-// a workgroup.  The recycling runs as one workgroup; every thread writes the
-// entries of its own sequences.  The plan's tables are most of its output
+// a workgroup.  The recycling runs as one workgroup: a wave per sequence
+// counts the live entries of its dead pages (coalesced reads), the scan turns
+// the counts into offsets, and a wave per sequence writes its entries in
+// table order (a ballot and a bit count per 64 entries).  The plan's tables are most of its output
 // (V rows of L / 16 entries), so it runs on several workgroups: each one
 // repeats the scan (a few loads per thread), describes its share of the
 // virtual rows in LDS and then writes their table entries, consecutive
@@ -154,9 +156,10 @@ __global__ __launch_bounds__(kLT) void chunked_local_plan_kernel(LocalPlanParams
 }
 
 __global__ __launch_bounds__(kLT) void recycle_pages_kernel(RecycleParams p) {
+  constexpr int kWaves = kLT / 64;
+  constexpr int kU = 4;                         // 64-entry pieces read at once per wave
   const int B = p.num_seqs;
-  const int per = (B + kLT - 1) / kLT;
-  const int s0 = threadIdx.x * per;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   auto dead_of = [&](int s) __attribute__((always_inline)) {
     const int n = max(p.context_lens[s], 0);
     int dead = 0;
@@ -164,29 +167,71 @@ __global__ __launch_bounds__(kLT) void recycle_pages_kernel(RecycleParams p) {
     if (p.chunk > 0) dead = max(dead, (n / p.chunk) * p.chunk);
     return min(max(dead, 0) / 16, p.bt_stride);
   };
+  // live entries among each sequence's dead pages, into freed_offsets[s]
+  for (int s = wave; s < B; s += kWaves) {
+    const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
+    const int d = dead_of(s);
+    int c = 0;
+    for (int j0 = 0; j0 < d; j0 += 64 * kU) {
+      int32_t x[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int j = j0 + 64 * k + lane;
+        x[k] = j < d ? bt[j] : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kU; ++k) c += x[k] >= 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0) p.freed_offsets[s] = c;
+  }
+  __syncthreads();
+  // the counts become offsets (each thread a run of consecutive sequences)
+  const int per = (B + kLT - 1) / kLT;
+  const int s0 = threadIdx.x * per;
   int64_t cnt = 0;
   for (int i = 0; i < per; ++i) {
     const int s = s0 + i;
     if (s >= B) break;
-    const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
-    const int d = dead_of(s);
-    for (int j = 0; j < d; ++j) cnt += bt[j] >= 0;
+    cnt += p.freed_offsets[s];
   }
   int64_t total = 0;
   int64_t off = block_exclusive_scan(cnt, &total);
   for (int i = 0; i < per; ++i) {
     const int s = s0 + i;
     if (s >= B) break;
-    int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
+    const int c = p.freed_offsets[s];
     p.freed_offsets[s] = (int32_t)off;
-    const int d = dead_of(s);
-    for (int j = 0; j < d; ++j) {
-      if (bt[j] < 0) continue;                  // recycled before
-      p.freed_pages[off++] = bt[j];
-      bt[j] = -1;
-    }
+    off += c;
   }
   if (threadIdx.x == 0) p.freed_offsets[B] = (int32_t)total;
+  __syncthreads();
+  // the entries: reported in table order, then set to -1 (entries already
+  // -1 were recycled before)
+  for (int s = wave; s < B; s += kWaves) {
+    int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
+    const int d = dead_of(s);
+    int o = p.freed_offsets[s];
+    for (int j0 = 0; j0 < d; j0 += 64 * kU) {
+      int32_t x[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int j = j0 + 64 * k + lane;
+        x[k] = j < d ? bt[j] : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const bool keep = x[k] >= 0;
+        const uint64_t m = __ballot(keep);
+        if (keep) {
+          p.freed_pages[o + __popcll(m & ((1ull << lane) - 1))] = x[k];
+          bt[j0 + 64 * k + lane] = -1;
+        }
+        o += __popcll(m);
+      }
+    }
+  }
 }
 
 hipError_t launch_chunked_local_plan(const LocalPlanParams& p, hipStream_t stream) {

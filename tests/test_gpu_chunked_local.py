@@ -197,6 +197,22 @@ def test_recycle_bit_exact(window, chunk, B):
     assert np.array_equal(nb2, nb) and not off2.any()
 
 
+@pytest.mark.parametrize("window,chunk", [(16, 0), (0, 16), (3000, 1024)])
+def test_recycle_long_tables(window, chunk):
+    """Tables of 700 pages (up to 690 dead ones per sequence: several
+    rounds of 256 entries per wave), a third of the entries already -1."""
+    g = np.random.default_rng(5000 + window + chunk)
+    B, mb = 50, 700
+    ctx = g.integers(0, 11200, B).astype(np.int32)
+    bt = g.integers(0, 50000, (B, mb)).astype(np.int32)
+    bt[g.random((B, mb)) < 0.33] = -1
+    nb, off, pages = run_recycle(ctx, bt, window, chunk)
+    wb, woff, wpages = expected_recycle(ctx, bt, window, chunk)
+    assert np.array_equal(nb, wb)
+    assert np.array_equal(off, woff)
+    assert np.array_equal(pages[:woff[-1]], wpages)
+
+
 def test_recycle_empty_batch():
     nb, off, _ = run_recycle(np.zeros(0, np.int32), np.zeros((0, 4), np.int32), 16, 0)
     assert off.tolist() == [0]
