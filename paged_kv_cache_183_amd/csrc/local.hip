@@ -41,22 +41,31 @@ constexpr int kCopyUnroll = 8;     // table entries in flight per thread
 constexpr int kPlanMaxGroups = 64;
 
 // Exclusive prefix of per-thread totals over the workgroup; returns this
-// thread's offset and writes the grand total to *total.
+// thread's offset and writes the grand total to *total.  Each wave scans its
+// 64 values with lane shifts, then every thread adds the totals of the waves
+// before its own (two barriers).
 __device__ int64_t block_exclusive_scan(int64_t v, int64_t* total) {
-  __shared__ int64_t s[kLT];
-  const int t = threadIdx.x;
-  s[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kLT; off <<= 1) {        // inclusive Hillis-Steele scan
-    const int64_t a = t >= off ? s[t - off] : 0;
-    __syncthreads();
-    s[t] += a;
-    __syncthreads();
+  constexpr int kW = kLT / 64;
+  __shared__ int64_t s_w[kW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int64_t x = v;                                 // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  *total = s[kLT - 1];
-  const int64_t ex = t > 0 ? s[t - 1] : 0;
+  if (lane == 63) s_w[w] = x;
   __syncthreads();
-  return ex;
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kW; ++i) {
+    const int64_t t = s_w[i];
+    before += i < w ? t : 0;
+    all += t;
+  }
+  *total = all;
+  __syncthreads();                               // (s_w is reused by the next call)
+  return before + x - v;
 }
 
 }  // namespace
