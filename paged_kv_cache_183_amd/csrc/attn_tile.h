@@ -149,7 +149,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   // direct path: three stages of 16 KiB (K at +0, V at +8 KiB)
   __shared__ __attribute__((aligned(16))) uint8_t d_s0[DMA ? 16384 : 16], d_s1[DMA ? 16384 : 16],
       d_s2[DMA ? 16384 : 16];
-  __shared__ int s_red[3];
+  __shared__ int s_red[PFX ? 3 * kPW : 1];    // per-wave row bounds (shared prefix)
 
   const int g = p.group;
   const int lane = threadIdx.x & 63;
@@ -184,6 +184,7 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   int hk, seq_tbl;                             // kv-head, sequence whose table is read
   int key_begin, key_end;                      // keys of this workgroup, before row ranges
   int r_lo, r_hi;                              // this row's kept keys [r_lo, r_hi)
+  int max_lo = 0, min_hi = 0;                  // over the workgroup's rows (see below)
   bool row_ok;
   bool wave_on;                                // some row of this wave is valid (uniform)
   int64_t q_off;                               // element offset of this row in q (and out)
@@ -211,6 +212,10 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
     r_lo = p.window > 0 ? max(0, ppos - p.window + 1) : 0;
     key_begin = p.window > 0 ? max(0, pos0 - p.window + 1) : 0;
     key_end = pos0 + nt;
+    // the rows are the positions pos0 .. pos0 + nt - 1 (each for g heads): the
+    // largest lower bound is the last token's, the smallest upper the first's
+    max_lo = p.window > 0 ? max(0, pos0 + nt - p.window) : 0;
+    min_hi = pos0 + 1;
     q_off = ((int64_t)(q_begin + q0 + tok) * p.num_q_heads + hk * g + head) * D;
   } else {
     hk = u / p.num_splits;
@@ -234,8 +239,8 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   }
 
   // Q operand: lane (row, hf) holds d = D/2 hf + 8 t + i for k-step t.  The
-  // loads are in flight during the reduction below and waited for after it:
-  // once that wait has been seen, the block loop need not wait for them (the
+  // loads are in flight during the setup below (block ids, the first loads,
+  // the shared prefix's row bounds) and waited for at its end: once that wait has been seen, the block loop need not wait for them (the
   // memory counter cannot tell them from the next block's loads, so an
   // in-loop wait for Q would wait for those every block).
   uint4 qr[KS];
@@ -250,9 +255,8 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   const uint8_t* vpool = static_cast<const uint8_t*>(p.v_cache) + (int64_t)hk * kPageBytes;
   const int64_t blk_stride = (int64_t)p.num_kv_heads * kPageBytes;
   // Keys of the block walk.  In prefill every row's range ends at or below
-  // key_end and the tile's last row reaches it, so n_valid = key_end is
-  // known before the reduction below; the direct path issues its first
-  // loads right away.  (The other paths take n_valid from the reduction.)
+  // key_end and the tile's last row reaches it, so n_valid = key_end; the
+  // shared prefix takes it from the reduction of its rows' bounds below.
   int n_valid = key_end;
   int kb0 = (key_begin / kBK) * kBK;
   int nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
@@ -275,15 +279,6 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
   };
   auto clamp_blk = [&](int blk) __attribute__((always_inline)) {
     return (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
-  };
-  // A barrier for LDS values only that leaves the loads into LDS in flight:
-  // this wave's LDS operations done (lgkmcnt(0)), then s_barrier.  (A
-  // workgroup fence on LDS would also wait for the loads that write LDS.)
-  auto lds_only_barrier = []() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
   };
   // Direct path: the loads of one block into a stage (see the block loop)
   typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -324,37 +319,49 @@ __device__ __forceinline__ void attn_tile_body(const PrefillParams& p, const int
 
   // Over the workgroup's rows: the largest lower and the smallest and largest
   // upper bounds.  A block inside every row's range needs no per-key mask;
-  // keys at or past every row's range are staged as zeros.
-  if (threadIdx.x == 0) {
-    s_red[0] = INT32_MIN;
-    s_red[1] = INT32_MAX;
-    s_red[2] = INT32_MIN;
-  }
-  if constexpr (DMA) lds_only_barrier(); else __syncthreads();
-  if (row_ok && hf == 0) {
-    atomicMax(&s_red[0], r_lo);
-    atomicMin(&s_red[1], r_hi);
-    atomicMax(&s_red[2], r_hi);
+  // keys at or past every row's range are staged as zeros.  Prefill takes
+  // them from its first and last token (above).  Shared-prefix rows belong to
+  // different sequences: each wave reduces its rows by lane exchanges (both
+  // half-waves hold the same rows), then the waves' bounds meet in LDS.
+  if constexpr (PFX) {
+    int a = row_ok ? r_lo : INT32_MIN, m = row_ok ? r_hi : INT32_MAX, x = row_ok ? r_hi : INT32_MIN;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      a = max(a, __shfl_xor(a, o));
+      m = min(m, __shfl_xor(m, o));
+      x = max(x, __shfl_xor(x, o));
+    }
+    if (lane == 0) {
+      s_red[3 * wave] = a;
+      s_red[3 * wave + 1] = m;
+      s_red[3 * wave + 2] = x;
+    }
+    __syncthreads();
+    int max_hi = INT32_MIN;
+    max_lo = INT32_MIN;
+    min_hi = INT32_MAX;
+#pragma unroll
+    for (int w = 0; w < kPW; ++w) {
+      max_lo = max(max_lo, s_red[3 * w]);
+      min_hi = min(min_hi, s_red[3 * w + 1]);
+      max_hi = max(max_hi, s_red[3 * w + 2]);
+    }
+    max_lo = __builtin_amdgcn_readfirstlane(max_lo);
+    min_hi = __builtin_amdgcn_readfirstlane(min_hi);
+    n_valid = min(key_end, __builtin_amdgcn_readfirstlane(max_hi));
+    nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
   }
   if constexpr (DMA) {
-    // blocks 0 and 1, unconditionally (with no block the loads have size 0);
-    // after the LDS atomics above, which would otherwise wait for them
+    // blocks 0 and 1, unconditionally (with no block the loads have size 0)
     int i0[2], i1[2];
     ids_of(i0, kb_of(0));
     ids_of(i1, kb_of(1));
     dma(d_s0, d_s0 + 8192, i0[0], i0[1], kb_of(0));
     dma(d_s1, d_s1 + 8192, i1[0], i1[1], kb_of(1));
     ids_of(ids, kb_of(2));
-  }
-  if constexpr (DMA) lds_only_barrier(); else __syncthreads();
-  const int max_lo = __builtin_amdgcn_readfirstlane(s_red[0]);
-  const int min_hi = __builtin_amdgcn_readfirstlane(s_red[1]);
-  if constexpr (!DMA) {
-    n_valid = min(key_end, __builtin_amdgcn_readfirstlane(s_red[2]));
-    nblk = n_valid > key_begin ? ((n_valid - 1) / kBK - kb0 / kBK + 1) : 0;
-    __builtin_amdgcn_s_waitcnt(0);             // (the Q loads)
-  } else {
     __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8): the Q loads (blocks 0 and 1 may fly)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);             // (the Q loads)
   }
 
   // Loads are unconditional (rows at or past n_valid are replaced by zeros
