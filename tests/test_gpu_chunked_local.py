@@ -67,16 +67,18 @@ def test_plan_spare_rows(chunk, B, spare):
 
 
 def test_plan_empty_and_degenerate():
-    # no sequences; only Q = 0 sequences; one token at a chunk boundary
+    # no sequences; only Q = 0 sequences; one token at a chunk boundary; each
+    # also with 5 spare virtual sequences
     for qsl, ctx in (([0], []), ([0, 0, 0], [5, 0]), ([0, 1], [33]), ([0, 2], [33])):
         qsl, ctx = np.array(qsl, np.int32), np.array(ctx, np.int32)
         bt = np.arange(max(len(ctx), 1) * 4, dtype=np.int32).reshape(-1, 4)[:len(ctx)]
         bt = bt if len(ctx) else np.zeros((0, 4), np.int32)
-        V, vq, vc, vb = run_plan(qsl, ctx, bt, 32)
-        wq, wc, wb = A.chunked_local_plan(qsl, ctx, bt, 32, V)
-        assert np.array_equal(vq.cpu().numpy(), wq)
-        assert np.array_equal(vc.cpu().numpy(), wc)
-        assert np.array_equal(vb.cpu().numpy(), wb)
+        for spare in (0, 5):
+            V, vq, vc, vb = run_plan(qsl, ctx, bt, 32, spare=spare)
+            wq, wc, wb = A.chunked_local_plan(qsl, ctx, bt, 32, V)
+            assert np.array_equal(vq.cpu().numpy(), wq)
+            assert np.array_equal(vc.cpu().numpy(), wc)
+            assert np.array_equal(vb.cpu().numpy(), wb)
 
 
 def prefill_virtual(case, kc, vc, chunk, ks=None, vs=None):
