@@ -272,9 +272,18 @@ __global__ __launch_bounds__(kBT) void bm_schedule_kernel(BmScheduleParams p) {
     if (lo >= nf) continue;
     uint64_t h = lo == 0 ? kSeed : S.chash[rows[r * MB + lo - 1]];
     uint64_t* w = p.ws_hash + r * MB;
-    for (int j = lo; j < nf; ++j) {
-      h = h * kBase16 + w[j];
-      w[j] = h;
+    // (eight blocks' hashes read before any is chained: one memory round
+    // trip per eight blocks of a long prompt, not one per block)
+    for (int j0 = lo; j0 < nf; j0 += 8) {
+      uint64_t x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = j0 + k < nf ? w[j0 + k] : 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (j0 + k < nf) {
+          h = h * kBase16 + x[k];
+          w[j0 + k] = h;
+        }
     }
   }
   __syncthreads();
