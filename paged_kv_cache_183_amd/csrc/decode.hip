@@ -102,18 +102,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a), bitcast<bf16x2_t>(b), c, false);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
 // Kept key range of a decode query and its page range.
 struct SeqRange {
   int n, lo, lo_page, np;   // np = pages of the kept range (0 if n <= 0)
@@ -136,10 +124,6 @@ __device__ __forceinline__ SeqRange seq_range_of(const DecodeParams& p, int ctx)
   r.lo_page = r.lo >> 4;
   r.np = ((r.n + 15) >> 4) - r.lo_page;
   return r;
-}
-
-__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int s) {
-  return seq_range_of(p, p.context_lens[s]);
 }
 
 // Exclusive prefix of np(s) over the batch, computed by one workgroup of
