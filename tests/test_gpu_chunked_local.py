@@ -10,7 +10,7 @@ from oracle import attention as A
 from workloads import make_case, raw_bits
 
 from _util import oracle_pools
-from _gpu import gpu_fill, gpu_decode, to_f64, pool_view, assert_close, dev_scale, DEV
+from _gpu import gpu_fill, gpu_decode, to_f64, pool_view, assert_close, DEV
 
 pytestmark = pytest.mark.gpu
 

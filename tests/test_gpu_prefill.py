@@ -5,7 +5,6 @@ element by element with the oracle (max-abs 2e-3 fp16, 8e-3 bf16, plus half
 an ulp of the output format); the
 properties that the kernel's arithmetic order makes exact (page permutation,
 table padding, causality) are checked bit for bit."""
-import numpy as np
 import pytest
 import torch
 

@@ -5,7 +5,6 @@ sequence's context through its block table).
 Bars: element by element within the stated tolerances plus half an ulp of
 the output format; properties the arithmetic order makes exact are
 checked bit for bit."""
-import numpy as np
 import pytest
 import torch
 

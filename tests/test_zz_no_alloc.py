@@ -6,7 +6,6 @@ for bit; each is also checked against the fp64 oracle within the stated
 tolerance plus half an output ulp.  Two calls in a row on the library's one
 scratch array, the second with a smaller batch, show that the array needs no
 clearing between calls."""
-import numpy as np
 import pytest
 import torch
 
