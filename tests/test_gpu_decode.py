@@ -229,6 +229,30 @@ def test_heads_dims_dtypes(hq, hkv, d, kvq):
     check_decode(case, gpu_decode(case, kc, vc, partition=128), kp, vp)
 
 
+DEC_HEADS = [(1, 1), (4, 1), (8, 2), (10, 2), (32, 8), (40, 8), (16, 1), (6, 3), (5, 5), (24, 2)]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_decode_random_shapes(seed):
+    """Seeded random decode shapes through the automatic or a fixed split:
+    1 to 40 sequences, head groupings of 1 to 16, D = 64 or 128, f16, bf16,
+    E4M3 or E5M2 pools, windows of 0 to 2,000, contexts of 1 to 3,000
+    tokens, partitions automatic or 16 to 1,024 tokens."""
+    r = np.random.RandomState(3000 + seed)
+    hq, hkv = DEC_HEADS[r.randint(len(DEC_HEADS))]
+    kv = ["f16", "bf16", "e4m3", "e5m2"][r.randint(4)]
+    qd = kv if kv in ("f16", "bf16") else ["f16", "bf16"][r.randint(2)]
+    over = dict(B=int(r.randint(1, 41)), ctx_range=(1, int(r.randint(2, 3001))), Hq=hq, Hkv=hkv,
+                D=[64, 128][r.randint(2)], kv=kv, q=qd, window=[0, 0, 16, 333, 2000][r.randint(5)])
+    if kv in ("e4m3", "e5m2"):
+        over.update(kv_src=qd, k_scale=0.05, v_scale=0.07)
+    case = make_case(1, seed=4000 + seed, **over)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    part = [0, 0, 16, 48, 512, 1024][r.randint(6)]
+    check_decode(case, gpu_decode(case, kc, vc, partition=part), kp, vp)
+
+
 def test_zero_and_clipped_context():
     case = make_case(1, B=4, ctx_range=(20, 90))
     kc, vc = gpu_fill(case)

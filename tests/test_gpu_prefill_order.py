@@ -143,3 +143,36 @@ def test_prefill_random_shapes(seed):
     kp, vp = oracle_pools(case)
     assert_close(case, to_f64(run_prefill(case, kc, vc, max_query_len=mq)),
                  oracle_prefill(case, kp, vp))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_random_shapes_fp8(seed):
+    """The same sweep over E4M3 and E5M2 pools (register staging, codes
+    converted exactly to q's format, the K scale folded into the score scale
+    and the V scale into the output), with per-tensor scales."""
+    import numpy as np
+    from oracle import attention as A
+    from workloads import raw_bits
+    from _gpu import dev_scale
+    r = np.random.RandomState(1100 + seed)
+    hq, hkv = SWEEP_HEADS[r.randint(len(SWEEP_HEADS))]
+    qd = ["bf16", "f16"][r.randint(2)]
+    kv = ["e4m3", "e5m2"][r.randint(2)]
+    case = make_case(4, seed=2100 + seed, B=int(r.randint(1, 121)),
+                     qlen_range=(0, int(r.randint(1, 151))), cached_range=(0, int(r.randint(0, 301))),
+                     Hq=hq, Hkv=hkv, D=[64, 128][r.randint(2)], kv=kv, q=qd, kv_src=qd,
+                     window=[0, 16, 100, 1000][r.randint(4)])
+    ks, vs = 0.05, 0.07
+    mq = max(case.max_query_len, 1) * [1, 8, 64][r.randint(3)]
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    q = case.q.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    P.vllm_paged_attn_prefill(out, q, pool_view(kc, kv), pool_view(vc, kv),
+                              case.block_tables.to(DEV), case.query_start_loc.to(DEV),
+                              case.context_lens.to(DEV), mq, case.scale, case.window,
+                              k_scale=dev_scale(ks), v_scale=dev_scale(vs))
+    ref = A.prefill(raw_bits(case.q), qd, kp, vp, kv, case.block_tables.numpy(),
+                    case.query_start_loc.numpy(), case.context_lens.numpy(), case.scale,
+                    case.window, np.array(ks), np.array(vs))
+    assert_close(case, to_f64(out), ref)
