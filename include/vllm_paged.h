@@ -152,7 +152,8 @@ const char* vllm_last_error(void);
  *   k_cache, v_cache [num_blocks, Hkv, 16, D]  the input's dtype, FP8_E4M3 or FP8_E5M2
  *   opts         nullable; k_scale / v_scale (or per-head k_scales / v_scales)
  *                used for FP8 pools only
- * Supported: D a multiple of 8, D <= 512.  T = 0 is a no-op.
+ * Supported: D a multiple of 8, D <= 512, T * Hkv * D / 8 below 2^31.
+ * T = 0 is a no-op.
  */
 vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
                                    const vllm_tensor* slot_mapping,

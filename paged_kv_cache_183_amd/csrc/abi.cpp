@@ -291,7 +291,9 @@ vllm_status vllm_paged_cache_write(const vllm_tensor* k, const vllm_tensor* v,
   VP_TRY(check_dtype(v_cache, "v_cache", k_cache->dtype));
   if (D % 8 != 0 || D > 512 || D == 0)
     return fail(VLLM_ERR_UNSUPPORTED, "head_dim %lld: must be a positive multiple of 8, <= 512", (long long)D);
-  if ((double)T * (double)Hkv * (double)(D / 8) >= 4294967295.0)
+  // (items of 8 elements below 2^31: the kernel's 32-bit item indices,
+  // its unrolled strides included, never wrap)
+  if ((double)T * (double)Hkv * (double)(D / 8) >= 2147483648.0)
     return fail(VLLM_ERR_UNSUPPORTED, "too many tokens for one call");
   const bool to_fp8 = is_fp8_dtype(k_cache->dtype);
   float ks = 1.0f, vs = 1.0f;
