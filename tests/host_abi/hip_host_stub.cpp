@@ -93,7 +93,7 @@ hipError_t hipFreeAsync(void* p, hipStream_t) {
   std::free(p);
   return hipSuccess;
 }
-// The library's scratch array is a host array of this size in this build.
+// The library's scratch array is a host array of this size in the host-only test.
 hipError_t hipGetSymbolAddress(void** p, const void* sym) {
   *p = const_cast<void*>(sym);
   stub_register(*p, VLLM_PAGED_NOALLOC_SCRATCH_BYTES);

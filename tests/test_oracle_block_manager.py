@@ -162,7 +162,7 @@ class Checked:
                     assert s // 16 == bt[r, t // 16] and s % 16 == t % 16
         # LRU and closure
         # (an evicted block may be allocated again and cached under a new
-        # prefix in the same call: judge by the entry it had before)
+        # prefix in the same call: decide by the entry it had before)
         survived = lambda b: m.index.get(int(before["chash"][b])) == b  # noqa: E731
         dropped = [b for b in range(self.N) if before["cached"][b] and not survived(b)]
         if dropped:
