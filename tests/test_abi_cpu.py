@@ -67,6 +67,27 @@ def test_cache_write_validation():
     P.vllm_paged_cache_write(k[:0], k[:0], sl[:0], _pool(), _pool(), stream=0)
 
 
+def test_cache_write_item_limit():
+    """A call of 2^31 or more 8-element items is refused before any pointer
+    is touched: here 2^28 tokens x 2 heads x 64 (2^32 items), described
+    with contiguous strides over a small host buffer."""
+    k = torch.zeros(4, 2, 64, dtype=torch.float16)
+    sl = torch.zeros(4, dtype=torch.int64)
+    T = 1 << 28
+    kd, vd, sd = Bd.tensor_desc(k), Bd.tensor_desc(k), Bd.tensor_desc(sl)
+    for d in (kd, vd):
+        d.shape[0] = T
+    sd.shape[0] = T
+    pool = _pool()
+    kc, vc = Bd.tensor_desc(pool), Bd.tensor_desc(pool.clone())
+    o = Bd.VllmAttnOpts()
+    st = Bd.LIB.vllm_paged_cache_write(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(sd),
+                                       ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(o),
+                                       ctypes.c_void_p(0))
+    assert st == Bd.VLLM_ERR_UNSUPPORTED
+    assert b"too many tokens" in Bd.LIB.vllm_last_error()
+
+
 def _decode_args(B=2, Hq=4, Hkv=2, D=64, dt=torch.float16, kvdt=None, mb=3):
     q = torch.zeros(B, Hq, D, dtype=dt)
     kv = _pool(h=Hkv, d=D, dt=kvdt or dt)
