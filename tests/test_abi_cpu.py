@@ -119,6 +119,16 @@ def test_decode_validation():
             **{**d, "partition_size": 512, "workspace": torch.zeros(8, dtype=torch.uint8)})
 
 
+def test_decode_work_unit_limit():
+    """At most 131,072 work units per call: 16,384 sequences x 8 kv-heads
+    (g = 1) pass the size checks and stop only at the host pointers; one
+    sequence more is refused as unsupported before any pointer is read."""
+    _expect(Bd.VLLM_ERR_DEVICE_PTR, P.vllm_paged_attn_decode,
+            **_decode_args(B=16384, Hq=8, Hkv=8, mb=1))
+    _expect(Bd.VLLM_ERR_UNSUPPORTED, P.vllm_paged_attn_decode,
+            **_decode_args(B=16385, Hq=8, Hkv=8, mb=1))
+
+
 def test_noalloc_decode_validation():
     """The allocation-free decode checks everything on the host before it
     looks up its scratch: a caller workspace is refused, sizes beyond the

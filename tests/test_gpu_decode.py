@@ -253,6 +253,18 @@ def test_decode_random_shapes(seed):
     check_decode(case, gpu_decode(case, kc, vc, partition=part), kp, vp)
 
 
+def test_decode_at_work_unit_limit():
+    """131,072 work units, the most one call takes (16,384 sequences x 8
+    kv-heads, g = 1), contexts of 1 to 40 tokens: every element against the
+    oracle, with the automatic split and with 32-token partitions."""
+    case = make_case(1, seed=77, B=16384, ctx_range=(1, 40), Hq=8, Hkv=8, D=64)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    ref = oracle_decode(case, kp, vp)
+    for part in (0, 32):
+        assert_close(case, to_f64(gpu_decode(case, kc, vc, partition=part)), ref)
+
+
 def test_zero_and_clipped_context():
     case = make_case(1, B=4, ctx_range=(20, 90))
     kc, vc = gpu_fill(case)
