@@ -265,6 +265,18 @@ def test_decode_at_work_unit_limit():
         assert_close(case, to_f64(gpu_decode(case, kc, vc, partition=part)), ref)
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (128, 1), (96, 4), (40, 1)])
+def test_decode_large_groups(hq, hkv):
+    """Large head groups, split into head chunks of at most 8 (g = 32, 128,
+    24 and 40: chunks of 8, 8, 8 and 8), with the automatic split and
+    32-token partitions."""
+    case = make_case(1, seed=600 + hq, B=5, ctx_range=(1, 900), Hq=hq, Hkv=hkv, D=128)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    for part in (0, 32):
+        check_decode(case, gpu_decode(case, kc, vc, partition=part), kp, vp)
+
+
 def test_zero_and_clipped_context():
     case = make_case(1, B=4, ctx_range=(20, 90))
     kc, vc = gpu_fill(case)

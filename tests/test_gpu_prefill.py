@@ -60,6 +60,20 @@ def test_prefill_heads_dtypes(hq, hkv, qd):
     check_all_rows(case, run_prefill(case, kc, vc), kp, vp)
 
 
+@pytest.mark.parametrize("hq,hkv", [(3, 1), (14, 2), (32, 1), (128, 1), (256, 2)])
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_extreme_groups(hq, hkv, d):
+    """Head groups whose rows do not fill a tile by whole tokens (g = 3 and
+    7: 42 and 18 tokens, 126 rows each) and large groups up to the largest
+    supported, g = 128 (one token per tile); windows on half of them."""
+    qd = "bf16" if d == 128 else "f16"
+    case = make_case(4, seed=450 + hq + d, B=4, qlen_range=(1, 70), cached_range=(0, 250),
+                     Hq=hq, Hkv=hkv, D=d, kv=qd, q=qd, window=40 if hq % 3 == 2 else 0)
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    check_all_rows(case, run_prefill(case, kc, vc), kp, vp)
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (4, 1), (10, 2), (64, 8), (32, 8)])
 @pytest.mark.parametrize("qd", ["bf16", "f16"])
 def test_prefill_head_dim_64(hq, hkv, qd):
