@@ -71,10 +71,12 @@ def test_shared_prefix_dtypes(kvq):
     assert_close(case, to_f64(shared_decode(case, kc, vc, 16)), oracle(case, kp, vp))
 
 
-@pytest.mark.parametrize("shared_pages", [1, 5, 15, 16, 17, 33])
+@pytest.mark.parametrize("shared_pages", [1, 5, 33, 63, 64, 65, 127, 130])
 def test_shared_prefix_lengths(shared_pages):
-    """Splits of 16 pages: fewer, exactly one, a ragged last split, several."""
-    case = shared_case(41, B=5, shared_tokens=16 * 33, suffix_range=(0, 300))
+    """Splits of 64 pages: fewer, exactly one, one page past it, a ragged
+    last split, three splits (the prefix is the first shared_pages of 130
+    pages every sequence maps alike)."""
+    case = shared_case(41, B=5, shared_tokens=16 * 130, suffix_range=(0, 300))
     kc, vc = gpu_fill(case)
     kp, vp = oracle_pools(case)
     assert_close(case, to_f64(shared_decode(case, kc, vc, shared_pages)), oracle(case, kp, vp))
