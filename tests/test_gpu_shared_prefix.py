@@ -185,3 +185,34 @@ def test_many_whole_units_in_one_chunk():
     for part in (1024, 256, 16):
         assert_close(case, to_f64(shared_decode(case, kc, vc, 16, partition=part)),
                      oracle(case, kp, vp), f" partition {part}")
+
+
+SP_HEADS = [(4, 1), (8, 2), (32, 8), (10, 2), (16, 16), (40, 8), (24, 3)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_shared_prefix_random_shapes(seed):
+    """Seeded random shared-prefix batches: 1 to 60 sequences, prefixes of 1
+    to 130 pages with the shared part passed as a random count of them,
+    suffixes of 0 to 500 tokens, head groups of 1 to 8, D = 64 or 128, all
+    four pool formats, windows of 0 to 3,000, automatic or fixed splits."""
+    import numpy as np
+    r = np.random.RandomState(5000 + seed)
+    hq, hkv = SP_HEADS[r.randint(len(SP_HEADS))]
+    kv = ["f16", "bf16", "e4m3", "e5m2"][r.randint(4)]
+    qd = kv if kv in ("f16", "bf16") else ["f16", "bf16"][r.randint(2)]
+    pages = int(r.randint(1, 131))
+    over = dict(B=int(r.randint(1, 61)), shared_tokens=16 * pages,
+                suffix_range=(0, int(r.randint(1, 501))), Hq=hq, Hkv=hkv,
+                D=[64, 128][r.randint(2)], kv=kv, q=qd,
+                kv_src=qd if kv in ("e4m3", "e5m2") else kv,
+                window=[0, 0, 50, 700, 3000][r.randint(5)])
+    if kv in ("f16", "bf16"):
+        over.update(k_scale=1.0, v_scale=1.0)
+    case = shared_case(6000 + seed, **over)
+    shared = int(r.randint(1, pages + 1))
+    part = [0, 0, 32, 512][r.randint(4)]
+    kc, vc = gpu_fill(case)
+    kp, vp = oracle_pools(case)
+    assert_close(case, to_f64(shared_decode(case, kc, vc, shared, partition=part)),
+                 oracle(case, kp, vp))
