@@ -16,7 +16,7 @@ from oracle import scatter as S
 from workloads import make_case, raw_bits
 
 from _util import oracle_pools
-from _gpu import gpu_fill, gpu_decode, to_f64, bits, pool_view, assert_close, DEV
+from _gpu import gpu_fill, gpu_decode, to_f64, bits, pool_view, assert_close, dev_scale, DEV
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,43 @@ def test_scatter_negative_and_out_of_range_slots_skipped():
     kp = S.cache_write_fast(raw_bits(case.sentinel_pool()), raw_bits(case.fill_k), keep.numpy(),
                             case.kv_src_dtype, case.kv_dtype)
     assert np.array_equal(bits(kc), kp)
+
+
+@pytest.mark.parametrize("d,hkv", [(8, 3), (40, 1), (256, 5), (512, 2)])
+@pytest.mark.parametrize("fmts", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e5m2")])
+def test_scatter_other_head_dims(d, hkv, fmts):
+    """The cache write takes any head_dim that is a multiple of 8 up to 512
+    and any kv-head count: random rows into random distinct slots of a pool
+    of random bits, a quarter of the slots negative or past the pool, FP8
+    with per-head scales.  Bit-exact against the oracle's cache write."""
+    src, dst = fmts
+    g = np.random.default_rng(10 * d + hkv)
+    T, nb = 300, 40
+    tdt = torch.float16 if src == "f16" else torch.bfloat16
+    k = torch.from_numpy(g.standard_normal((T, hkv, d)) * 2).to(tdt)
+    v = torch.from_numpy(g.standard_normal((T, hkv, d)) * 2).to(tdt)
+    slots = g.permutation(nb * 16)[:T].astype(np.int64)
+    bad = g.random(T) < 0.25
+    past = bad & (g.random(T) < 0.5)
+    slots[bad] = -1
+    slots[past] = nb * 16 + g.integers(0, 1000, int(past.sum()))
+    fp8 = dst in ("e4m3", "e5m2")
+    ks = tuple(float(x) for x in g.uniform(0.02, 0.5, hkv)) if fp8 else 1.0
+    vs = tuple(float(x) for x in g.uniform(0.02, 0.5, hkv)) if fp8 else 1.0
+    if fp8:
+        p0 = g.integers(0, 256, (nb, hkv, 16, d)).astype(np.uint8)
+        kc, vc = torch.from_numpy(p0).to(DEV), torch.from_numpy(p0.copy()).to(DEV)
+    else:
+        p0 = g.integers(0, 1 << 16, (nb, hkv, 16, d)).astype(np.uint16)
+        kc = torch.from_numpy(p0.view(np.int16)).to(DEV)
+        vc = torch.from_numpy(p0.view(np.int16).copy()).to(DEV)
+    P.vllm_paged_cache_write(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV),
+                             pool_view(kc, dst), pool_view(vc, dst),
+                             k_scale=dev_scale(ks), v_scale=dev_scale(vs))
+    keep = np.where(slots < nb * 16, slots, -1)
+    for pool, x, sc in ((kc, k, ks), (vc, v, vs)):
+        want = S.cache_write(p0, raw_bits(x), keep, src, dst, np.asarray(sc))
+        assert np.array_equal(bits(pool), want)
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
